@@ -1,0 +1,194 @@
+// C entry points of libmoe: host-side argument checks, the workspace plan
+// and the launch sequence of each step.  No allocation, no synchronisation.
+#include <stdint.h>
+#include <string.h>
+
+#include "moe_internal.hpp"
+
+namespace moe {
+
+bool mfma_shapes_ok(const moe_config* c);  // ffn_mfma.hip
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_config(const moe_config* c) {
+  if (!c) return MOE_EINVAL;
+  if (c->hidden <= 0 || c->n_expert <= 0 || c->top_k <= 0 || c->expert_ff <= 0 || c->shared_ff < 0)
+    return MOE_EINVAL;
+  if (c->n_expert > kMaxExperts || c->top_k > kMaxTopK || c->top_k > c->n_expert) return MOE_EINVAL;
+  if (c->gating != MOE_GATING_SOFTMAX_TOPK && c->gating != MOE_GATING_TOPK_SOFTMAX) return MOE_EINVAL;
+  if (c->act != MOE_ACT_SWIGLU && c->act != MOE_ACT_SWIGLU_OAI) return MOE_EINVAL;
+  if (c->x_dtype != MOE_DTYPE_F32 && c->x_dtype != MOE_DTYPE_BF16) return MOE_EINVAL;
+  if (c->w_dtype != MOE_DTYPE_F32 && c->w_dtype != MOE_DTYPE_BF16 && c->w_dtype != MOE_DTYPE_MXFP4)
+    return MOE_EINVAL;
+  if (c->hidden % 32 || c->expert_ff % 32 || c->shared_ff % 32) return MOE_EUNSUPPORTED;
+  if (c->x_dtype == MOE_DTYPE_F32 && c->w_dtype != MOE_DTYPE_F32) return MOE_EUNSUPPORTED;
+  if (c->x_dtype == MOE_DTYPE_BF16 && c->w_dtype == MOE_DTYPE_F32) return MOE_EUNSUPPORTED;
+  // MXFP4 experts come in the fused interleaved gate_up layout only
+  if (c->w_dtype == MOE_DTYPE_MXFP4 && c->act != MOE_ACT_SWIGLU_OAI) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+static size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+int make_plan(const moe_config* c, int32_t T, Plan* p) {
+  int st = check_config(c);
+  if (st) return st;
+  if (T < 0) return MOE_EINVAL;
+  memset(p, 0, sizeof(*p));
+  p->T = T; p->H = c->hidden; p->E = c->n_expert; p->k = c->top_k; p->F = c->expert_ff; p->Fs = c->shared_ff;
+  p->shared = c->shared_ff > 0;
+  p->n_assign = (int64_t)T * c->top_k;
+  p->n_rows = p->n_assign + (p->shared ? T : 0);
+  p->nseg = c->n_expert + p->shared;
+  p->elem_x = c->x_dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  const int64_t G = (p->n_assign + kPermChunk - 1) / kPermChunk;
+  p->perm_bytes = up256((size_t)G * c->n_expert * 4);
+  p->y_bytes = up256((size_t)p->n_rows * c->hidden * 4);
+  size_t o = 0;
+  p->off_logits = o; o += up256((size_t)T * c->n_expert * 4);
+  p->off_idx = o; o += up256((size_t)p->n_assign * 4);
+  p->off_w = o; o += up256((size_t)p->n_assign * 4);
+  p->off_sgate = o; o += up256((size_t)T * 4);
+  p->off_offsets = o; o += up256((size_t)(p->nseg + 1) * 4);
+  p->off_sorted = o; o += up256((size_t)p->n_rows * 4);
+  p->off_pos = o; o += up256((size_t)p->n_rows * 4);
+  p->off_perm = o; o += p->perm_bytes;
+  p->off_h = o; o += up256((size_t)(p->n_assign * c->expert_ff + (p->shared ? (int64_t)T * c->shared_ff : 0)) * p->elem_x);
+  p->off_y = o; o += p->y_bytes;
+  p->total = o;
+  return MOE_OK;
+}
+
+static int weights_ok(const moe_config* c, const moe_weights* w, bool need_router, bool need_experts) {
+  if (!w) return MOE_EINVAL;
+  const void* ptrs[14] = {w->router_w, w->router_b, w->gate_w, w->up_w, w->gate_up_w, w->gate_up_scales,
+                          w->gate_up_b, w->down_w, w->down_scales, w->down_b, w->sh_gate_w, w->sh_up_w,
+                          w->sh_down_w, w->sh_gate_inp};
+  for (int i = 0; i < 14; ++i)
+    if (ptrs[i] && !aligned16(ptrs[i])) return MOE_EINVAL;
+  if (need_router && c->shared_ff > 0 && !w->sh_gate_inp) return MOE_EINVAL;
+  if (need_experts) {
+    if (c->act == MOE_ACT_SWIGLU && (!w->gate_w || !w->up_w || !w->down_w)) return MOE_EINVAL;
+    if (c->act == MOE_ACT_SWIGLU_OAI && (!w->gate_up_w || !w->down_w)) return MOE_EINVAL;
+    if (c->w_dtype == MOE_DTYPE_MXFP4 && (!w->gate_up_scales || !w->down_scales)) return MOE_EINVAL;
+    if (c->shared_ff > 0 && (!w->sh_gate_w || !w->sh_up_w || !w->sh_down_w)) return MOE_EINVAL;
+  }
+  return MOE_OK;
+}
+
+static int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_config* cfg, int32_t T) {
+  Plan p;
+  if (make_plan(cfg, T, &p)) return 0;
+  return p.total;
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument (null or misaligned pointer, bad shape or enum)";
+    case MOE_EUNSUPPORTED: return "unsupported dtype or shape combination";
+    case MOE_EWORKSPACE: return "workspace too small or misaligned";
+    case MOE_EHIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int moe_route(const moe_config* cfg, const moe_weights* w, const void* x, float* logits, int32_t* topk_idx,
+              float* topk_w, float* sgate, int32_t T, hipStream_t stream) {
+  int st = check_config(cfg);
+  if (st) return st;
+  if (T < 0) return MOE_EINVAL;
+  if ((st = weights_ok(cfg, w, true, false))) return st;
+  if (T == 0) return MOE_OK;
+  const bool shared = cfg->shared_ff > 0;
+  if (!logits || !topk_idx || !topk_w || !aligned16(logits)) return MOE_EINVAL;
+  if ((w->router_w || shared) && (!x || !aligned16(x))) return MOE_EINVAL;
+  if (shared && !sgate) return MOE_EINVAL;
+  // the pre-sigmoid shared-gate dot is staged in sgate itself
+  hipError_t e = launch_router_logits(cfg, w, x, T, logits, sgate, stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  return hip_status(launch_gating(cfg, logits, sgate, T, topk_idx, topk_w, sgate, stream));
+}
+
+int moe_permute(const moe_config* cfg, const int32_t* topk_idx, int32_t T, int32_t* offsets, int32_t* sorted_assign,
+                int32_t* assign_pos, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Plan p;
+  int st = make_plan(cfg, T, &p);
+  if (st) return st;
+  if (T == 0) return MOE_OK;
+  if (!offsets || !topk_idx || !sorted_assign || !assign_pos) return MOE_EINVAL;
+  if (p.n_assign > kPermSmallMax && (!ws || ws_bytes < p.perm_bytes || ((uintptr_t)ws & 255u))) return MOE_EWORKSPACE;
+  return hip_status(launch_permute(cfg, topk_idx, T, offsets, sorted_assign, assign_pos, (int32_t*)ws, stream));
+}
+
+int moe_expert_ffn(const moe_config* cfg, const moe_weights* w, const void* x, const int32_t* offsets,
+                   const int32_t* sorted_assign, int32_t T, void* h, void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  Plan p;
+  int st = make_plan(cfg, T, &p);
+  if (st) return st;
+  if ((st = weights_ok(cfg, w, false, true))) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !offsets || !sorted_assign || !h || !aligned16(x) || !aligned16(h)) return MOE_EINVAL;
+  return hip_status(launch_expert_ffn(cfg, w, x, offsets, sorted_assign, T, h, stream));
+}
+
+int moe_combine(const moe_config* cfg, const moe_weights* w, const void* h, const int32_t* offsets,
+                const int32_t* sorted_assign, const float* topk_w, const float* sgate, int32_t T, float* out, void* ws,
+                size_t ws_bytes, hipStream_t stream) {
+  Plan p;
+  int st = make_plan(cfg, T, &p);
+  if (st) return st;
+  if ((st = weights_ok(cfg, w, false, true))) return st;
+  if (T == 0) return MOE_OK;
+  if (!h || !offsets || !sorted_assign || !topk_w || !out || !aligned16(h) || !aligned16(out)) return MOE_EINVAL;
+  if (p.shared && !sgate) return MOE_EINVAL;
+  if (!ws || ws_bytes < p.y_bytes || ((uintptr_t)ws & 255u)) return MOE_EWORKSPACE;
+  float* y = (float*)ws;
+  hipError_t e = launch_down(cfg, w, h, offsets, sorted_assign, T, y, stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  return hip_status(launch_combine_gather(cfg, y, topk_w, sgate, T, out, stream));
+}
+
+int moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T, float* out, float* logits,
+                int32_t* topk_idx, float* topk_w, float* sgate, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Plan p;
+  int st = make_plan(cfg, T, &p);
+  if (st) return st;
+  if ((st = weights_ok(cfg, w, true, true))) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !out || !aligned16(x) || !aligned16(out)) return MOE_EINVAL;
+  if (!w->router_w && !logits) return MOE_EINVAL;
+  if (logits && !aligned16(logits)) return MOE_EINVAL;
+  if (!ws || ws_bytes < p.total || ((uintptr_t)ws & 255u)) return MOE_EWORKSPACE;
+  char* b = (char*)ws;
+  float* lg = logits ? logits : (float*)(b + p.off_logits);
+  int32_t* idx = topk_idx ? topk_idx : (int32_t*)(b + p.off_idx);
+  float* wt = topk_w ? topk_w : (float*)(b + p.off_w);
+  float* sg = p.shared ? (sgate ? sgate : (float*)(b + p.off_sgate)) : nullptr;
+  int32_t* offsets = (int32_t*)(b + p.off_offsets);
+  int32_t* sorted = (int32_t*)(b + p.off_sorted);
+  int32_t* pos = (int32_t*)(b + p.off_pos);
+  int32_t* perm = (int32_t*)(b + p.off_perm);
+  void* h = b + p.off_h;
+  float* y = (float*)(b + p.off_y);
+  hipError_t e;
+  if ((e = launch_router_logits(cfg, w, x, T, lg, sg, stream)) != hipSuccess) return MOE_EHIP;
+  if ((e = launch_gating(cfg, lg, sg, T, idx, wt, sg, stream)) != hipSuccess) return MOE_EHIP;
+  if ((e = launch_permute(cfg, idx, T, offsets, sorted, pos, perm, stream)) != hipSuccess) return MOE_EHIP;
+  if ((e = launch_expert_ffn(cfg, w, x, offsets, sorted, T, h, stream)) != hipSuccess) return MOE_EHIP;
+  if ((e = launch_down(cfg, w, h, offsets, sorted, T, y, stream)) != hipSuccess) return MOE_EHIP;
+  return hip_status(launch_combine_gather(cfg, y, wt, sg, T, out, stream));
+}
+
+}  // extern "C"

@@ -160,7 +160,7 @@ class Case:
         return self.Fs > 0
 
 
-def _tiny_case(T: int = 8, seed: int = BASE_SEED) -> Case:
+def _tiny_case(T: int = 8, seed: int = BASE_SEED, only=None) -> Case:
     """fp32 layer small enough for brute force, with planted exact ties.
 
     Router rows 9 and 13 are copies of row 4, row 12 a copy of row 7, so those
@@ -193,32 +193,47 @@ def _tiny_case(T: int = 8, seed: int = BASE_SEED) -> Case:
 
 
 def _qwen_case(T: int, drawn: bool, seed: int = BASE_SEED, E: int = 256, H: int = 2048,
-               F: int = 512, Fs: int = 512, k: int = 8) -> Case:
+               F: int = 512, Fs: int = 512, k: int = 8, only=None) -> Case:
     name = "qwen35moe_prefill_zipf" if drawn else "qwen35moe_decode"
     c = Case(name, T, H, E, k, F, Fs, "softmax_topk", True, 1.0, "swiglu", 1.702, 7.0,
              "bf16", "bf16", "bf16", drawn_logits=drawn)
-    c.t["x"] = normal("x", (T, H), 1.0, "bf16", seed)
-    c.t["router_w"] = normal("router_w", (E, H), 1.0 / np.sqrt(H), "bf16", seed)
-    c.t["gate_w"] = normal("gate_w", (E, F, H), 1.0 / np.sqrt(H), "bf16", seed)
-    c.t["up_w"] = normal("up_w", (E, F, H), 1.0 / np.sqrt(H), "bf16", seed)
-    c.t["down_w"] = normal("down_w", (E, H, F), 1.0 / np.sqrt(F), "bf16", seed)
-    c.t["sh_gate_w"] = normal("sh_gate_w", (Fs, H), 1.0 / np.sqrt(H), "bf16", seed)
-    c.t["sh_up_w"] = normal("sh_up_w", (Fs, H), 1.0 / np.sqrt(H), "bf16", seed)
-    c.t["sh_down_w"] = normal("sh_down_w", (H, Fs), 1.0 / np.sqrt(Fs), "bf16", seed)
-    c.t["sh_gate_inp"] = normal("sh_gate_inp", (1, H), 1.0 / np.sqrt(H), "bf16", seed)[0]
-    if drawn:
+    want = (lambda n: True) if only is None else (lambda n: n in only)
+    if want("x"):
+        c.t["x"] = normal("x", (T, H), 1.0, "bf16", seed)
+    if want("router_w"):
+        c.t["router_w"] = normal("router_w", (E, H), 1.0 / np.sqrt(H), "bf16", seed)
+    if want("gate_w"):
+        c.t["gate_w"] = normal("gate_w", (E, F, H), 1.0 / np.sqrt(H), "bf16", seed)
+    if want("up_w"):
+        c.t["up_w"] = normal("up_w", (E, F, H), 1.0 / np.sqrt(H), "bf16", seed)
+    if want("down_w"):
+        c.t["down_w"] = normal("down_w", (E, H, F), 1.0 / np.sqrt(F), "bf16", seed)
+    if want("sh_gate_w"):
+        c.t["sh_gate_w"] = normal("sh_gate_w", (Fs, H), 1.0 / np.sqrt(H), "bf16", seed)
+    if want("sh_up_w"):
+        c.t["sh_up_w"] = normal("sh_up_w", (Fs, H), 1.0 / np.sqrt(H), "bf16", seed)
+    if want("sh_down_w"):
+        c.t["sh_down_w"] = normal("sh_down_w", (H, Fs), 1.0 / np.sqrt(Fs), "bf16", seed)
+    if want("sh_gate_inp"):
+        c.t["sh_gate_inp"] = normal("sh_gate_inp", (1, H), 1.0 / np.sqrt(H), "bf16", seed)[0]
+    if drawn and want("logits"):
         c.t["logits"] = zipf_logits(T, E, 1.0, seed)
     return c
 
 
 def _gptoss_case(T: int, mxfp4: bool, seed: int = BASE_SEED, E: int = 32, H: int = 2880,
-                 F: int = 2880, k: int = 4) -> Case:
+                 F: int = 2880, k: int = 4, only=None) -> Case:
     name = "gptoss20b_mxfp4" if mxfp4 else "gptoss20b_bf16"
     c = Case(name, T, H, E, k, F, 0, "topk_softmax", False, 1.0, "swiglu_oai", 1.702, 7.0,
              "bf16", "mxfp4" if mxfp4 else "bf16", "bf16")
-    c.t["x"] = normal("x", (T, H), 1.0, "bf16", seed)
-    c.t["router_w"] = normal("router_w", (E, H), 1.0 / np.sqrt(H), "bf16", seed)
-    c.t["router_b"] = normal("router_b", (1, E), 1.0 / np.sqrt(H), "bf16", seed)[0]
+    want = (lambda n: True) if only is None else (lambda n: n in only)
+    if want("x"):
+        c.t["x"] = normal("x", (T, H), 1.0, "bf16", seed)
+    if want("router_w"):
+        c.t["router_w"] = normal("router_w", (E, H), 1.0 / np.sqrt(H), "bf16", seed)
+        c.t["router_b"] = normal("router_b", (1, E), 1.0 / np.sqrt(H), "bf16", seed)[0]
+    if not want("experts"):
+        return c
     c.t["gate_up_b"] = normal("gate_up_b", (E, 2 * F), 1.0 / np.sqrt(H), "bf16", seed)
     c.t["down_b"] = normal("down_b", (E, H), 1.0 / np.sqrt(F), "bf16", seed)
     if mxfp4:

@@ -1,0 +1,232 @@
+"""GPU expert FFN, combine and whole layer (moe_expert_ffn, moe_combine,
+moe_forward) against the oracle on the same seeded inputs.
+
+Small layers are compared element by element in full; the full-size layers
+(the shapes the benchmark times) on seeded samples of tokens / sorted rows
+that the oracle computes one by one."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_moe_ffn_router_amd as moe
+import synth
+from tests._gpu import act_dtype, config_of, device_weights, h_numel, to_torch
+from tests._parity import assert_normwise, assert_rel, cached_case, log, tol_of
+
+pytestmark = pytest.mark.gpu
+
+# (case name, T, token sample size or None for all, extra shape overrides)
+LAYERS = [
+    ("tiny_fp32", 8, None, {}),
+    ("qwen35moe_decode", 8, None, {}),
+    ("qwen35moe_decode", 64, 16, {}),                       # largest GEMV batch
+    ("qwen35moe_decode", 1, None, {}),
+    ("qwen35moe_decode", 200, None, dict(E=16, H=256, F=192, Fs=128, k=4)),  # MFMA, ragged tiles
+    ("qwen35moe_decode", 300, None, dict(E=8, H=288, F=96, Fs=96, k=2)),     # H % 64 != 0: GEMV path
+    ("qwen35moe_prefill_zipf", 4096, 40, {}),
+    ("gptoss20b_bf16", 16, None, dict(E=8, H=320, F=192, k=2)),
+    ("gptoss20b_bf16", 150, None, dict(E=8, H=320, F=192, k=2)),
+    ("gptoss20b_bf16", 2048, 20, {}),
+    ("gptoss20b_mxfp4", 16, None, {}),
+    ("gptoss20b_mxfp4", 150, None, dict(E=8, H=320, F=192, k=2)),
+    ("gptoss20b_mxfp4", 2048, 20, {}),
+]
+
+
+def _case(name, T, over):
+    if over:
+        return synth.make_case(name, T=T, **over)
+    return cached_case(name, T)
+
+
+def _ids(p):
+    name, T, s, over = p
+    return "%s-T%d%s" % (name, T, "-" + "-".join("%s%d" % kv for kv in over.items()) if over else "")
+
+
+def _sample(T, n, seed=1):
+    if n is None or n >= T:
+        return np.arange(T, dtype=np.int32)
+    rng = np.random.default_rng(seed + T)
+    s = set(rng.choice(T, n - 2, replace=False).tolist()) | {0, T - 1}
+    return np.array(sorted(s), np.int32)
+
+
+def _forward(case):
+    cfg = config_of(case)
+    w = device_weights(case)
+    T = case.T
+    x = to_torch(case.t["x"])
+    out = torch.full((T, case.H), float("nan"), dtype=torch.float32, device="cuda")
+    if case.drawn_logits:
+        lg = to_torch(case.t["logits"])
+    else:
+        lg = torch.empty((T, case.E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, case.k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((T, case.k), dtype=torch.float32, device="cuda")
+    sg = torch.empty(T, dtype=torch.float32, device="cuda") if case.has_shared else None
+    ws = torch.empty(moe.moe_workspace_bytes(cfg, T), dtype=torch.uint8, device="cuda")
+    moe.moe_forward(cfg, w, x, T, out, ws, logits=lg, topk_idx=idx, topk_w=wt, sgate=sg)
+    torch.cuda.synchronize()
+    return (out.cpu().numpy(), lg.cpu().numpy(), idx.cpu().numpy(), wt.cpu().numpy(),
+            None if sg is None else sg.cpu().numpy())
+
+
+def _f64(a, dt):
+    return synth.bf16_to_f32(a).astype(np.float64) if dt == "bf16" else a.astype(np.float64)
+
+
+def _logit_bound(case, tokens):
+    """fp32 dot-product error bound of the router logits, per (token, expert)."""
+    if case.drawn_logits:
+        return np.zeros((len(tokens), case.E))
+    xa = np.abs(_f64(case.t["x"][tokens], case.x_dtype))
+    wa = np.abs(_f64(case.t["router_w"], case.router_dtype))
+    return case.H * 2.0 ** -24 * (xa @ wa.T) + 2.0 ** -23
+
+
+@pytest.mark.parametrize("p", LAYERS, ids=_ids)
+def test_forward_matches_oracle(p):
+    name, T, nsample, over = p
+    log("forward %s" % _ids(p))
+    case = _case(name, T, over)
+    out, lg, idx, wt, sg = _forward(case)
+    tokens = _sample(T, nsample)
+    L = oracle.Layer(case)
+    r_out, r_idx, r_w, r_sg = L.forward(logits=case.t.get("logits"), tokens=tokens)
+    r_out, r_idx, r_w = r_out[tokens], r_idx[tokens], r_w[tokens]
+    g_out, g_idx, g_w = out[tokens], idx[tokens], wt[tokens]
+    same = (g_idx == r_idx).all(1)
+    if not same.all():
+        # A token may route differently only where the oracle's logits leave a
+        # gap no larger than the fp32 rounding bound of the GPU's logits.
+        ref_lg = L.router_logits()[tokens] if not case.drawn_logits else case.t["logits"][tokens]
+        bnd = _logit_bound(case, tokens)
+        for i in np.nonzero(~same)[0]:
+            kth = np.sort(ref_lg[i])[::-1][case.k - 1]
+            sel = set(g_idx[i].tolist())
+            for e in range(case.E):
+                if e in sel:
+                    assert ref_lg[i, e] >= kth - 2 * bnd[i].max(), "token %d: GPU picked a clearly losing expert" % i
+                else:
+                    assert ref_lg[i, e] <= kth + 2 * bnd[i].max(), "token %d: GPU dropped a clear winner" % i
+        log("  %d of %d sampled tokens routed differently inside the rounding bound" % ((~same).sum(), len(tokens)))
+    assert same.mean() >= 0.95
+    tol = tol_of(case)
+    rel = assert_normwise(g_out[same], r_out[same], tol, "layer output")
+    # routing weights from independently rounded logits: 1e-5 relative plus
+    # the logits' rounding bound carried through the softmax
+    bnd = _logit_bound(case, tokens)[same].max(1, keepdims=True)
+    assert np.all(np.abs(g_w[same] - r_w[same]) <= 1e-5 * r_w[same] + 2.0 * r_w[same] * bnd + 1e-30)
+    if case.has_shared:
+        r_s = r_sg[tokens]
+        xs = np.abs(_f64(case.t["x"][tokens], case.x_dtype)) @ np.abs(_f64(case.t["sh_gate_inp"], case.x_dtype))
+        assert np.all(np.abs(sg[tokens] - r_s) <= 1e-5 * r_s + 0.25 * case.H * 2.0 ** -24 * xs + 1e-30)
+    log("  max|err|/max|ref| = %.3e (tol %.0e)" % (rel, tol))
+
+
+def _routing_from_oracle(case):
+    """Oracle routing and permutation of a case (inputs for the step tests)."""
+    L = oracle.Layer(case)
+    lg = case.t["logits"] if case.drawn_logits else L.router_logits()
+    idx, wt = L.route(lg)
+    sg = oracle.sigmoid(L.shared_gate_logit()) if case.has_shared else None
+    off, sa, ap = oracle.permute(case.E, case.k, case.T, case.has_shared, idx)
+    return L, idx, wt, sg, off, sa, ap
+
+
+def _h_row(case, h_flat, p):
+    nas = case.T * case.k
+    if p < nas:
+        return h_flat[p * case.F:(p + 1) * case.F]
+    q = nas * case.F + (p - nas) * case.Fs
+    return h_flat[q:q + case.Fs]
+
+
+STEP = [LAYERS[i] for i in (0, 1, 4, 5, 6, 8, 9, 11, 12)]
+
+
+@pytest.mark.parametrize("p", STEP, ids=_ids)
+def test_expert_ffn_and_combine_match_oracle(p):
+    name, T, nsample, over = p
+    log("expert_ffn/combine %s" % _ids(p))
+    case = _case(name, T, over)
+    cfg = config_of(case)
+    w = device_weights(case)
+    L, idx, wt, sg, off, sa, ap = _routing_from_oracle(case)
+    nas = T * case.k
+    n_rows = len(sa)
+    d_off, d_sa = to_torch(off), to_torch(sa)
+    h = torch.empty(h_numel(case, T), dtype=act_dtype(case), device="cuda")
+    moe.moe_expert_ffn(cfg, w, to_torch(case.t["x"]), d_off, d_sa, T, h)
+    torch.cuda.synchronize()
+    h_gpu = h.float().cpu().numpy()
+    # h rows: all of them for small layers, a seeded sample of sorted rows otherwise
+    rows = np.arange(n_rows) if nsample is None else _sample(n_rows, 3 * nsample, seed=7)
+    nseg = case.E + (1 if case.has_shared else 0)
+    seg_of = np.searchsorted(off, rows, side="right") - 1
+    xs = _f64(case.t["x"], case.x_dtype)
+    ref_rows, got_rows = [], []
+    for p_, e in zip(rows, seg_of):
+        a = sa[p_]
+        t = a // case.k if a < nas else a - nas
+        ref_rows.append(L.expert_act(int(min(e, nseg - 1)), xs[t]))
+        got_rows.append(_h_row(case, h_gpu, p_))
+    for g, r in zip(got_rows, ref_rows):
+        assert g.shape == r.shape
+    assert_normwise(np.concatenate(got_rows), np.concatenate(ref_rows), tol_of(case), "h")
+
+    # combine: the oracle's h rounded to the activation dtype is the input of both sides
+    h_in = np.zeros(h_numel(case, T), np.float32)
+    need = np.arange(n_rows) if nsample is None else None
+    tokens = np.arange(T) if nsample is None else _sample(T, nsample)
+    rows_needed = set()
+    for t in tokens:
+        rows_needed.update(int(ap[t * case.k + j]) for j in range(case.k))
+        if case.has_shared:
+            rows_needed.add(int(ap[nas + t]))
+    for p_ in sorted(rows_needed):
+        a = sa[p_]
+        t = a // case.k if a < nas else a - nas
+        e = int(np.searchsorted(off, p_, side="right") - 1)
+        hv = L.expert_act(min(e, nseg - 1), xs[t]).astype(np.float32)
+        if case.x_dtype == "bf16":
+            hv = synth.bf16_to_f32(synth.bf16_bits(hv))
+        if p_ < nas:
+            h_in[p_ * case.F:(p_ + 1) * case.F] = hv
+        else:
+            q = nas * case.F + (p_ - nas) * case.Fs
+            h_in[q:q + case.Fs] = hv
+    h_dev = to_torch(synth.bf16_bits(h_in)) if case.x_dtype == "bf16" else to_torch(h_in)
+    out = torch.full((T, case.H), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.moe_workspace_bytes(cfg, T), dtype=torch.uint8, device="cuda")
+    moe.moe_combine(cfg, w, h_dev, d_off, d_sa, to_torch(wt), None if sg is None else to_torch(sg), T, out, ws)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    ref = np.zeros((len(tokens), case.H))
+    for i, t in enumerate(tokens):
+        for j in range(case.k):
+            p_ = int(ap[t * case.k + j])
+            ref[i] += float(wt[t, j]) * L.expert_down(int(idx[t, j]), h_in[p_ * case.F:(p_ + 1) * case.F])
+        if case.has_shared:
+            p_ = int(ap[nas + t])
+            q = nas * case.F + (p_ - nas) * case.Fs
+            ref[i] += float(sg[t]) * L.expert_down(case.E, h_in[q:q + case.Fs])
+    assert_normwise(out[tokens], ref, tol_of(case), "combine output")
+
+
+def test_forward_repeatable_and_rejects_bad_args():
+    case = cached_case("qwen35moe_decode", 8)
+    a = _forward(case)
+    b = _forward(case)
+    for u, v in zip(a[1:], b[1:]):
+        assert np.array_equal(u, v)   # routing is bit-identical run to run
+    cfg = config_of(case)
+    w = device_weights(case)
+    x = to_torch(case.t["x"])
+    out = torch.empty((8, case.H), dtype=torch.float32, device="cuda")
+    small = torch.empty(256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_forward(cfg, w, x, 8, out, small)
+    assert ei.value.status == moe.MOE_EWORKSPACE

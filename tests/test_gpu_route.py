@@ -1,0 +1,149 @@
+"""GPU routing (moe_route) against the oracle: bit-exact expert indices on
+the same logits, fp32 weights and shared gate within 1e-5 relative, planted
+ties through the GPU router product, determinism."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_moe_ffn_router_amd as moe
+import synth
+from tests._gpu import config_of, device_weights, to_torch
+from tests._parity import assert_rel, cached_case, log
+
+pytestmark = pytest.mark.gpu
+
+ROUTE_CASES = [("tiny_fp32", 8), ("qwen35moe_decode", 8), ("qwen35moe_prefill_zipf", 4096),
+               ("gptoss20b_bf16", 2048), ("gptoss20b_mxfp4", 16), ("qwen35moe_decode", 333)]
+ROUTE_ONLY = ("x", "router_w", "sh_gate_inp", "logits")
+
+
+def _route(case, logits_np, with_router):
+    cfg = config_of(case)
+    w = device_weights(case) if with_router else {k: v for k, v in device_weights(case).items()
+                                                  if k not in ("router_w", "router_b")}
+    T = case.T
+    x = to_torch(case.t["x"]) if "x" in case.t else None
+    lg = to_torch(np.ascontiguousarray(logits_np, np.float32)) if logits_np is not None else \
+        torch.empty((T, case.E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, case.k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((T, case.k), dtype=torch.float32, device="cuda")
+    sg = torch.empty(T, dtype=torch.float32, device="cuda") if case.has_shared else None
+    moe.moe_route(cfg, w, x, lg, idx, wt, sg, T)
+    torch.cuda.synchronize()
+    return lg.cpu().numpy(), idx.cpu().numpy(), wt.cpu().numpy(), None if sg is None else sg.cpu().numpy()
+
+
+@pytest.mark.parametrize("name,T", ROUTE_CASES)
+def test_route_given_logits_matches_oracle(name, T):
+    log("route given logits: %s T=%d" % (name, T))
+    case = cached_case(name, T, ROUTE_ONLY) if name != "tiny_fp32" else synth.make_case(name, T=T)
+    if case.drawn_logits:
+        logits = case.t["logits"]
+    else:
+        logits = oracle_logits(case)
+    _, idx, wt, sg = _route(case, logits, with_router=False)
+    ref_idx, ref_w = route_ref(case, logits)
+    assert np.array_equal(idx, ref_idx), "indices differ at tokens %s" % np.nonzero((idx != ref_idx).any(1))[0][:10]
+    assert_rel(wt, ref_w, 1e-5, 1e-30, "routing weights")
+    if case.has_shared:
+        ref_s = oracle.sigmoid(shared_logit_ref(case))
+        # the gate dot is fp32 on the GPU: allow its error bound through sigmoid' <= 1/4
+        xs = np.abs(_f64(case.t["x"], case.x_dtype)) @ np.abs(_f64(case.t["sh_gate_inp"], case.x_dtype))
+        bound = 0.25 * case.H * 2.0 ** -24 * xs
+        assert np.all(np.abs(sg.astype(np.float64) - ref_s) <= 1e-5 * np.abs(ref_s) + bound)
+
+
+def _f64(a, dt):
+    return synth.bf16_to_f32(a).astype(np.float64) if dt == "bf16" else a.astype(np.float64)
+
+
+def _layer_for_route(case):
+    # the oracle's gating only needs the config; weights may be partial here
+    return oracle.Layer(case)
+
+
+def oracle_logits(case):
+    return _layer_for_route(case).router_logits()
+
+
+def shared_logit_ref(case):
+    return _layer_for_route(case).shared_gate_logit()
+
+
+def route_ref(case, logits):
+    return _layer_for_route(case).route(logits)
+
+
+def _hand_case(E, k, gating="softmax_topk", norm=True):
+    c = synth.Case("hand", 1, 32, E, k, 32, 0, gating, norm, 1.0,
+                   "swiglu" if gating == "softmax_topk" else "swiglu_oai", 1.702, 7.0, "f32", "f32", "f32")
+    return c
+
+
+HAND = [
+    # (E, k, logits rows) with ties the first-seen rule must resolve
+    (16, 3, [[0.5] * 16]),
+    (16, 2, [[0, 1, 3, 0, 2, 3, 1, 0, 0, 0, 0, 0, 0, 0, 0, 0]]),
+    (8, 2, [[-0.0, 0.0, -1, -1, -1, -1, -1, -1], [0.0, -0.0, -2, -3, -1, -1, -1, -1]]),
+    (256, 8, None),   # built below: ties across lanes and register slots
+    (1024, 32, None),
+    (32, 4, [[1.0] * 32]),
+]
+
+
+@pytest.mark.parametrize("gating", ["softmax_topk", "topk_softmax"])
+@pytest.mark.parametrize("hi", range(len(HAND)))
+def test_route_hand_ties(hi, gating):
+    E, k, rows = HAND[hi]
+    if rows is None:
+        rng = np.random.default_rng(E)
+        lg = rng.integers(-3, 4, (64, E)).astype(np.float32) * np.float32(0.25)
+        lg[0, [3, 67, 131, 195]] = 9.0   # same lane, different register slots
+        lg[1, [5, 6, 7, 900 % E]] = 9.0   # neighbouring lanes
+        lg[2, :] = -0.0
+        lg[2, E - 1] = 0.0
+    else:
+        lg = np.array(rows, np.float32)
+    case = _hand_case(E, k, gating)
+    case.T = lg.shape[0]
+    case.t["x"] = np.zeros((case.T, 32), np.float32)
+    _, idx, wt, _ = _route(case, lg, with_router=False)
+    ref_idx, ref_w = route_ref(case, lg)
+    assert np.array_equal(idx, ref_idx)
+    assert_rel(wt, ref_w, 1e-5, 1e-30, "weights")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_router_product_keeps_planted_ties(dtype):
+    """Bit-equal router rows must give bit-equal GPU logits (every row is
+    reduced in the same order), so first-seen decides as on the CPU."""
+    case = synth.make_case("tiny_fp32")
+    if dtype == "bf16":
+        case.x_dtype = case.w_dtype = case.router_dtype = "bf16"
+        for n, a in list(case.t.items()):
+            case.t[n] = synth.bf16_bits(a)
+    lg, idx, wt, sg = _route(case, None, with_router=True)
+    assert lg[3, 4] == lg[3, 9] == lg[3, 13]
+    assert lg[6, 7] == lg[6, 12]
+    assert list(idx[3]) == [4, 9] and list(idx[6]) == [0, 7]
+    # GPU logits vs the oracle's, within the fp32 dot-product error bound
+    L = oracle.Layer(case)
+    ref = L.router_logits()
+    xa = np.abs(_f64(case.t["x"], case.x_dtype))
+    wa = np.abs(_f64(case.t["router_w"], case.router_dtype))
+    bound = case.H * 2.0 ** -24 * (xa @ wa.T) + 2.0 ** -24 * np.abs(ref)
+    assert np.all(np.abs(lg.astype(np.float64) - ref) <= bound)
+    # and on identical logits the indices are the oracle's
+    ref_idx, _ = L.route(lg)
+    assert np.array_equal(idx, ref_idx)
+
+
+def test_route_deterministic_and_T0():
+    case = cached_case("qwen35moe_decode", 333, ROUTE_ONLY)
+    a = _route(case, None, with_router=True)
+    b = _route(case, None, with_router=True)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+    cfg = config_of(case)
+    moe.moe_route(cfg, device_weights(case), None, None, None, None, None, 0)  # T = 0: no-op
