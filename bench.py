@@ -1,0 +1,249 @@
+"""Benchmark of the MoE FFN layer on one MI355X.
+
+Default workload: the qwen35moe-shaped decode layer (T=8 tokens, H=2048,
+256 experts, top-8, expert FF 512, shared expert FF 512, bf16 weights and
+activations, fp32 router).  A step is one whole-layer pass (moe_forward:
+router product, gating, permutation, expert gate/up + SwiGLU, down +
+weighted combine + shared expert) over one batch of synthetic tokens, with
+inputs resident in HBM.  Weights rotate over several identical copies at
+different addresses so every step streams its experts cold from HBM (the
+256 MB last-level cache never holds the previous step's experts), as
+consecutive layers of a model would.
+
+The same JSON line also reports the prefill-sized layer (same weights,
+T=4096 tokens, router logits drawn so expert load is Zipf(1.0)-skewed),
+the roofline of the dominant kernel and the CPU oracle's throughput.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-prefill]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec + %HBM-roofline (T=8 decode) and %MFMA-peak (T=4096)"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=4, help="weight copies rotated per step")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the T=4096 measurement")
+    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+class Layer:
+    """Device-resident layer: weight copies, one batch of tokens, outputs."""
+
+    def __init__(self, case, copies, T=None, logits=None, x=None):
+        import torch
+        from tests._gpu import config_of, device_weights, to_torch
+        import sparse_moe_ffn_router_amd as moe
+        self.moe = moe
+        self.case = case
+        self.T = case.T if T is None else T
+        self.cfg = config_of(case)
+        base = device_weights(case)
+        if logits is not None:
+            base = {k: v for k, v in base.items() if k not in ("router_w", "router_b")}
+        self.weights = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
+        self.x = to_torch(case.t["x"] if x is None else x)
+        self.logits = to_torch(logits) if logits is not None else \
+            torch.empty((self.T, case.E), dtype=torch.float32, device="cuda")
+        self.out = torch.empty((self.T, case.H), dtype=torch.float32, device="cuda")
+        self.idx = torch.empty((self.T, case.k), dtype=torch.int32, device="cuda")
+        self.wt = torch.empty((self.T, case.k), dtype=torch.float32, device="cuda")
+        self.sg = torch.empty(self.T, dtype=torch.float32, device="cuda")
+        self.ws = torch.empty(moe.moe_workspace_bytes(self.cfg, self.T), dtype=torch.uint8, device="cuda")
+        n_rows = self.T * case.k + (self.T if case.has_shared else 0)
+        self.offsets = torch.empty(case.E + 2, dtype=torch.int32, device="cuda")
+        self.sorted = torch.empty(n_rows, dtype=torch.int32, device="cuda")
+        self.pos = torch.empty(n_rows, dtype=torch.int32, device="cuda")
+        self.h = torch.empty(self.T * case.k * case.F + (self.T * case.Fs if case.has_shared else 0),
+                             dtype=torch.bfloat16, device="cuda")
+
+    def forward(self, step):
+        self.moe.moe_forward(self.cfg, self.weights[step % len(self.weights)], self.x, self.T, self.out, self.ws,
+                             logits=self.logits, topk_idx=self.idx, topk_w=self.wt, sgate=self.sg)
+
+    def ops(self, step, ev_ffn=None):
+        """The same kernels through the four step entry points; optional
+        events bracket the expert gate/up launch."""
+        m, w = self.moe, self.weights[step % len(self.weights)]
+        m.moe_route(self.cfg, w, self.x, self.logits, self.idx, self.wt, self.sg, self.T)
+        m.moe_permute(self.cfg, self.idx, self.T, self.offsets, self.sorted, self.pos, self.ws)
+        if ev_ffn:
+            ev_ffn[0].record()
+        m.moe_expert_ffn(self.cfg, w, self.x, self.offsets, self.sorted, self.T, self.h)
+        if ev_ffn:
+            ev_ffn[1].record()
+        m.moe_combine(self.cfg, w, self.h, self.offsets, self.sorted, self.wt, self.sg, self.T, self.out, self.ws)
+
+
+def time_loop(fn, steps, warmup):
+    import torch
+    for s in range(warmup):
+        fn(s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for s in range(steps):
+        fn(warmup + s)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def active_experts(idx_np, E):
+    import numpy as np
+    return int(np.unique(idx_np.reshape(-1)).size)
+
+
+def gateup_bytes(case, n_active, T):
+    """Algorithmic bytes of one expert gate/up launch: every active routed
+    expert's gate and up rows once (2*F*H bf16 = 4 MiB each for this shape),
+    the shared expert's, the tokens read and h written."""
+    w = n_active * 2 * case.F * case.H * 2
+    if case.has_shared:
+        w += 2 * case.Fs * case.H * 2
+    x = T * case.H * 2
+    h = (T * case.k * case.F + (T * case.Fs if case.has_shared else 0)) * 2
+    return w + x + h
+
+
+def layer_bytes(case, n_active, T):
+    """Algorithmic bytes of the whole layer: active experts' weights, router,
+    shared expert, tokens in, fp32 out."""
+    per_expert = 3 * case.F * case.H * 2
+    b = n_active * per_expert + case.E * case.H * 2 + T * case.H * 2 + T * case.H * 4
+    if case.has_shared:
+        b += 3 * case.Fs * case.H * 2 + case.H * 2
+    return b
+
+
+def layer_flops(case, T):
+    f = 2 * T * case.k * 3 * case.F * case.H + 2 * T * case.H * case.E
+    if case.has_shared:
+        f += 2 * T * 3 * case.Fs * case.H + 2 * T * case.H
+    return f
+
+
+def cpu_baseline(case, seconds):
+    """The oracle (plain C, double accumulation, OpenMP over tokens) on the
+    decode batch, repeated for about `seconds` seconds."""
+    import oracle
+    L = oracle.Layer(case)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        L.forward()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    return {"value": round(n * case.T / el, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d repeats of the whole T=%d decode batch (%.1f s)" % (n, case.T, el)}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (requested --gpus %d)" % a.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import synth
+
+    torch.cuda.set_device(0)
+    t0 = time.perf_counter()
+    dec = synth.make_case("qwen35moe_decode", T=8)
+    log("decode case generated in %.1f s" % (time.perf_counter() - t0))
+    layer = Layer(dec, a.copies)
+    ms, wall = time_loop(layer.forward, a.steps, a.warmup)
+    n_active = active_experts(layer.idx.cpu().numpy(), dec.E)
+    tok_s = dec.T / (ms * 1e-3)
+    log("decode: %.4f ms/step, %.0f tokens/s, %d active experts" % (ms, tok_s, n_active))
+
+    # dominant kernel (expert gate/up), timed with events on the launch stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    for s in range(a.warmup):
+        layer.ops(s)
+    torch.cuda.synchronize()
+    for s in range(a.steps):
+        layer.ops(s, evs[s])
+    torch.cuda.synchronize()
+    k_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    gb = gateup_bytes(dec, n_active, dec.T)
+    achieved = gb / (k_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": "k_gateup_gemv (expert gate/up + SwiGLU)", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel_ms": round(k_ms, 5), "algorithmic_bytes": gb}
+    lb = layer_bytes(dec, n_active, dec.T)
+    layer_gbs = lb / (ms * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "qwen35moe-shaped decode MoE layer", "tokens": dec.T, "hidden": dec.H,
+                   "n_expert": dec.E, "top_k": dec.k, "expert_ff": dec.F, "shared_ff": dec.Fs,
+                   "active_experts": n_active, "weight_copies_rotated": a.copies,
+                   "layer_algorithmic_bytes": lb, "layer_GBps": round(layer_gbs, 1),
+                   "layer_frac_hbm": round(layer_gbs / HBM_PEAK_GBS, 4), "wall_s": round(wall, 3)},
+        "roofline": roofline,
+    }
+    del layer
+    torch.cuda.empty_cache()
+
+    if not a.no_prefill:
+        T = 4096
+        pre = synth.make_case("qwen35moe_prefill_zipf", T=T, only={"x", "logits"})
+        pre.t.update({k: v for k, v in dec.t.items() if k != "x"})
+        pl = Layer(pre, a.copies, logits=pre.t["logits"])
+        p_ms, _ = time_loop(pl.forward, a.prefill_steps, 3)
+        # the drawn logits skip the router product; time it at the same shape
+        # (this batch's tokens, the decode layer's router) and add it
+        rt = Layer(dec, 1, T=T, x=pre.t["x"])
+        r_ms, _ = time_loop(lambda s: rt.moe.moe_route(rt.cfg, rt.weights[0], rt.x, rt.logits, rt.idx, rt.wt,
+                                                        rt.sg, T), a.prefill_steps, 3)
+        tot = p_ms + r_ms
+        fl = layer_flops(pre, T)
+        tf = fl / (tot * 1e-3) / 1e12
+        pb = layer_bytes(pre, pre.E, T)
+        result["prefill"] = {
+            "workload": "qwen35moe-shaped prefill MoE layer, Zipf(1.0) expert load", "tokens": T,
+            "ms_per_step": round(tot, 4), "layer_ms_drawn_logits": round(p_ms, 4), "router_ms": round(r_ms, 4),
+            "tokens_per_s": round(T / (tot * 1e-3), 1), "TFLOPs": round(tf, 2),
+            "frac_bf16_mfma_peak": round(tf / BF16_PEAK_TFLOPS, 4), "algorithmic_flops": fl,
+            "algorithmic_bytes": pb, "frac_hbm": round(pb / (tot * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log("prefill: %.3f ms (+router %.3f ms), %.1f TFLOP/s" % (p_ms, r_ms, tf))
+        del pl, rt
+
+    if not a.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(dec, a.cpu_seconds)
+        log("cpu oracle: %s" % result["cpu_baseline"])
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -117,8 +117,8 @@ class Layer:
         w.router_w = _mat(t.get("router_w"), rd)
         w.router_b = _mat(t.get("router_b"), rd)
         if wd == "mxfp4":
-            w.gate_up_w = _mat(t["gate_up_codes"], "mxfp4", t["gate_up_scales"])
-            w.down_w = _mat(t["down_codes"], "mxfp4", t["down_scales"])
+            w.gate_up_w = _mat(t.get("gate_up_codes"), "mxfp4", t.get("gate_up_scales"))
+            w.down_w = _mat(t.get("down_codes"), "mxfp4", t.get("down_scales"))
         else:
             w.gate_w = _mat(t.get("gate_w"), wd)
             w.up_w = _mat(t.get("up_w"), wd)

@@ -44,10 +44,10 @@ def device_weights(case, device="cuda", router=True):
         if k in t:
             w[n] = to_torch(t[k], device)
     if case.w_dtype == "mxfp4":
-        w["gate_up_w"] = to_torch(t["gate_up_codes"], device)
-        w["gate_up_scales"] = to_torch(t["gate_up_scales"], device)
-        w["down_w"] = to_torch(t["down_codes"], device)
-        w["down_scales"] = to_torch(t["down_scales"], device)
+        for field, key in (("gate_up_w", "gate_up_codes"), ("gate_up_scales", "gate_up_scales"),
+                           ("down_w", "down_codes"), ("down_scales", "down_scales")):
+            if key in t:
+                w[field] = to_torch(t[key], device)
     return w
 
 
