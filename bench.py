@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true", help="skip the T=4096 measurement")
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--gptoss", action="store_true",
+                    help="also time the gpt-oss-20b-shaped layers (bf16 T=2048, MXFP4 T=16 and T=2048)")
     return ap.parse_args()
 
 
@@ -238,6 +240,27 @@ def main():
             "algorithmic_bytes": pb, "frac_hbm": round(pb / (tot * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         log("prefill: %.3f ms (+router %.3f ms), %.1f TFLOP/s" % (p_ms, r_ms, tf))
         del pl, rt
+
+    if a.gptoss:
+        del dec
+        result["gptoss"] = {}
+        for name, T in (("gptoss20b_bf16", 2048), ("gptoss20b_mxfp4", 16), ("gptoss20b_mxfp4", 2048)):
+            c = synth.make_case(name, T=T)
+            gl = Layer(c, 2)
+            g_ms, _ = time_loop(gl.forward, a.prefill_steps if T > 64 else a.steps, 3)
+            n_act = active_experts(gl.idx.cpu().numpy(), c.E)
+            per_expert = (2 * c.F * c.H + c.H * c.F) * (2 if c.w_dtype == "bf16" else 0.5 + 1 / 16.0)
+            byt = n_act * per_expert + c.E * c.H * 2 + T * c.H * 6
+            fl = layer_flops(c, T)
+            key = "%s_T%d" % (name, T)
+            result["gptoss"][key] = {"ms": round(g_ms, 4), "tokens_per_s": round(T / (g_ms * 1e-3), 1),
+                                     "TFLOPs": round(fl / (g_ms * 1e-3) / 1e12, 2),
+                                     "frac_hbm": round(byt / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                     "active_experts": n_act}
+            log("%s: %s" % (key, result["gptoss"][key]))
+            del gl, c
+            torch.cuda.empty_cache()
+        dec = synth.make_case("qwen35moe_decode", T=8)
 
     if not a.no_cpu:
         result["cpu_baseline"] = cpu_baseline(dec, a.cpu_seconds)

@@ -42,8 +42,7 @@ int make_plan(const moe_config* c, int32_t T, Plan* p) {
   p->n_rows = p->n_assign + (p->shared ? T : 0);
   p->nseg = c->n_expert + p->shared;
   p->elem_x = c->x_dtype == MOE_DTYPE_BF16 ? 2 : 4;
-  const int64_t G = (p->n_assign + kPermChunk - 1) / kPermChunk;
-  p->perm_bytes = up256((size_t)G * c->n_expert * 4);
+  p->perm_bytes = up256(permute_scratch_bytes(T, c->n_expert));
   p->y_bytes = up256((size_t)p->n_rows * c->hidden * 4);
   size_t o = 0;
   p->off_logits = o; o += up256((size_t)T * c->n_expert * 4);
@@ -116,7 +115,7 @@ int moe_route(const moe_config* cfg, const moe_weights* w, const void* x, float*
   // the pre-sigmoid shared-gate dot is staged in sgate itself
   hipError_t e = launch_router_logits(cfg, w, x, T, logits, sgate, stream);
   if (e != hipSuccess) return MOE_EHIP;
-  return hip_status(launch_gating(cfg, logits, sgate, T, topk_idx, topk_w, sgate, stream));
+  return hip_status(launch_gating(cfg, w, x, logits, sgate, T, topk_idx, topk_w, sgate, stream));
 }
 
 int moe_permute(const moe_config* cfg, const int32_t* topk_idx, int32_t T, int32_t* offsets, int32_t* sorted_assign,
@@ -126,7 +125,7 @@ int moe_permute(const moe_config* cfg, const int32_t* topk_idx, int32_t T, int32
   if (st) return st;
   if (T == 0) return MOE_OK;
   if (!offsets || !topk_idx || !sorted_assign || !assign_pos) return MOE_EINVAL;
-  if (p.n_assign > kPermSmallMax && (!ws || ws_bytes < p.perm_bytes || ((uintptr_t)ws & 255u))) return MOE_EWORKSPACE;
+  if (T > kPermSmallTokens && (!ws || ws_bytes < p.perm_bytes || ((uintptr_t)ws & 255u))) return MOE_EWORKSPACE;
   return hip_status(launch_permute(cfg, topk_idx, T, offsets, sorted_assign, assign_pos, (int32_t*)ws, stream));
 }
 
@@ -184,8 +183,13 @@ int moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, int3
   float* y = (float*)(b + p.off_y);
   hipError_t e;
   if ((e = launch_router_logits(cfg, w, x, T, lg, sg, stream)) != hipSuccess) return MOE_EHIP;
-  if ((e = launch_gating(cfg, lg, sg, T, idx, wt, sg, stream)) != hipSuccess) return MOE_EHIP;
-  if ((e = launch_permute(cfg, idx, T, offsets, sorted, pos, perm, stream)) != hipSuccess) return MOE_EHIP;
+  if (can_fuse_gate_permute(T)) {
+    if ((e = launch_gate_permute(cfg, lg, sg, T, idx, wt, sg, offsets, sorted, pos, stream)) != hipSuccess)
+      return MOE_EHIP;
+  } else {
+    if ((e = launch_gating(cfg, w, x, lg, sg, T, idx, wt, sg, stream)) != hipSuccess) return MOE_EHIP;
+    if ((e = launch_permute(cfg, idx, T, offsets, sorted, pos, perm, stream)) != hipSuccess) return MOE_EHIP;
+  }
   if ((e = launch_expert_ffn(cfg, w, x, offsets, sorted, T, h, stream)) != hipSuccess) return MOE_EHIP;
   if ((e = launch_down(cfg, w, h, offsets, sorted, T, y, stream)) != hipSuccess) return MOE_EHIP;
   return hip_status(launch_combine_gather(cfg, y, wt, sg, T, out, stream));

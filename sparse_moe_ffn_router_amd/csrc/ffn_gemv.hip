@@ -1,9 +1,12 @@
 // Expert kernels for few tokens per expert (decode-sized batches): each
 // weight row is streamed from HBM once per expert and applied to every token
-// routed to that expert.  Work unit: (active expert segment, tile of output
-// rows).  A group of 8 lanes owns one output row pair and splits its input
-// dimension in 16-byte pieces, so a wavefront keeps 8 rows streaming with
-// 128-byte contiguous segments each.
+// routed to that expert.
+//
+// Work unit: (active expert segment, tile of 32 row pairs).  The segment's
+// activation rows (x of its tokens, or its h rows) are staged in LDS, up to
+// 8 at a time.  A group of 8 lanes owns one row pair and splits the input
+// dimension in 16-byte pieces, 4 pieces per row in flight plus the next 4
+// prefetched, so a wavefront streams 16 rows in 128-byte segments.
 //
 // Sources: "qwen35moe - Forward-Pass Design", section "Shared-expert MoE
 // FFN" (SwiGLU experts, shared expert); "Phase 19: MoE - gpt-oss-20b",
@@ -15,9 +18,10 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kGroup = 8;                      // lanes per output row
-constexpr int kRowsPerBlock = kThreads / kGroup;  // 32
-constexpr int kTG = 16;                        // tokens per pass
+constexpr int kGroup = 8;                          // lanes per row pair
+constexpr int kPairsPerBlock = kThreads / kGroup;  // 32
+constexpr int kStage = 8;                          // activation rows staged at once
+constexpr int kU = 4;                              // pieces per row per pipeline step
 
 enum { W_F32 = 0, W_BF16 = 1, W_MXFP4 = 2 };
 
@@ -30,27 +34,20 @@ __device__ int find_segment(const int32_t* __restrict__ offsets, int nseg, int s
     const uint64_t m = __ballot(ne);
     const int c = __popcll(m);
     if (s < c) {
-      const uint64_t lower = lane ? (~0ull >> (64 - lane)) : 0ull;
-      const bool hit = ne && __popcll(m & lower) == s;
-      const uint64_t h = __ballot(hit);
-      return base + __ffsll((unsigned long long)h) - 1;
+      const bool hit = ne && __popcll(m & (lane ? (~0ull >> (64 - lane)) : 0ull)) == s;
+      return base + __ffsll((unsigned long long)__ballot(hit)) - 1;
     }
     s -= c;
   }
   return -1;
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.f + expf(-g)); }
-
-// Dot of one 16-byte weight piece with the matching activations of one
-// token, accumulated into acc.  `xp` points at the piece's first element.
 template <int WK> struct Piece;
 
+// bf16 weights: 8 elements per 16-byte piece, products summed in pairs.
 template <> struct Piece<W_BF16> {
-  static constexpr int kElems = 8;     // elements per lane piece
-  typedef uint4 W;
-  __device__ static W load(const void* row, int piece) { return reinterpret_cast<const uint4*>(row)[piece]; }
-  __device__ static float dot(const W& w, const uint16_t* xp, float acc, float) {
+  static constexpr int kElems = 8;
+  __device__ static float dot(uint4 w, const uint16_t* xp, float acc, float) {
     const uint4 xv = *reinterpret_cast<const uint4*>(xp);
     acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), __builtin_bit_cast(bf16x2_t, xv.x), acc, false);
     acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), __builtin_bit_cast(bf16x2_t, xv.y), acc, false);
@@ -62,14 +59,12 @@ template <> struct Piece<W_BF16> {
 
 template <> struct Piece<W_F32> {
   static constexpr int kElems = 4;
-  typedef float4 W;
-  __device__ static W load(const void* row, int piece) { return reinterpret_cast<const float4*>(row)[piece]; }
-  __device__ static float dot(const W& w, const float* xp, float acc, float) {
+  __device__ static float dot(uint4 w, const float* xp, float acc, float) {
     const float4 xv = *reinterpret_cast<const float4*>(xp);
-    acc = fmaf(w.x, xv.x, acc);
-    acc = fmaf(w.y, xv.y, acc);
-    acc = fmaf(w.z, xv.z, acc);
-    acc = fmaf(w.w, xv.w, acc);
+    acc = fmaf(__uint_as_float(w.x), xv.x, acc);
+    acc = fmaf(__uint_as_float(w.y), xv.y, acc);
+    acc = fmaf(__uint_as_float(w.z), xv.z, acc);
+    acc = fmaf(__uint_as_float(w.w), xv.w, acc);
     return acc;
   }
 };
@@ -79,37 +74,102 @@ template <> struct Piece<W_F32> {
 // E2M1 values times 2^(e-127) that bf16 represents).
 template <> struct Piece<W_MXFP4> {
   static constexpr int kElems = 32;
-  typedef uint4 W;
-  __device__ static W load(const void* row, int piece) { return reinterpret_cast<const uint4*>(row)[piece]; }
-  __device__ static float dot(const W& w, const uint16_t* xp, float acc, float scale) {
+  __device__ static float dot(uint4 w, const uint16_t* xp, float acc, float scale) {
     const uint4* xq = reinterpret_cast<const uint4*>(xp);
     const uint32_t words[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint4 xv = xq[q];
       const uint32_t cw = words[q];
-      const bf16x2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, scale, 0);
-      const bf16x2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, scale, 1);
-      const bf16x2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, scale, 2);
-      const bf16x2_t w3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, scale, 3);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(w0, __builtin_bit_cast(bf16x2_t, xv.x), acc, false);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(w1, __builtin_bit_cast(bf16x2_t, xv.y), acc, false);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(w2, __builtin_bit_cast(bf16x2_t, xv.z), acc, false);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(w3, __builtin_bit_cast(bf16x2_t, xv.w), acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, scale, 0),
+                                            __builtin_bit_cast(bf16x2_t, xv.x), acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, scale, 1),
+                                            __builtin_bit_cast(bf16x2_t, xv.y), acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, scale, 2),
+                                            __builtin_bit_cast(bf16x2_t, xv.z), acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, scale, 3),
+                                            __builtin_bit_cast(bf16x2_t, xv.w), acc, false);
     }
     return acc;
   }
 };
 
-template <typename XT> __device__ __forceinline__ float xscalar(const XT* p, int i);
-template <> __device__ __forceinline__ float xscalar<float>(const float* p, int i) { return p[i]; }
-template <> __device__ __forceinline__ float xscalar<uint16_t>(const uint16_t* p, int i) {
+template <typename XT> __device__ __forceinline__ float xscalar(const XT* p, size_t i);
+template <> __device__ __forceinline__ float xscalar<float>(const float* p, size_t i) { return p[i]; }
+template <> __device__ __forceinline__ float xscalar<uint16_t>(const uint16_t* p, size_t i) {
   return __uint_as_float((uint32_t)p[i] << 16);
 }
 template <typename XT> __device__ __forceinline__ void xstore(XT* p, size_t i, float v);
 template <> __device__ __forceinline__ void xstore<float>(float* p, size_t i, float v) { p[i] = v; }
 template <> __device__ __forceinline__ void xstore<uint16_t>(uint16_t* p, size_t i, float v) {
   p[i] = (uint16_t)f32_to_bf16(v);
+}
+
+// acc[r][i] += row r . xs[i] over K inputs, this lane's share (pieces
+// lig, lig+8, ...).  Rows are streamed with the next kU pieces prefetched.
+template <typename XT, int WK, int NT>
+__device__ __forceinline__ void rows2_dot(const uint4* r0, const uint4* r1, const uint8_t* s0, const uint8_t* s1,
+                                          const XT* xs, int K, int lig, float (&acc)[2][kStage]) {
+  using P = Piece<WK>;
+  const int npieces = K / P::kElems;
+  uint4 w0[kU], w1[kU];
+  uint8_t c0[kU], c1[kU];
+  auto fetch = [&](int pc, uint4 (&a)[kU], uint4 (&b)[kU], uint8_t (&sa)[kU], uint8_t (&sb)[kU]) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int q = pc + u * kGroup;
+      const bool ok = q < npieces;
+      a[u] = ok ? r0[q] : make_uint4(0, 0, 0, 0);
+      b[u] = ok ? r1[q] : make_uint4(0, 0, 0, 0);
+      if (WK == W_MXFP4) {
+        sa[u] = ok ? s0[q] : 0;
+        sb[u] = ok ? s1[q] : 0;
+      }
+    }
+  };
+  fetch(lig, w0, w1, c0, c1);
+  for (int pc = lig; pc < npieces; pc += kU * kGroup) {
+    uint4 n0[kU], n1[kU];
+    uint8_t d0[kU], d1[kU];
+    fetch(pc + kU * kGroup, n0, n1, d0, d1);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int q = pc + u * kGroup;
+      if (q < npieces) {
+        const float sc0 = WK == W_MXFP4 ? e8m0_to_f32(c0[u]) : 1.f;
+        const float sc1 = WK == W_MXFP4 ? e8m0_to_f32(c1[u]) : 1.f;
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+          const XT* xp = xs + (size_t)i * K + (size_t)q * P::kElems;
+          acc[0][i] = P::dot(w0[u], xp, acc[0][i], sc0);
+          acc[1][i] = P::dot(w1[u], xp, acc[1][i], sc1);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      w0[u] = n0[u];
+      w1[u] = n1[u];
+      c0[u] = d0[u];
+      c1[u] = d1[u];
+    }
+  }
+}
+
+template <typename XT, int WK>
+__device__ __forceinline__ void rows2_dot_n(int nt, const uint4* r0, const uint4* r1, const uint8_t* s0,
+                                            const uint8_t* s1, const XT* xs, int K, int lig,
+                                            float (&acc)[2][kStage]) {
+  switch (nt) {
+    case 1: rows2_dot<XT, WK, 1>(r0, r1, s0, s1, xs, K, lig, acc); break;
+    case 2: rows2_dot<XT, WK, 2>(r0, r1, s0, s1, xs, K, lig, acc); break;
+    case 3: rows2_dot<XT, WK, 3>(r0, r1, s0, s1, xs, K, lig, acc); break;
+    case 4: rows2_dot<XT, WK, 4>(r0, r1, s0, s1, xs, K, lig, acc); break;
+    case 5: rows2_dot<XT, WK, 5>(r0, r1, s0, s1, xs, K, lig, acc); break;
+    case 6: rows2_dot<XT, WK, 6>(r0, r1, s0, s1, xs, K, lig, acc); break;
+    case 7: rows2_dot<XT, WK, 7>(r0, r1, s0, s1, xs, K, lig, acc); break;
+    default: rows2_dot<XT, WK, 8>(r0, r1, s0, s1, xs, K, lig, acc); break;
+  }
 }
 
 // Row byte pitch of a weight matrix with `cols` inputs.
@@ -133,28 +193,28 @@ struct GateUpArgs {
 };
 
 // h[p][f] = act(gate row f . x_t, up row f . x_t) for every sorted position
-// p of the block's expert segment.  Grid: (segment slot, row tile).
+// p of the block's expert segment.  Grid: (segment slot, tile of 32 features).
 template <typename XT, int WK>
 __global__ __launch_bounds__(kThreads) void k_gateup_gemv(GateUpArgs a) {
-  using P = Piece<WK>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  XT* xs = reinterpret_cast<XT*>(smem);
   const int nseg = a.E + a.shared;
   const int e = find_segment(a.offsets, nseg, blockIdx.x);
   if (e < 0) return;
   const bool sh = e == a.E;
   const int Fe = sh ? a.Fs : a.F;
+  if (blockIdx.y * kPairsPerBlock >= Fe) return;
   const int grp = threadIdx.x / kGroup, lig = threadIdx.x & (kGroup - 1);
-  const int f = blockIdx.y * kRowsPerBlock + grp;
-  if (blockIdx.y * kRowsPerBlock >= Fe) return;
+  const int f = blockIdx.y * kPairsPerBlock + grp;
   const bool active = f < Fe;
-  const int fr = active ? f : Fe - 1;   // inactive groups still join the shuffles
-  // the two input rows of feature fr
-  const uint8_t *rg, *ru;
-  const uint8_t *sg = nullptr, *su = nullptr;
-  const int rb = (int)row_bytes<WK>(a.H);
+  const int fr = active ? f : Fe - 1;
+  const uint8_t *rg, *ru, *sg = nullptr, *su = nullptr;
+  constexpr int WS = WK == W_MXFP4 ? W_BF16 : WK;  // shared-expert element kind
   if (sh) {
-    rg = (const uint8_t*)a.sh_gate_w + (size_t)fr * row_bytes<(WK == W_MXFP4 ? W_BF16 : WK)>(a.H);
-    ru = (const uint8_t*)a.sh_up_w + (size_t)fr * row_bytes<(WK == W_MXFP4 ? W_BF16 : WK)>(a.H);
+    rg = (const uint8_t*)a.sh_gate_w + (size_t)fr * row_bytes<WS>(a.H);
+    ru = (const uint8_t*)a.sh_up_w + (size_t)fr * row_bytes<WS>(a.H);
   } else if (a.oai) {
+    const size_t rb = row_bytes<WK>(a.H);
     rg = (const uint8_t*)a.gate_w + ((size_t)e * 2 * a.F + 2 * fr) * rb;
     ru = rg + rb;
     if (WK == W_MXFP4) {
@@ -162,101 +222,55 @@ __global__ __launch_bounds__(kThreads) void k_gateup_gemv(GateUpArgs a) {
       su = sg + a.H / 32;
     }
   } else {
+    const size_t rb = row_bytes<WK>(a.H);
     rg = (const uint8_t*)a.gate_w + ((size_t)e * a.F + fr) * rb;
     ru = (const uint8_t*)a.up_w + ((size_t)e * a.F + fr) * rb;
   }
   const int p0 = a.offsets[e];
   const int n = a.offsets[e + 1] - p0;
   const int64_t nas = (int64_t)a.T * a.k;
-  const XT* x = (const XT*)a.x;
   float bg = 0.f, bu = 0.f;
   if (a.oai && !sh && a.gate_up_b) {
-    bg = xscalar<XT>((const XT*)a.gate_up_b, e * 2 * a.F + 2 * fr);
-    bu = xscalar<XT>((const XT*)a.gate_up_b, e * 2 * a.F + 2 * fr + 1);
+    bg = xscalar<XT>((const XT*)a.gate_up_b, (size_t)e * 2 * a.F + 2 * fr);
+    bu = xscalar<XT>((const XT*)a.gate_up_b, (size_t)e * 2 * a.F + 2 * fr + 1);
   }
-  for (int tb = 0; tb < n; tb += kTG) {
-    const int nt = min(kTG, n - tb);
-    int tok[kTG];
-#pragma unroll
-    for (int i = 0; i < kTG; ++i) {
-      const int sa = i < nt ? a.sorted_assign[p0 + tb + i] : 0;
-      tok[i] = sa < nas ? sa / a.k : (int)(sa - nas);
+  const int xpieces = a.H * (int)sizeof(XT) / 16;  // 16-byte pieces per x row
+  for (int tb = 0; tb < n; tb += kStage) {
+    const int nt = min(kStage, n - tb);
+    if (tb) __syncthreads();
+    for (int i = threadIdx.x; i < nt * xpieces; i += kThreads) {
+      const int j = i / xpieces, q = i - j * xpieces;
+      const int sa = a.sorted_assign[p0 + tb + j];
+      const int t = sa < nas ? sa / a.k : (int)(sa - nas);
+      reinterpret_cast<uint4*>(xs)[i] = reinterpret_cast<const uint4*>((const XT*)a.x + (size_t)t * a.H)[q];
     }
-    float ag[kTG], au[kTG];
+    __syncthreads();
+    float acc[2][kStage];
 #pragma unroll
-    for (int i = 0; i < kTG; ++i) ag[i] = au[i] = 0.f;
-    if (sh && WK == W_MXFP4) {
-      // shared expert rows are bf16 even when routed experts are MXFP4
-      using PB = Piece<W_BF16>;
-      const int npieces = a.H / PB::kElems;
-      for (int pc = lig; pc < npieces; pc += kGroup) {
-        const uint4 wg = PB::load(rg, pc), wu = PB::load(ru, pc);
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
-        for (int i = 0; i < kTG; ++i)
-          if (i < nt) {
-            const uint16_t* xp = (const uint16_t*)x + (size_t)tok[i] * a.H + pc * PB::kElems;
-            ag[i] = PB::dot(wg, xp, ag[i], 1.f);
-            au[i] = PB::dot(wu, xp, au[i], 1.f);
-          }
-      }
-    } else {
-      const int npieces = a.H / P::kElems;
-      int pc = lig;
-      // four pieces per row in flight per lane
-      for (; pc + 3 * kGroup < npieces; pc += 4 * kGroup) {
-        typename P::W wg[4], wu[4];
-        float sgv[4] = {1.f, 1.f, 1.f, 1.f}, suv[4] = {1.f, 1.f, 1.f, 1.f};
+      for (int i = 0; i < kStage; ++i) acc[r][i] = 0.f;
+    if (sh || WK != W_MXFP4)
+      rows2_dot_n<XT, WS>(nt, (const uint4*)rg, (const uint4*)ru, sg, su, xs, a.H, lig, acc);
+    else
+      rows2_dot_n<XT, WK>(nt, (const uint4*)rg, (const uint4*)ru, sg, su, xs, a.H, lig, acc);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          wg[u] = P::load(rg, pc + u * kGroup);
-          wu[u] = P::load(ru, pc + u * kGroup);
-          if (WK == W_MXFP4) {
-            sgv[u] = e8m0_to_f32(sg[pc + u * kGroup]);
-            suv[u] = e8m0_to_f32(su[pc + u * kGroup]);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int i = 0; i < kTG; ++i)
-            if (i < nt) {
-              const XT* xp = x + (size_t)tok[i] * a.H + (size_t)(pc + u * kGroup) * P::kElems;
-              ag[i] = P::dot(wg[u], xp, ag[i], sgv[u]);
-              au[i] = P::dot(wu[u], xp, au[i], suv[u]);
-            }
-      }
-      for (; pc < npieces; pc += kGroup) {
-        const typename P::W wg = P::load(rg, pc), wu = P::load(ru, pc);
-        const float sgv = WK == W_MXFP4 ? e8m0_to_f32(sg[pc]) : 1.f;
-        const float suv = WK == W_MXFP4 ? e8m0_to_f32(su[pc]) : 1.f;
-#pragma unroll
-        for (int i = 0; i < kTG; ++i)
-          if (i < nt) {
-            const XT* xp = x + (size_t)tok[i] * a.H + (size_t)pc * P::kElems;
-            ag[i] = P::dot(wg, xp, ag[i], sgv);
-            au[i] = P::dot(wu, xp, au[i], suv);
-          }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kTG; ++i) {
-#pragma unroll
-      for (int o = 1; o < kGroup; o <<= 1) {
-        ag[i] += __shfl_xor(ag[i], o, kWave);
-        au[i] += __shfl_xor(au[i], o, kWave);
-      }
+    for (int i = 0; i < kStage; ++i) {
+      acc[0][i] = group8_sum(acc[0][i]);
+      acc[1][i] = group8_sum(acc[1][i]);
     }
     if (active) {
 #pragma unroll
-      for (int i = 0; i < kTG; ++i) {
-        if (i < nt && (i & (kGroup - 1)) == lig) {
+      for (int i = 0; i < kStage; ++i) {
+        if (i < nt && i == lig) {
           float hv;
           if (a.oai && !sh) {
-            float g = fminf(ag[i] + bg, a.limit);
-            float u = fminf(fmaxf(au[i] + bu, -a.limit), a.limit);
+            const float g = fminf(acc[0][i] + bg, a.limit);
+            const float u = fminf(fmaxf(acc[1][i] + bu, -a.limit), a.limit);
             hv = (u + 1.f) * (g / (1.f + expf(-a.alpha * g)));
           } else {
-            hv = silu(ag[i]) * au[i];
+            const float g = acc[0][i];
+            hv = g / (1.f + expf(-g)) * acc[1][i];
           }
           const int p = p0 + tb + i;
           const size_t row = p < nas ? (size_t)p * a.F : (size_t)nas * a.F + (size_t)(p - nas) * a.Fs;
@@ -280,70 +294,74 @@ struct DownArgs {
 };
 
 // y[a][o] = down row o . h[p] (+ bias) for every sorted position p of the
-// segment, written at the row of its assignment id a.
+// segment, written at the row of its assignment id a.  Grid: (segment slot,
+// tile of 64 output rows); a group of 8 lanes owns rows o and o + 32.
 template <typename XT, int WK>
 __global__ __launch_bounds__(kThreads) void k_down_gemv(DownArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  XT* hs = reinterpret_cast<XT*>(smem);
   const int nseg = a.E + a.shared;
   const int e = find_segment(a.offsets, nseg, blockIdx.x);
   if (e < 0) return;
   const bool sh = e == a.E;
   const int Fe = sh ? a.Fs : a.F;
+  const int obase = blockIdx.y * 2 * kPairsPerBlock;
+  if (obase >= a.H) return;
   const int grp = threadIdx.x / kGroup, lig = threadIdx.x & (kGroup - 1);
-  const int o = blockIdx.y * kRowsPerBlock + grp;
-  if (blockIdx.y * kRowsPerBlock >= a.H) return;
-  const bool active = o < a.H;
-  const int orow = active ? o : a.H - 1;
+  const int o0 = obase + grp, o1 = obase + kPairsPerBlock + grp;
+  const int q0 = min(o0, a.H - 1), q1 = min(o1, a.H - 1);
+  constexpr int WS = WK == W_MXFP4 ? W_BF16 : WK;
+  const uint8_t *r0, *r1, *s0 = nullptr, *s1 = nullptr;
+  if (sh) {
+    r0 = (const uint8_t*)a.sh_down_w + (size_t)q0 * row_bytes<WS>(a.Fs);
+    r1 = (const uint8_t*)a.sh_down_w + (size_t)q1 * row_bytes<WS>(a.Fs);
+  } else {
+    const size_t rb = row_bytes<WK>(a.F);
+    r0 = (const uint8_t*)a.down_w + ((size_t)e * a.H + q0) * rb;
+    r1 = (const uint8_t*)a.down_w + ((size_t)e * a.H + q1) * rb;
+    if (WK == W_MXFP4) {
+      s0 = a.scales + ((size_t)e * a.H + q0) * (a.F / 32);
+      s1 = a.scales + ((size_t)e * a.H + q1) * (a.F / 32);
+    }
+  }
   const int p0 = a.offsets[e];
   const int n = a.offsets[e + 1] - p0;
   const int64_t nas = (int64_t)a.T * a.k;
   const XT* hb = (const XT*)a.h;
-  const XT* hbase = sh ? hb + (size_t)nas * a.F : hb;  // shared rows follow the routed rows
-  const int prow0 = sh ? p0 - (int)nas : p0;
-  float bias = 0.f;
-  if (!sh && a.down_b) bias = xscalar<XT>((const XT*)a.down_b, e * a.H + orow);
-  for (int tb = 0; tb < n; tb += kTG) {
-    const int nt = min(kTG, n - tb);
-    float acc[kTG];
+  const XT* hbase = sh ? hb + (size_t)nas * a.F + (size_t)(p0 - nas) * a.Fs : hb + (size_t)p0 * a.F;
+  float b0 = 0.f, b1 = 0.f;
+  if (!sh && a.down_b) {
+    b0 = xscalar<XT>((const XT*)a.down_b, (size_t)e * a.H + q0);
+    b1 = xscalar<XT>((const XT*)a.down_b, (size_t)e * a.H + q1);
+  }
+  const int hpieces = Fe * (int)sizeof(XT) / 16;
+  for (int tb = 0; tb < n; tb += kStage) {
+    const int nt = min(kStage, n - tb);
+    if (tb) __syncthreads();
+    for (int i = threadIdx.x; i < nt * hpieces; i += kThreads)
+      reinterpret_cast<uint4*>(hs)[i] = reinterpret_cast<const uint4*>(hbase + (size_t)tb * Fe)[i];
+    __syncthreads();
+    float acc[2][kStage];
 #pragma unroll
-    for (int i = 0; i < kTG; ++i) acc[i] = 0.f;
-    if (sh || WK != W_MXFP4) {
-      constexpr int WB = WK == W_F32 ? W_F32 : W_BF16;
-      using P = Piece<WB>;
-      const uint8_t* row = sh ? (const uint8_t*)a.sh_down_w + (size_t)orow * row_bytes<WB>(a.Fs)
-                              : (const uint8_t*)a.down_w + ((size_t)e * a.H + orow) * row_bytes<WB>(a.F);
-      const int npieces = Fe / P::kElems;
-      for (int pc = lig; pc < npieces; pc += kGroup) {
-        const typename P::W w = P::load(row, pc);
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
-        for (int i = 0; i < kTG; ++i)
-          if (i < nt) acc[i] = P::dot(w, hbase + (size_t)(prow0 + tb + i) * Fe + (size_t)pc * P::kElems, acc[i], 1.f);
-      }
-    } else {
-      using P = Piece<W_MXFP4>;
-      const uint8_t* row = (const uint8_t*)a.down_w + ((size_t)e * a.H + orow) * row_bytes<W_MXFP4>(a.F);
-      const uint8_t* srow = a.scales + ((size_t)e * a.H + orow) * (a.F / 32);
-      const int npieces = a.F / P::kElems;
-      for (int pc = lig; pc < npieces; pc += kGroup) {
-        const uint4 w = P::load(row, pc);
-        const float sc = e8m0_to_f32(srow[pc]);
+      for (int i = 0; i < kStage; ++i) acc[r][i] = 0.f;
+    if (sh || WK != W_MXFP4)
+      rows2_dot_n<XT, WS>(nt, (const uint4*)r0, (const uint4*)r1, s0, s1, hs, Fe, lig, acc);
+    else
+      rows2_dot_n<XT, WK>(nt, (const uint4*)r0, (const uint4*)r1, s0, s1, hs, Fe, lig, acc);
 #pragma unroll
-        for (int i = 0; i < kTG; ++i)
-          if (i < nt)
-            acc[i] = P::dot(w, (const uint16_t*)hbase + (size_t)(prow0 + tb + i) * Fe + (size_t)pc * P::kElems, acc[i], sc);
-      }
+    for (int i = 0; i < kStage; ++i) {
+      acc[0][i] = group8_sum(acc[0][i]);
+      acc[1][i] = group8_sum(acc[1][i]);
     }
 #pragma unroll
-    for (int i = 0; i < kTG; ++i)
-#pragma unroll
-      for (int q = 1; q < kGroup; q <<= 1) acc[i] += __shfl_xor(acc[i], q, kWave);
-    if (active) {
-#pragma unroll
-      for (int i = 0; i < kTG; ++i)
-        if (i < nt && (i & (kGroup - 1)) == lig) {
-          const int asg = a.sorted_assign[p0 + tb + i];
-          a.y[(size_t)asg * a.H + o] = acc[i] + bias;
-        }
-    }
+    for (int i = 0; i < kStage; ++i)
+      if (i < nt && i == lig) {
+        const int asg = a.sorted_assign[p0 + tb + i];
+        if (o0 < a.H) a.y[(size_t)asg * a.H + o0] = acc[0][i] + b0;
+        if (o1 < a.H) a.y[(size_t)asg * a.H + o1] = acc[1][i] + b1;
+      }
   }
 }
 
@@ -382,7 +400,6 @@ hipError_t launch_gateup_mfma(const moe_config* c, const moe_weights* w, const v
                               const int32_t* sorted_assign, int32_t T, void* h, hipStream_t s);
 hipError_t launch_down_mfma(const moe_config* c, const moe_weights* w, const void* h, const int32_t* offsets,
                             const int32_t* sorted_assign, int32_t T, float* y, hipStream_t s);
-
 bool mfma_shapes_ok(const moe_config* c);
 
 static int max_segments(const moe_config* c, int32_t T) {
@@ -390,11 +407,12 @@ static int max_segments(const moe_config* c, int32_t T) {
   return (int)(nk < c->n_expert ? nk : c->n_expert) + (c->shared_ff > 0 ? 1 : 0);
 }
 
+static size_t stage_rows(int32_t T) { return (size_t)(T < kStage ? T : kStage); }
+
 hipError_t launch_expert_ffn(const moe_config* c, const moe_weights* w, const void* x, const int32_t* offsets,
                              const int32_t* sorted_assign, int32_t T, void* h, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (T > kGemvMaxT && mfma_shapes_ok(c))
-    return launch_gateup_mfma(c, w, x, offsets, sorted_assign, T, h, s);
+  if (T > kGemvMaxT && mfma_shapes_ok(c)) return launch_gateup_mfma(c, w, x, offsets, sorted_assign, T, h, s);
   GateUpArgs a;
   const bool oai = c->act == MOE_ACT_SWIGLU_OAI;
   a.x = x;
@@ -410,21 +428,22 @@ hipError_t launch_expert_ffn(const moe_config* c, const moe_weights* w, const vo
   a.T = T; a.k = c->top_k; a.H = c->hidden; a.E = c->n_expert; a.F = c->expert_ff; a.Fs = c->shared_ff;
   a.shared = c->shared_ff > 0; a.oai = oai; a.alpha = c->act_alpha; a.limit = c->act_limit;
   const int fmax = c->expert_ff > c->shared_ff ? c->expert_ff : c->shared_ff;
-  dim3 grid(max_segments(c, T), (fmax + kRowsPerBlock - 1) / kRowsPerBlock);
+  dim3 grid(max_segments(c, T), (fmax + kPairsPerBlock - 1) / kPairsPerBlock);
+  const size_t esz = c->x_dtype == MOE_DTYPE_F32 ? 4 : 2;
+  const size_t lds = stage_rows(T) * c->hidden * esz;
   if (c->x_dtype == MOE_DTYPE_F32)
-    k_gateup_gemv<float, W_F32><<<grid, kThreads, 0, s>>>(a);
+    k_gateup_gemv<float, W_F32><<<grid, kThreads, lds, s>>>(a);
   else if (c->w_dtype == MOE_DTYPE_BF16)
-    k_gateup_gemv<uint16_t, W_BF16><<<grid, kThreads, 0, s>>>(a);
+    k_gateup_gemv<uint16_t, W_BF16><<<grid, kThreads, lds, s>>>(a);
   else
-    k_gateup_gemv<uint16_t, W_MXFP4><<<grid, kThreads, 0, s>>>(a);
+    k_gateup_gemv<uint16_t, W_MXFP4><<<grid, kThreads, lds, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_down(const moe_config* c, const moe_weights* w, const void* h, const int32_t* offsets,
                        const int32_t* sorted_assign, int32_t T, float* y, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (T > kGemvMaxT && mfma_shapes_ok(c))
-    return launch_down_mfma(c, w, h, offsets, sorted_assign, T, y, s);
+  if (T > kGemvMaxT && mfma_shapes_ok(c)) return launch_down_mfma(c, w, h, offsets, sorted_assign, T, y, s);
   DownArgs a;
   a.h = h;
   a.down_w = w->down_w;
@@ -436,13 +455,16 @@ hipError_t launch_down(const moe_config* c, const moe_weights* w, const void* h,
   a.y = y;
   a.T = T; a.k = c->top_k; a.H = c->hidden; a.E = c->n_expert; a.F = c->expert_ff; a.Fs = c->shared_ff;
   a.shared = c->shared_ff > 0;
-  dim3 grid(max_segments(c, T), (c->hidden + kRowsPerBlock - 1) / kRowsPerBlock);
+  dim3 grid(max_segments(c, T), (c->hidden + 2 * kPairsPerBlock - 1) / (2 * kPairsPerBlock));
+  const size_t esz = c->x_dtype == MOE_DTYPE_F32 ? 4 : 2;
+  const int fmax = c->expert_ff > c->shared_ff ? c->expert_ff : c->shared_ff;
+  const size_t lds = stage_rows(T) * fmax * esz;
   if (c->x_dtype == MOE_DTYPE_F32)
-    k_down_gemv<float, W_F32><<<grid, kThreads, 0, s>>>(a);
+    k_down_gemv<float, W_F32><<<grid, kThreads, lds, s>>>(a);
   else if (c->w_dtype == MOE_DTYPE_BF16)
-    k_down_gemv<uint16_t, W_BF16><<<grid, kThreads, 0, s>>>(a);
+    k_down_gemv<uint16_t, W_BF16><<<grid, kThreads, lds, s>>>(a);
   else
-    k_down_gemv<uint16_t, W_MXFP4><<<grid, kThreads, 0, s>>>(a);
+    k_down_gemv<uint16_t, W_MXFP4><<<grid, kThreads, lds, s>>>(a);
   return hipGetLastError();
 }
 

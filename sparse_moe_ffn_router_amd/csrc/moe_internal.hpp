@@ -17,9 +17,8 @@ constexpr int kMaxTopK = 32;
 // GEMV-style expert kernels (one weight stream, few tokens per expert) are
 // used while T <= this; above it bf16 layers go to the MFMA grouped GEMM.
 constexpr int kGemvMaxT = 64;
-// Permutation: up to this many assignments one workgroup does everything.
-constexpr int kPermSmallMax = 2048;
-constexpr int kPermChunk = 256;
+// Permutation: up to this many tokens one workgroup does everything.
+constexpr int kPermSmallTokens = 256;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -47,15 +46,69 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+// DPP lane exchanges (gfx9 encodings): quad permutes, mirrors within a
+// 16-lane row.  Used for the butterfly steps xor 1, xor 2, then half-row and
+// row swaps, which leave the full reduction of each 8- or 16-lane group in
+// every lane of the group.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i inside each 8 lanes
+constexpr int kDppMirror = 0x140;      // lane i <-> 15-i inside each 16 lanes
+
+template <int CTRL> __device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL> __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Sum over each group of 8 consecutive lanes, result in all 8 lanes.
+__device__ __forceinline__ float group8_sum(float v) {
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
   return v;
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+// Sum over each 16-lane row, result in all 16 lanes.
+__device__ __forceinline__ float row16_sum(float v) {
+  v = group8_sum(v);
+  v += dpp<kDppMirror>(v);
   return v;
+}
+// Wave-wide sum, wave-uniform result; the same order for every call.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (a + b) + (c + d);
+}
+__device__ __forceinline__ uint64_t u64max(uint64_t a, uint64_t b) { return a > b ? a : b; }
+// Wave-wide maximum of a 64-bit key, wave-uniform result.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+#define MOE_U64_STEP(CTRL)                                              \
+  {                                                                    \
+    const uint32_t l2 = dpp_u32<CTRL>(lo), h2 = dpp_u32<CTRL>(hi);    \
+    const uint64_t o = ((uint64_t)h2 << 32) | l2;                      \
+    const uint64_t m = u64max(((uint64_t)hi << 32) | lo, o);           \
+    lo = (uint32_t)m;                                                  \
+    hi = (uint32_t)(m >> 32);                                          \
+  }
+  MOE_U64_STEP(kDppXor1)
+  MOE_U64_STEP(kDppXor2)
+  MOE_U64_STEP(kDppHalfMirror)
+  MOE_U64_STEP(kDppMirror)
+#undef MOE_U64_STEP
+  uint64_t r = 0;
+#pragma unroll
+  for (int row = 0; row < 4; ++row) {
+    const uint64_t x = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, row * 16) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)lo, row * 16);
+    r = u64max(r, x);
+  }
+  return r;
 }
 
 // E8M0 exponent byte -> 2^(s-127) as fp32 (s = 0 gives 2^-127, subnormal).
@@ -84,10 +137,20 @@ int check_config(const moe_config* c);
 // Launchers (return hipError_t of the last launch).
 hipError_t launch_router_logits(const moe_config* c, const moe_weights* w, const void* x, int32_t T,
                                 float* logits, float* sgate_pre, hipStream_t s);
-hipError_t launch_gating(const moe_config* c, const float* logits, const float* sgate_pre, int32_t T,
-                         int32_t* topk_idx, float* topk_w, float* sgate, hipStream_t s);
+hipError_t launch_gating(const moe_config* c, const moe_weights* w, const void* x, const float* logits,
+                         const float* sgate_pre, int32_t T, int32_t* topk_idx, float* topk_w, float* sgate,
+                         hipStream_t s);
+// Whether the shared-gate dot is computed by the router-product kernel
+// (few tokens) rather than by the gating kernel.
+bool sgate_in_router(const moe_config* c, int32_t T);
 hipError_t launch_permute(const moe_config* c, const int32_t* topk_idx, int32_t T, int32_t* offsets,
                           int32_t* sorted_assign, int32_t* assign_pos, int32_t* scratch, hipStream_t s);
+size_t permute_scratch_bytes(int32_t T, int32_t E);
+// Gating + permutation in one launch for small batches.
+bool can_fuse_gate_permute(int32_t T);
+hipError_t launch_gate_permute(const moe_config* c, const float* logits, const float* sgate_pre, int32_t T,
+                               int32_t* topk_idx, float* topk_w, float* sgate, int32_t* offsets,
+                               int32_t* sorted_assign, int32_t* assign_pos, hipStream_t s);
 hipError_t launch_expert_ffn(const moe_config* c, const moe_weights* w, const void* x, const int32_t* offsets,
                              const int32_t* sorted_assign, int32_t T, void* h, hipStream_t s);
 hipError_t launch_down(const moe_config* c, const moe_weights* w, const void* h, const int32_t* offsets,

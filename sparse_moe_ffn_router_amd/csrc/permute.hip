@@ -1,184 +1,245 @@
 // Token -> expert permutation: a stable counting sort of the T*k
-// token-expert assignments a = t*k + j by expert id.  Counts use LDS
-// atomics; positions never depend on atomic return order: inside a
-// wavefront a lane's rank is the number of lower lanes holding the same
-// expert (ballot + popcount), and wavefront steps run in assignment order,
-// so the result is deterministic and ascending in a inside each segment.
+// token-expert assignments a = t*k + j by expert id.
+//
+// A token picks each expert at most once, so inside an expert's segment
+// ascending a is ascending token.  For every expert the kernels build a
+// bitmask over a block of tokens (bit t set when token t picked the expert)
+// with LDS atomic ORs, whose result does not depend on their order; an
+// assignment's rank in its segment is then the popcount of the mask below
+// its token plus the counts of earlier blocks.  Positions are therefore
+// deterministic and need no serial pass.
 //
 // The pages only imply this step ("qwen35moe - Forward-Pass Design",
 // section "K80 GPU decode": grouped expert launches; section "Batched
 // prefill": tokens sharing an expert stream its weights once).
+#include "gating.hpp"
 #include "moe_internal.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kSmallThreads = 1024;
+constexpr int kThreadsBig = 1024;
+constexpr int kBlockTokens = 256;             // tokens per mask block
+constexpr int kWords = kBlockTokens / 64;     // 64-bit words per expert mask
 
-// Places one wavefront's 64 assignments [a0, a0+64) given the running
-// per-expert fill pointers `fill` (LDS); returns nothing, writes outputs.
-__device__ __forceinline__ void place_wave(const int32_t* __restrict__ topk_idx, int64_t n, int64_t a0,
-                                           int32_t* fill, int32_t* __restrict__ sorted_assign,
-                                           int32_t* __restrict__ assign_pos) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t a = a0 + lane;
-  const int e = a < n ? topk_idx[a] : -1;
-  const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  uint64_t pending = __ballot(e >= 0);
-  int rank = 0, base = 0;
-  bool leader = false;
-  int group = 0;
-  while (pending) {
-    const int src = __ffsll((unsigned long long)pending) - 1;
-    const int v = __shfl(e, src, kWave);
-    const uint64_t m = __ballot(e == v);
-    if (e == v) {
-      rank = __popcll(m & lower);
-      group = __popcll(m);
-      leader = lane == src;
-      base = fill[v];
-    }
-    pending &= ~m;
-  }
-  if (e >= 0) {
-    const int pos = base + rank;
-    sorted_assign[pos] = (int32_t)a;
-    assign_pos[a] = pos;
-  }
-  // all lanes read `fill` above before any leader advances it
-  __builtin_amdgcn_s_waitcnt(0);
-  if (e >= 0 && leader) fill[e] = base + group;
-  __builtin_amdgcn_s_waitcnt(0);
-}
+__device__ __forceinline__ uint64_t lower_bits(int t) { return t ? (~0ull >> (64 - t)) : 0ull; }
 
-// Whole permutation in one workgroup (n = T*k small): LDS histogram,
-// exclusive scan, then wave 0 places the assignments in order.
-__global__ __launch_bounds__(kSmallThreads) void k_permute_small(const int32_t* __restrict__ topk_idx, int32_t T,
-                                                                 int32_t k, int32_t E, int32_t shared,
-                                                                 int32_t* __restrict__ offsets,
-                                                                 int32_t* __restrict__ sorted_assign,
-                                                                 int32_t* __restrict__ assign_pos) {
-  __shared__ int32_t cnt[kMaxExperts + 2];
-  __shared__ int32_t wsum[kSmallThreads / kWave];
-  const int tid = threadIdx.x;
-  const int64_t n = (int64_t)T * k;
-  for (int e = tid; e <= E; e += kSmallThreads) cnt[e] = 0;
-  __syncthreads();
-  for (int64_t a = tid; a < n; a += kSmallThreads) atomicAdd(&cnt[topk_idx[a]], 1);
-  __syncthreads();
-  // exclusive scan over E entries (E <= 1024: one per thread)
-  const int lane = tid & (kWave - 1), wid = tid / kWave;
-  int v = tid < E ? cnt[tid] : 0;
+// Exclusive scan of v over the first n threads of a 1024-thread block
+// (n <= 1024); returns the exclusive prefix, *total gets the sum.
+__device__ int block_excl_scan(int v, int* wsum, int* total) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   int incl = v;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
-    int u = __shfl_up(incl, o, kWave);
+    const int u = __shfl_up(incl, o, kWave);
     if (lane >= o) incl += u;
   }
   if (lane == kWave - 1) wsum[wid] = incl;
   __syncthreads();
-  int before = 0;
-  for (int w2 = 0; w2 < wid; ++w2) before += wsum[w2];
-  const int excl = before + incl - v;
+  int before = 0, all = 0;
+  for (int w2 = 0; w2 < kThreadsBig / kWave; ++w2) {
+    const int s = wsum[w2];
+    before += w2 < wid ? s : 0;
+    all += s;
+  }
+  *total = all;
+  return before + incl - v;
+}
+
+// Permutation of up to kBlockTokens tokens inside one workgroup, from the
+// picks in LDS (idx_s, T*k entries).
+__device__ void permute_one_block(const int32_t* idx_s, int32_t T, int32_t k, int32_t E, int32_t shared,
+                                  uint64_t* mask, int* base, int* wsum, int32_t* __restrict__ offsets,
+                                  int32_t* __restrict__ sorted_assign, int32_t* __restrict__ assign_pos) {
+  const int tid = threadIdx.x;
+  const int n = T * k;
+  const int W = (T + 63) / 64;
+  for (int i = tid; i < E * W; i += kThreadsBig) mask[i] = 0ull;
   __syncthreads();
+  for (int a = tid; a < n; a += kThreadsBig) {
+    const int t = a / k;
+    atomicOr((unsigned long long*)&mask[idx_s[a] * W + t / 64], 1ull << (t & 63));
+  }
+  __syncthreads();
+  int cnt = 0;
+  if (tid < E)
+    for (int w = 0; w < W; ++w) cnt += __popcll(mask[tid * W + w]);
+  int total;
+  const int excl = block_excl_scan(tid < E ? cnt : 0, wsum, &total);
   if (tid < E) {
-    cnt[tid] = excl;
+    base[tid] = excl;
     offsets[tid] = excl;
   }
   if (tid == 0) {
-    offsets[E] = (int32_t)n;
-    if (shared) offsets[E + 1] = (int32_t)(n + T);
+    offsets[E] = n;
+    if (shared) offsets[E + 1] = n + T;
   }
   __syncthreads();
-  if (wid == 0)
-    for (int64_t a0 = 0; a0 < n; a0 += kWave) place_wave(topk_idx, n, a0, cnt, sorted_assign, assign_pos);
+  for (int a = tid; a < n; a += kThreadsBig) {
+    const int t = a / k, e = idx_s[a];
+    int r = __popcll(mask[e * W + t / 64] & lower_bits(t & 63));
+    for (int w = 0; w < t / 64; ++w) r += __popcll(mask[e * W + w]);
+    const int pos = base[e] + r;
+    sorted_assign[pos] = a;
+    assign_pos[a] = pos;
+  }
   if (shared)
-    for (int t = tid; t < T; t += kSmallThreads) {
-      sorted_assign[n + t] = (int32_t)(n + t);
-      assign_pos[n + t] = (int32_t)(n + t);
+    for (int t = tid; t < T; t += kThreadsBig) {
+      sorted_assign[n + t] = n + t;
+      assign_pos[n + t] = n + t;
     }
 }
 
-// Large n, pass 1: per-chunk histograms counts[g][e].
-__global__ __launch_bounds__(256) void k_perm_count(const int32_t* __restrict__ topk_idx, int64_t n, int32_t E,
-                                                    int32_t* __restrict__ counts) {
-  __shared__ int32_t h[kMaxExperts];
-  const int g = blockIdx.x;
-  for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
+// Up to kBlockTokens tokens: the whole permutation in one workgroup.
+__global__ __launch_bounds__(kThreadsBig) void k_permute_small(const int32_t* __restrict__ topk_idx, int32_t T,
+                                                               int32_t k, int32_t E, int32_t shared,
+                                                               int32_t* __restrict__ offsets,
+                                                               int32_t* __restrict__ sorted_assign,
+                                                               int32_t* __restrict__ assign_pos) {
+  __shared__ uint64_t mask[kMaxExperts * kWords];
+  __shared__ int32_t idx_s[kBlockTokens * kMaxTopK];
+  __shared__ int base[kMaxExperts];
+  __shared__ int wsum[kThreadsBig / kWave];
+  for (int a = threadIdx.x; a < T * k; a += kThreadsBig) idx_s[a] = topk_idx[a];
   __syncthreads();
-  const int64_t a = (int64_t)g * kPermChunk + threadIdx.x;
-  if (threadIdx.x < kPermChunk && a < n) atomicAdd(&h[topk_idx[a]], 1);
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) counts[(size_t)g * E + e] = h[e];
+  permute_one_block(idx_s, T, k, E, shared, mask, base, wsum, offsets, sorted_assign, assign_pos);
 }
 
-// Large n, pass 2 (one workgroup): column prefix over chunks (turns counts
-// into each chunk's start inside its expert segment), expert offsets.
-__global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ counts, int32_t G, int32_t T, int32_t k,
-                                                    int32_t E, int32_t shared, int32_t* __restrict__ offsets,
-                                                    int32_t* __restrict__ sorted_assign,
-                                                    int32_t* __restrict__ assign_pos) {
-  __shared__ int32_t wsum[16];
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-  int total = 0;
+// Gating and permutation of a small batch (T <= 16) in one workgroup: wave t
+// gates token t, then the block permutes.
+__global__ __launch_bounds__(kThreadsBig) void k_gate_permute_small(
+    const float* __restrict__ logits, const float* __restrict__ sgate_pre, int32_t T, int32_t E, int32_t k,
+    int32_t softmax_first, int32_t renorm, float scale, int32_t shared, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, float* __restrict__ sgate, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_assign, int32_t* __restrict__ assign_pos) {
+  __shared__ uint64_t mask[kMaxExperts];
+  __shared__ int32_t idx_s[16 * kMaxTopK];
+  __shared__ int base[kMaxExperts];
+  __shared__ int wsum[kThreadsBig / kWave];
+  const int lane = threadIdx.x & (kWave - 1), t = threadIdx.x / kWave;
+  if (t < T) {
+    const int e = gate_token(logits + (size_t)t * E, E, k, softmax_first, renorm, scale, topk_idx + (size_t)t * k,
+                             topk_w + (size_t)t * k);
+    if (lane < k) idx_s[t * k + lane] = e;
+    if (shared && lane == 0) sgate[t] = 1.f / (1.f + expf(-sgate_pre[t]));
+  }
+  __syncthreads();
+  permute_one_block(idx_s, T, k, E, shared, mask, base, wsum, offsets, sorted_assign, assign_pos);
+}
+
+// Large batches, pass 1: masks and counts of one block of kBlockTokens
+// tokens, stored to scratch (masks [G][E][kWords], counts [G][E]).
+__global__ __launch_bounds__(kThreadsBig) void k_perm_masks(const int32_t* __restrict__ topk_idx, int32_t T,
+                                                            int32_t k, int32_t E, uint64_t* __restrict__ gmask,
+                                                            int32_t* __restrict__ counts) {
+  __shared__ uint64_t mask[kMaxExperts * kWords];
+  const int g = blockIdx.x, tid = threadIdx.x;
+  for (int i = tid; i < E * kWords; i += kThreadsBig) mask[i] = 0ull;
+  __syncthreads();
+  const int t0 = g * kBlockTokens;
+  const int nt = min(kBlockTokens, T - t0);
+  for (int i = tid; i < nt * k; i += kThreadsBig) {
+    const int tl = i / k;
+    const int e = topk_idx[(size_t)t0 * k + i];
+    atomicOr((unsigned long long*)&mask[e * kWords + tl / 64], 1ull << (tl & 63));
+  }
+  __syncthreads();
+  for (int i = tid; i < E * kWords; i += kThreadsBig) gmask[(size_t)g * E * kWords + i] = mask[i];
+  if (tid < E) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kWords; ++w) c += __popcll(mask[tid * kWords + w]);
+    counts[(size_t)g * E + tid] = c;
+  }
+}
+
+// Pass 2 (one workgroup): expert offsets and each block's start inside each
+// segment (counts[g][e] becomes that start).
+__global__ __launch_bounds__(kThreadsBig) void k_perm_scan(int32_t* __restrict__ counts, int32_t G, int32_t T,
+                                                           int32_t k, int32_t E, int32_t shared,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ sorted_assign,
+                                                           int32_t* __restrict__ assign_pos) {
+  __shared__ int wsum[kThreadsBig / kWave];
+  const int tid = threadIdx.x;
+  int tot = 0;
   if (tid < E)
+    for (int g = 0; g < G; ++g) tot += counts[(size_t)g * E + tid];
+  int all;
+  const int excl = block_excl_scan(tid < E ? tot : 0, wsum, &all);
+  if (tid < E) {
+    offsets[tid] = excl;
+    int run = excl;
     for (int g = 0; g < G; ++g) {
       const int c = counts[(size_t)g * E + tid];
-      counts[(size_t)g * E + tid] = total;
-      total += c;
+      counts[(size_t)g * E + tid] = run;
+      run += c;
     }
-  int incl = total;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int u = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += u;
   }
-  if (lane == kWave - 1) wsum[wid] = incl;
-  __syncthreads();
-  int before = 0;
-  for (int w2 = 0; w2 < wid; ++w2) before += wsum[w2];
-  const int64_t n = (int64_t)T * k;
-  if (tid < E) offsets[tid] = before + incl - total;
+  const int n = T * k;
   if (tid == 0) {
-    offsets[E] = (int32_t)n;
-    if (shared) offsets[E + 1] = (int32_t)(n + T);
+    offsets[E] = n;
+    if (shared) offsets[E + 1] = n + T;
   }
   if (shared)
-    for (int t = tid; t < T; t += 1024) {
-      sorted_assign[n + t] = (int32_t)(n + t);
-      assign_pos[n + t] = (int32_t)(n + t);
+    for (int t = tid; t < T; t += kThreadsBig) {
+      sorted_assign[n + t] = n + t;
+      assign_pos[n + t] = n + t;
     }
 }
 
-// Large n, pass 3: one wave per chunk places its assignments in order.
-__global__ __launch_bounds__(kWave) void k_perm_scatter(const int32_t* __restrict__ topk_idx, int64_t n, int32_t E,
-                                                        const int32_t* __restrict__ counts,
-                                                        const int32_t* __restrict__ offsets,
-                                                        int32_t* __restrict__ sorted_assign,
-                                                        int32_t* __restrict__ assign_pos) {
-  __shared__ int32_t fill[kMaxExperts];
-  const int g = blockIdx.x;
-  for (int e = threadIdx.x; e < E; e += kWave) fill[e] = offsets[e] + counts[(size_t)g * E + e];
-  __syncthreads();
-  const int64_t a_end = min<int64_t>(n, (int64_t)(g + 1) * kPermChunk);
-  for (int64_t a0 = (int64_t)g * kPermChunk; a0 < a_end; a0 += kWave)
-    place_wave(topk_idx, a_end, a0, fill, sorted_assign, assign_pos);
+// Pass 3: every assignment's position from its block's masks and start.
+__global__ __launch_bounds__(256) void k_perm_place(const int32_t* __restrict__ topk_idx, int32_t T, int32_t k,
+                                                    int32_t E, const uint64_t* __restrict__ gmask,
+                                                    const int32_t* __restrict__ start,
+                                                    int32_t* __restrict__ sorted_assign,
+                                                    int32_t* __restrict__ assign_pos) {
+  const int a = blockIdx.x * 256 + threadIdx.x;
+  if (a >= T * k) return;
+  const int t = a / k, e = topk_idx[a];
+  const int g = t / kBlockTokens, tl = t % kBlockTokens;
+  const uint64_t* m = gmask + ((size_t)g * E + e) * kWords;
+  int r = __popcll(m[tl / 64] & lower_bits(tl & 63));
+  for (int w = 0; w < tl / 64; ++w) r += __popcll(m[w]);
+  const int pos = start[(size_t)g * E + e] + r;
+  sorted_assign[pos] = a;
+  assign_pos[a] = pos;
 }
 
 }  // namespace
 
+size_t permute_scratch_bytes(int32_t T, int32_t E) {
+  const size_t G = (size_t)(T + kBlockTokens - 1) / kBlockTokens;
+  return G * E * kWords * sizeof(uint64_t) + G * E * sizeof(int32_t);
+}
+
 hipError_t launch_permute(const moe_config* c, const int32_t* topk_idx, int32_t T, int32_t* offsets,
                           int32_t* sorted_assign, int32_t* assign_pos, int32_t* scratch, hipStream_t s) {
   const int E = c->n_expert, k = c->top_k, shared = c->shared_ff > 0;
-  const int64_t n = (int64_t)T * k;
-  if (n <= kPermSmallMax) {
-    k_permute_small<<<1, kSmallThreads, 0, s>>>(topk_idx, T, k, E, shared, offsets, sorted_assign, assign_pos);
+  if (T == 0) return hipSuccess;
+  if (T <= kBlockTokens) {
+    k_permute_small<<<1, kThreadsBig, 0, s>>>(topk_idx, T, k, E, shared, offsets, sorted_assign, assign_pos);
     return hipGetLastError();
   }
-  const int G = (int)((n + kPermChunk - 1) / kPermChunk);
-  k_perm_count<<<G, 256, 0, s>>>(topk_idx, n, E, scratch);
-  k_perm_scan<<<1, 1024, 0, s>>>(scratch, G, T, k, E, shared, offsets, sorted_assign, assign_pos);
-  k_perm_scatter<<<G, kWave, 0, s>>>(topk_idx, n, E, scratch, offsets, sorted_assign, assign_pos);
+  const int G = (T + kBlockTokens - 1) / kBlockTokens;
+  uint64_t* gmask = reinterpret_cast<uint64_t*>(scratch);
+  int32_t* counts = reinterpret_cast<int32_t*>(gmask + (size_t)G * E * kWords);
+  k_perm_masks<<<G, kThreadsBig, 0, s>>>(topk_idx, T, k, E, gmask, counts);
+  k_perm_scan<<<1, kThreadsBig, 0, s>>>(counts, G, T, k, E, shared, offsets, sorted_assign, assign_pos);
+  k_perm_place<<<(T * k + 255) / 256, 256, 0, s>>>(topk_idx, T, k, E, gmask, counts, sorted_assign, assign_pos);
+  return hipGetLastError();
+}
+
+bool can_fuse_gate_permute(int32_t T) { return T > 0 && T <= 16; }
+
+hipError_t launch_gate_permute(const moe_config* c, const float* logits, const float* sgate_pre, int32_t T,
+                               int32_t* topk_idx, float* topk_w, float* sgate, int32_t* offsets,
+                               int32_t* sorted_assign, int32_t* assign_pos, hipStream_t s) {
+  const int softmax_first = c->gating == MOE_GATING_SOFTMAX_TOPK;
+  const int shared = c->shared_ff > 0;
+  k_gate_permute_small<<<1, kThreadsBig, 0, s>>>(logits, sgate_pre, T, c->n_expert, c->top_k, softmax_first,
+                                                 c->norm_topk_prob, c->weights_scale, shared, topk_idx, topk_w,
+                                                 shared ? sgate : nullptr, offsets, sorted_assign, assign_pos);
   return hipGetLastError();
 }
 
