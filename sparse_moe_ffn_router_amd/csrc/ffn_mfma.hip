@@ -3,10 +3,12 @@
 //
 // One workgroup of 8 waves computes a 128 x 256 tile: 128 sorted rows of one
 // expert segment (the rows of a segment are contiguous after the
-// permutation) by 256 weight rows.  K advances in steps of 64; global loads
-// run two steps ahead through registers into a double-buffered LDS tile
-// (rows padded by 16 bytes).  Waves sit 2 (rows) x 4 (columns), each 64 x 64
-// as 2 x 2 v_mfma_f32_32x32x16_bf16 blocks.
+// permutation) by 256 weight rows.  K advances in steps of 64 through a ring
+// of three LDS stages filled by direct buffer-to-LDS loads issued two steps
+// ahead; each 128-byte LDS row holds its eight 16-byte pieces in XOR-swizzled
+// order (piece c of row r at slot c ^ ((r >> 1) & 7)) so MFMA operand reads
+// spread over the banks.  Waves sit 2 (rows) x 4 (columns), each 64 x 64 as 2 x 2
+// v_mfma_f32_32x32x16_bf16 blocks.
 //
 //  gate/up: A = x rows gathered by token; the 256 weight rows are 128 gate
 //           rows and the 128 matching up rows (for the interleaved gpt-oss
@@ -29,8 +31,8 @@ namespace moe {
 namespace {
 
 constexpr int BM = 128, BN = 256, BK = 64;
-constexpr int LDK = BK + 8;  // padded LDS row (bf16 elements)
 constexpr int kThreads = 512;
+constexpr int kStages = 3;
 constexpr int kAChunks = BM * BK / 8 / kThreads;  // 16-byte A pieces per thread per step (2)
 constexpr int kBChunks = BN * BK / 8 / kThreads;  // 16-byte B pieces per thread per step (4)
 
@@ -81,9 +83,44 @@ __device__ int tile_lookup(const int32_t* __restrict__ offsets, int nseg, int mt
   return -1;
 }
 
-__device__ __forceinline__ void store_u4(uint16_t* lds, int row, int col8, uint4 v) {
-  *reinterpret_cast<uint4*>(lds + row * LDK + col8 * 8) = v;
+// Raw buffer resource over [base, base + bytes): loads at offsets past the
+// end return zero (gfx9 descriptor word 3: 32-bit data format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ uint32_t buf_load_u8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
+}
+constexpr uint32_t kOutOfRange = 0x80000000u;  // an offset past every buffer: loads give 0
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Direct buffer -> LDS load of 16 bytes per lane: lane l of the wave writes
+// LDS bytes [lds + 16 l, lds + 16 l + 16) (lds must be wave-uniform).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, (int)voff, 0, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter limited (gfx9 encoding).
+template <int N> __device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier for the K pipeline: LDS writes of this wave complete,
+// then s_barrier.  Unlike __syncthreads it is not a release fence, so the
+// buffer->LDS loads still in flight for later steps are not waited for; the
+// loads of the step about to be read are waited for explicitly (wait_vm).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Byte offset of 16-byte piece c (of 8) in row r of a swizzled 128-byte-row
+// tile.  Two 128-byte rows span the 64 four-byte banks, so 16 consecutive
+// rows read at one logical piece (what 16 lanes of an MFMA operand read do)
+// hit 16 distinct 16-byte bank groups when the slot is c ^ ((r >> 1) & 7).
+__device__ __forceinline__ int swz_slot(int r, int c) { return c ^ ((r >> 1) & 7); }
+__device__ __forceinline__ int swz(int r, int c) { return r * 128 + (swz_slot(r, c) << 4); }
 
 // One 32-element MXFP4 block (16 code bytes, E8M0 exponent) to 32 bf16.
 __device__ __forceinline__ void mxfp4_block_to_bf16(uint4 codes, uint32_t e8m0, uint4 out[4]) {
@@ -100,17 +137,120 @@ __device__ __forceinline__ void mxfp4_block_to_bf16(uint4 codes, uint32_t e8m0, 
   }
 }
 
-// Staging registers of one K step.
-struct Stage {
-  uint4 a[kAChunks];
-  uint4 b[kBChunks];   // bf16 pieces, or in b[0] the MXFP4 block
-  uint32_t sc;         // MXFP4 block exponent
+// MXFP4 weight block of one K step held in registers until converted.
+struct CodeRegs {
+  uint4 codes;
+  uint32_t sc;
 };
+
+// Per-thread state of the K pipeline.
+struct Pipe {
+  __amdgpu_buffer_rsrc_t ra, rw0, rw1, rsc;
+  uint32_t a_off[kAChunks], b_off[kBChunks], sc_off;
+  bool two_mats, mx;
+  int nk, wid, tid, arow0, brow0, brow1, khalf;
+};
+
+// Issue the loads of step s into stage (la, lb) (all lanes, always: a step
+// past the end reads at an out-of-range offset, i.e. zeros, so every step
+// has the same number of outstanding loads).
+__device__ __forceinline__ void pipe_issue(const Pipe& p, int s, uint8_t* __restrict__ la, uint8_t* __restrict__ lb,
+                                           CodeRegs& cr) {
+  const uint32_t kb = s < p.nk ? (uint32_t)s * BK * 2 : kOutOfRange;  // byte offset of the step in a bf16 row
+#pragma unroll
+  for (int i = 0; i < kAChunks; ++i) dma16(p.ra, la + (i * kThreads + p.wid * kWave) * 16, p.a_off[i] + kb);
+  if (!p.mx) {
+#pragma unroll
+    for (int i = 0; i < kBChunks; ++i) {
+      const bool up = p.two_mats && i >= kBChunks / 2;  // pieces i >= 2 are tile rows >= 128
+      dma16(up ? p.rw1 : p.rw0, lb + (i * kThreads + p.wid * kWave) * 16, p.b_off[i] + kb);
+    }
+  } else {
+    cr.codes = buf_load16(p.rw0, p.b_off[0], s < p.nk ? (uint32_t)s * BK / 2 : kOutOfRange);
+    cr.sc = buf_load_u8(p.rsc, p.sc_off, s < p.nk ? (uint32_t)s * BK / 32 : kOutOfRange);
+  }
+}
+
+// MXFP4: decode a step's block to bf16 and write it (swizzled) to lb.
+__device__ __forceinline__ void pipe_put_codes(const Pipe& p, const CodeRegs& cr, uint8_t* __restrict__ lb) {
+  uint4 d[4];
+  mxfp4_block_to_bf16(cr.codes, cr.sc, d);
+  const int r = p.tid / 2, blk = p.tid % 2;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(lb + swz(r, blk * 4 + q)) = d[q];
+}
+
+__device__ __forceinline__ void pipe_compute(const Pipe& p, f32x16_t (&acc)[2][2], const uint8_t* __restrict__ la,
+                                             const uint8_t* __restrict__ lb) {
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int c = kk * 2 + p.khalf;  // logical 16-byte piece of the row
+    bf16x8_t fa[2], fb[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(la + swz(p.arow0 + i * 32, c));
+    fb[0] = *reinterpret_cast<const bf16x8_t*>(lb + swz(p.brow0, c));
+    fb[1] = *reinterpret_cast<const bf16x8_t*>(lb + swz(p.brow1, c));
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// The K loop over a ring of three LDS stages; the six stage buffers are
+// distinct restrict pointers so the loads landing in one stage are known
+// not to alias the reads of another.  Step s lives in stage s % 3 and its
+// loads are issued during step s - 2.  Per step: wait for this thread's
+// loads of step kt, barrier (all threads' loads landed; everyone finished
+// step kt - 1, whose stage the next loads reuse), issue step kt + 2,
+// compute step kt.
+__device__ __forceinline__ void mainloop(const Pipe& p, f32x16_t (&acc)[2][2], uint8_t* __restrict__ a0,
+                                         uint8_t* __restrict__ a1, uint8_t* __restrict__ a2,
+                                         uint8_t* __restrict__ b0, uint8_t* __restrict__ b1,
+                                         uint8_t* __restrict__ b2) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+  // step s's MXFP4 block sits in code registers cr[s % 3] until converted
+  CodeRegs cr0 = {}, cr1 = {}, cr2 = {};
+  pipe_issue(p, 0, a0, b0, cr0);
+  pipe_issue(p, 1, a1, b1, cr1);
+  if (p.mx) {
+    wait_vm<2>();  // step 0's block (step 1's code and scale loads may remain)
+    pipe_put_codes(p, cr0, b0);
+  }
+  // loads per thread per step: 6 (bf16) or 4 (MXFP4: 2 DMA + codes + scale)
+#define MOE_STEP(KT, LA, LB, LA2, LB2, LB1, CRN, CRP) \
+  {                                                   \
+    if (p.mx)                                         \
+      wait_vm<4>();                                   \
+    else                                              \
+      wait_vm<6>();                                   \
+    lds_barrier();                                    \
+    pipe_issue(p, (KT) + 2, LA2, LB2, CRN);           \
+    pipe_compute(p, acc, LA, LB);                     \
+    if (p.mx) {                                       \
+      wait_vm<4>();                                   \
+      pipe_put_codes(p, CRP, LB1);                    \
+    }                                                 \
+  }
+  for (int kt = 0; kt < p.nk; kt += 3) {
+    MOE_STEP(kt, a0, b0, a2, b2, b1, cr2, cr1)
+    if (kt + 1 < p.nk) MOE_STEP(kt + 1, a1, b1, a0, b0, b2, cr0, cr2)
+    if (kt + 2 < p.nk) MOE_STEP(kt + 2, a2, b2, a1, b1, b0, cr1, cr0)
+  }
+#undef MOE_STEP
+  wait_vm<0>();
+}
 
 template <int MODE, bool MX>
 __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_b[2][BN * LDK];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_a0[BM * 128], lds_a1[BM * 128], lds_a2[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_b0[BN * 128], lds_b1[BN * 128], lds_b2[BN * 128];
 
   // XCD-aware order: the hardware deals workgroups round-robin over 8 XCDs;
   // give each XCD a contiguous run of (column tile, row tiles) so the row
@@ -129,8 +269,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
     if (rows <= 0) return;
   } else {
     seg = tile_lookup(a.offsets, nseg, mt, &p0);
+    // the lookup is wave-uniform: keep it in scalar registers so buffer
+    // descriptors built from it stay scalar
+    seg = __builtin_amdgcn_readfirstlane(seg);
+    p0 = __builtin_amdgcn_readfirstlane(p0);
     if (seg < 0) return;
-    rows = min(BM, a.offsets[seg + 1] - p0);
+    rows = min(BM, __builtin_amdgcn_readfirstlane(a.offsets[seg + 1]) - p0);
   }
   const bool sh = MODE != MODE_ROUTER && seg == a.E;
   const int64_t nas = (int64_t)a.T * a.k;
@@ -143,28 +287,46 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
   const bool mx = MX && !sh && MODE != MODE_ROUTER;
 
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1), wid = tid / kWave;
+  const int lane = tid & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wid >> 2, wn = wid & 3;
 
-  // ---- per-thread staging sources (fixed over K).  Piece q = tid + i*512
-  // covers row q/8, 16-byte column q%8 of the step.
-  const uint16_t* a_ptr[kAChunks];
-#pragma unroll
-  for (int i = 0; i < kAChunks; ++i) {
-    const int q = tid + i * kThreads;
-    const int r = min(q / 8, rows - 1);
-    const int p = p0 + r;
-    const uint16_t* base;
-    if (MODE == MODE_ROUTER) {
-      base = a.a_src + (size_t)p * a.H;
-    } else if (MODE == MODE_GATEUP) {
-      const int asg = a.sorted_assign[p];
-      const int t = asg < nas ? asg / a.k : (int)(asg - nas);
-      base = a.a_src + (size_t)t * a.H;
+  // ---- staging sources.  Piece q = tid + i*512 of a step lands at LDS
+  // byte 16 q = row q/8, slot q%8; it must hold the logical piece whose
+  // swizzled slot that is (the XOR is its own inverse).  Rows past the
+  // tile's end read zeros.
+  __amdgpu_buffer_rsrc_t ra;
+  uint32_t a_off[kAChunks];
+  {
+    const uint16_t* abase;
+    uint32_t abytes;
+    if (MODE == MODE_DOWN) {
+      abase = sh ? a.a_src + (size_t)nas * a.F + (size_t)(p0 - nas) * a.Fs : a.a_src + (size_t)p0 * a.F;
+      abytes = (uint32_t)((size_t)rows * K * 2);
     } else {
-      base = p < nas ? a.a_src + (size_t)p * a.F : a.a_src + (size_t)nas * a.F + (size_t)(p - nas) * a.Fs;
+      abase = a.a_src;
+      abytes = (uint32_t)((size_t)a.T * a.H * 2);
     }
-    a_ptr[i] = base + (q % 8) * 8;
+    ra = make_rsrc(abase, abytes);
+#pragma unroll
+    for (int i = 0; i < kAChunks; ++i) {
+      const int q = tid + i * kThreads;
+      const int r = q / 8;
+      uint32_t off = kOutOfRange;
+      if (r < rows) {
+        if (MODE == MODE_ROUTER) {
+          off = (uint32_t)((size_t)(p0 + r) * a.H * 2);
+        } else if (MODE == MODE_GATEUP) {
+          const int asg = a.sorted_assign[p0 + r];
+          const int t = asg < nas ? asg / a.k : (int)(asg - nas);
+          off = (uint32_t)((size_t)t * a.H * 2);
+        } else {
+          off = (uint32_t)((size_t)r * K * 2);
+        }
+        off += swz_slot(r, q % 8) << 4;
+      }
+      a_off[i] = off;
+    }
   }
   auto wrow = [&](int r) -> int {  // row of the segment's weight matrix for tile row r
     if (MODE == MODE_GATEUP) {
@@ -175,81 +337,65 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
     if (MODE == MODE_ROUTER) return min(c0 + r, a.E - 1);
     return min(c0 + r, a.H - 1);
   };
-  const uint16_t* b_ptr[kBChunks];
-  const uint8_t* b_code = nullptr;
-  const uint8_t* b_sc = nullptr;
-  if (!mx) {
-#pragma unroll
-    for (int i = 0; i < kBChunks; ++i) {
-      const int q = tid + i * kThreads;
-      const int r = q / 8;
-      const int wr = wrow(r);
-      const uint16_t* base;
-      if (MODE == MODE_ROUTER) {
-        base = (const uint16_t*)a.w0 + (size_t)wr * a.H;
-      } else if (MODE == MODE_GATEUP) {
-        if (sh)
-          base = (r < BN / 2 ? a.sh0 : a.sh1) + (size_t)wr * a.H;
-        else if (a.oai)
-          base = (const uint16_t*)a.w0 + ((size_t)seg * 2 * a.F + wr) * a.H;
-        else
-          base = (const uint16_t*)(r < BN / 2 ? a.w0 : a.w1) + ((size_t)seg * a.F + wr) * a.H;
+  // weights: rw0 = the segment's first matrix (gate / fused gate_up / down /
+  // router), rw1 = its up matrix (separate SwiGLU layout)
+  __amdgpu_buffer_rsrc_t rw0, rw1, rsc;
+  uint32_t b_off[kBChunks];
+  uint32_t sc_off = 0;
+  {
+    const uint8_t *w0, *w1 = nullptr;
+    size_t wbytes;
+    const size_t pack = mx ? 4 : 1;  // MXFP4 holds 4 bits per element instead of 16
+    if (MODE == MODE_ROUTER) {
+      w0 = (const uint8_t*)a.w0;
+      wbytes = (size_t)a.E * a.H * 2;
+    } else if (MODE == MODE_GATEUP) {
+      if (sh) {
+        w0 = (const uint8_t*)a.sh0;
+        w1 = (const uint8_t*)a.sh1;
+        wbytes = (size_t)a.Fs * a.H * 2;
+      } else if (a.oai) {
+        wbytes = (size_t)2 * a.F * a.H * 2 / pack;
+        w0 = (const uint8_t*)a.w0 + (size_t)seg * wbytes;
       } else {
-        base = sh ? a.sh0 + (size_t)wr * a.Fs : (const uint16_t*)a.w0 + ((size_t)seg * a.H + wr) * a.F;
+        wbytes = (size_t)a.F * a.H * 2;
+        w0 = (const uint8_t*)a.w0 + (size_t)seg * wbytes;
+        w1 = (const uint8_t*)a.w1 + (size_t)seg * wbytes;
       }
-      b_ptr[i] = base + (q % 8) * 8;
-    }
-  } else {
-    // one 32-element block per thread per step: tile row tid/2, block tid%2
-    const int r = tid / 2;
-    const int wr = wrow(r);
-    const size_t row = MODE == MODE_GATEUP ? (size_t)seg * 2 * a.F + wr : (size_t)seg * a.H + wr;
-    b_code = (const uint8_t*)a.w0 + row * (K / 2) + (tid % 2) * 16;
-    b_sc = a.scales + row * (K / 32) + (tid % 2);
-  }
-
-  auto g_load = [&](Stage& st, int k0) {
-#pragma unroll
-    for (int i = 0; i < kAChunks; ++i) st.a[i] = *reinterpret_cast<const uint4*>(a_ptr[i] + k0);
-    if (!mx) {
-#pragma unroll
-      for (int i = 0; i < kBChunks; ++i) st.b[i] = *reinterpret_cast<const uint4*>(b_ptr[i] + k0);
     } else {
-      st.b[0] = *reinterpret_cast<const uint4*>(b_code + k0 / 2);
-      st.sc = b_sc[k0 / 32];
+      if (sh) {
+        w0 = (const uint8_t*)a.sh0;
+        wbytes = (size_t)a.H * a.Fs * 2;
+      } else {
+        wbytes = (size_t)a.H * a.F * 2 / pack;
+        w0 = (const uint8_t*)a.w0 + (size_t)seg * wbytes;
+      }
     }
-  };
-  auto s_store = [&](const Stage& st, int buf) {
-#pragma unroll
-    for (int i = 0; i < kAChunks; ++i) {
-      const int q = tid + i * kThreads;
-      store_u4(lds_a[buf], q / 8, q % 8, st.a[i]);
-    }
+    rw0 = make_rsrc(w0, (uint32_t)wbytes);
+    rw1 = make_rsrc(w1 ? w1 : w0, (uint32_t)wbytes);
+    rsc = rw0;
     if (!mx) {
 #pragma unroll
       for (int i = 0; i < kBChunks; ++i) {
         const int q = tid + i * kThreads;
-        store_u4(lds_b[buf], q / 8, q % 8, st.b[i]);
+        const int r = q / 8;
+        b_off[i] = (uint32_t)((size_t)wrow(r) * K * 2) + (swz_slot(r, q % 8) << 4);
       }
     } else {
-      uint4 d[4];
-      mxfp4_block_to_bf16(st.b[0], st.sc, d);
-      const int r = tid / 2, blk = tid % 2;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) store_u4(lds_b[buf], r, blk * 4 + q, d[q]);
+      // one 32-element block per thread per step: tile row tid/2, block tid%2
+      const size_t row = wrow(tid / 2);
+      b_off[0] = (uint32_t)(row * (K / 2)) + (tid % 2) * 16;
+      const size_t srow0 = MODE == MODE_GATEUP ? (size_t)seg * 2 * a.F : (size_t)seg * a.H;
+      const size_t nrows = MODE == MODE_GATEUP ? (size_t)2 * a.F : (size_t)a.H;
+      rsc = make_rsrc(a.scales + srow0 * (K / 32), (uint32_t)(nrows * (K / 32)));
+      sc_off = (uint32_t)(row * (K / 32)) + (tid % 2);
     }
-  };
+  }
+  // SwiGLU with separate gate and up matrices: B rows >= BN/2 read the up matrix
+  const bool two_mats = MODE == MODE_GATEUP && (sh || !a.oai);
+  const int nk = K / BK;
 
-  f32x16_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-
-  // LDS rows of this wave's operands
-  const int arow = wm * 64 + (lane & 31);
+  const int arow0 = wm * 64 + (lane & 31);
   int brow[2];
   if (MODE == MODE_GATEUP) {
     brow[0] = wn * 32 + (lane & 31);           // gate rows
@@ -258,42 +404,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
     brow[0] = wn * 64 + (lane & 31);
     brow[1] = wn * 64 + 32 + (lane & 31);
   }
-  const int kofs = (lane >> 5) * 8;
-
-  const int nk = K / BK;
-  Stage s0, s1;
-  g_load(s0, 0);
-  if (nk > 1) g_load(s1, BK);
-  s_store(s0, 0);
-  __syncthreads();
-  // step kt computes LDS buffer kt&1 while the loads of step kt+2 land in
-  // `nxt` (whose previous content was already stored) and step kt+1 (in
-  // `pend`) goes to the other buffer at the end
-  auto step = [&](int kt, Stage& nxt, Stage& pend, int buf) {
-    if (kt + 2 < nk) g_load(nxt, (kt + 2) * BK);
-    const uint16_t* la = lds_a[buf];
-    const uint16_t* lb = lds_b[buf];
+  Pipe p;
+  p.ra = ra; p.rw0 = rw0; p.rw1 = rw1; p.rsc = rsc;
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8_t fa[2], fb[2];
+  for (int i = 0; i < kAChunks; ++i) p.a_off[i] = a_off[i];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8_t*>(la + (arow + i * 32) * LDK + kk + kofs);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = *reinterpret_cast<const bf16x8_t*>(lb + brow[j] * LDK + kk + kofs);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) s_store(pend, buf ^ 1);
-    __syncthreads();
-  };
-  for (int kt = 0; kt < nk; kt += 2) {
-    step(kt, s0, s1, 0);
-    if (kt + 1 < nk) step(kt + 1, s1, s0, 1);
-  }
+  for (int i = 0; i < kBChunks; ++i) p.b_off[i] = b_off[i];
+  p.sc_off = sc_off;
+  p.two_mats = two_mats;
+  p.mx = mx;
+  p.nk = nk;
+  p.wid = wid;
+  p.tid = tid;
+  p.arow0 = arow0;
+  p.brow0 = brow[0];
+  p.brow1 = brow[1];
+  p.khalf = lane >> 5;
+  f32x16_t acc[2][2];
+  mainloop(p, acc, lds_a0, lds_a1, lds_a2, lds_b0, lds_b1, lds_b2);
 
   // ---- epilogue.  Lane l of a 32x32 block holds column (l & 31) and rows
   // (q / 4) * 8 + (l / 32) * 4 + (q % 4), q = 0..15.
