@@ -15,10 +15,21 @@ T=4096 tokens, router logits drawn so expert load is Zipf(1.0)-skewed),
 the roofline of the dominant kernel and the CPU oracle's throughput.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-prefill]
+       python bench.py --pmc-summary FETCH_DIR WRITE_DIR   (HBM traffic from two rocprofv3 --pmc runs)
+
+HBM traffic of the dominant kernel comes from two rocprofv3 counter runs of
+this script with --copy-calib-mib (FETCH_SIZE, then WRITE_SIZE); each counter
+is scaled by what it reads for a plain device copy of known size in the same
+run.  The summary written by --pmc-summary is kept next to the kernel
+profiles and carries a hash of the kernel's source: the JSON line reports the
+traffic only while that hash matches the current source.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +41,10 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/sec + %HBM-roofline (T=8 decode) and %MFMA-peak (T=4096)"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+GATEUP_KERNEL = "k_gateup_gemv"
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+KERNEL_SOURCES = ("sparse_moe_ffn_router_amd/csrc/ffn_gemv.hip", "sparse_moe_ffn_router_amd/csrc/moe_internal.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gateup_gemv_qwen35moe_decode_T8_hbm_traffic.txt")
 
 
 def parse():
@@ -44,6 +59,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--gptoss", action="store_true",
                     help="also time the gpt-oss-20b-shaped layers (bf16 T=2048, MXFP4 T=16 and T=2048)")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="after the decode measurement, copy a buffer of this many MiB 5 times (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc output folders and exit")
     return ap.parse_args()
 
 
@@ -149,6 +168,66 @@ def layer_flops(case, T):
     return f
 
 
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _pmc_means(folder, counter):
+    """Mean counter value per dispatch, per kernel name (KiB for FETCH_SIZE /
+    WRITE_SIZE), from a rocprofv3 --pmc csv folder; the copy kernel keeps only
+    its largest grid (the calibration copy)."""
+    rows = []
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
+    big = max((int(r["Grid_Size"]) for r in rows if r["Kernel_Name"] == COPY_KERNEL), default=0)
+    sums = {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        if name == COPY_KERNEL and int(r["Grid_Size"]) != big:
+            continue
+        key = COPY_KERNEL if name == COPY_KERNEL else (GATEUP_KERNEL if GATEUP_KERNEL in name else None)
+        if key:
+            sums.setdefault(key, []).append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in sums.items()}
+
+
+def pmc_summary(fetch_dir, write_dir, copy_mib):
+    """Text summary: the gate/up kernel's FETCH_SIZE and WRITE_SIZE per launch,
+    each scaled by copy bytes / the copy kernel's counter."""
+    copy_bytes = copy_mib * 2 ** 20
+    out, total = [], 0.0
+    for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        m = _pmc_means(folder, counter)
+        (ck, cn), (gk, gn) = m[COPY_KERNEL], m[GATEUP_KERNEL]
+        factor = copy_bytes / (ck * 1024.0)
+        b = gk * 1024.0 * factor
+        total += b
+        out += ["%s: copy of %d bytes reads %.1f KiB/dispatch (%d dispatches) -> factor %.4f" %
+                (counter, copy_bytes, ck, cn, factor),
+                "%s: %s %.1f KiB/dispatch (%d dispatches) -> %.0f bytes per launch" %
+                (counter, GATEUP_KERNEL, gk, gn, b)]
+    out += ["traffic_bytes_per_launch = %.0f" % total, "source_sha256 = %s" % kernel_source_hash()]
+    return "\n".join(out)
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the gate/up kernel from the committed counter
+    summary, or None when it is missing or the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(l.split(" = ", 1) for l in f.read().splitlines() if " = " in l)
+        if kv.get("source_sha256", "").strip() != kernel_source_hash():
+            return None
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(case, seconds):
     """The oracle (plain C, double accumulation, OpenMP over tokens) on the
     decode batch, repeated for about `seconds` seconds."""
@@ -168,6 +247,9 @@ def cpu_baseline(case, seconds):
 
 def main():
     a = parse()
+    if a.pmc_summary:
+        print(pmc_summary(a.pmc_summary[0], a.pmc_summary[1], a.copy_calib_mib or 1024))
+        return
     if a.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (requested --gpus %d)" % a.gpus,
               file=sys.stderr)
@@ -198,8 +280,16 @@ def main():
     gb = gateup_bytes(dec, n_active, dec.T)
     achieved = gb / (k_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "kernel": "k_gateup_gemv (expert gate/up + SwiGLU)", "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": recorded_traffic(),
                 "kernel_ms": round(k_ms, 5), "algorithmic_bytes": gb}
+    if a.copy_calib_mib:
+        src = torch.empty(a.copy_calib_mib * 2 ** 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     lb = layer_bytes(dec, n_active, dec.T)
     layer_gbs = lb / (ms * 1e-3) / 1e9
 
