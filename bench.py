@@ -177,23 +177,19 @@ def kernel_source_hash():
 
 
 def _pmc_means(folder, counter):
-    """Mean counter value per dispatch, per kernel name (KiB for FETCH_SIZE /
-    WRITE_SIZE), from a rocprofv3 --pmc csv folder; the copy kernel keeps only
-    its largest grid (the calibration copy)."""
+    """Mean counter value per dispatch (KiB for FETCH_SIZE / WRITE_SIZE) of the
+    gate/up kernel and of the calibration copies, from a rocprofv3 --pmc csv
+    folder.  The calibration copies are the copy dispatches issued after the
+    last gate/up dispatch."""
     rows = []
     for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
         with open(f) as fh:
             rows += [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
-    big = max((int(r["Grid_Size"]) for r in rows if r["Kernel_Name"] == COPY_KERNEL), default=0)
-    sums = {}
-    for r in rows:
-        name = r["Kernel_Name"]
-        if name == COPY_KERNEL and int(r["Grid_Size"]) != big:
-            continue
-        key = COPY_KERNEL if name == COPY_KERNEL else (GATEUP_KERNEL if GATEUP_KERNEL in name else None)
-        if key:
-            sums.setdefault(key, []).append(float(r["Counter_Value"]))
-    return {k: (sum(v) / len(v), len(v)) for k, v in sums.items()}
+    gate = [r for r in rows if GATEUP_KERNEL in r["Kernel_Name"]]
+    last = max(int(r["Dispatch_Id"]) for r in gate)
+    copy = [r for r in rows if r["Kernel_Name"] == COPY_KERNEL and int(r["Dispatch_Id"]) > last]
+    mean = lambda rs: (sum(float(r["Counter_Value"]) for r in rs) / len(rs), len(rs))
+    return {GATEUP_KERNEL: mean(gate), COPY_KERNEL: mean(copy)}
 
 
 def pmc_summary(fetch_dir, write_dir, copy_mib):
@@ -207,7 +203,7 @@ def pmc_summary(fetch_dir, write_dir, copy_mib):
         factor = copy_bytes / (ck * 1024.0)
         b = gk * 1024.0 * factor
         total += b
-        out += ["%s: copy of %d bytes reads %.1f KiB/dispatch (%d dispatches) -> factor %.4f" %
+        out += ["%s: copy of %d bytes counts %.1f KiB/dispatch (%d dispatches) -> factor %.4f" %
                 (counter, copy_bytes, ck, cn, factor),
                 "%s: %s %.1f KiB/dispatch (%d dispatches) -> %.0f bytes per launch" %
                 (counter, GATEUP_KERNEL, gk, gn, b)]
