@@ -22,6 +22,9 @@ int check_config(const moe_config* c) {
   if (c->w_dtype != MOE_DTYPE_F32 && c->w_dtype != MOE_DTYPE_BF16 && c->w_dtype != MOE_DTYPE_MXFP4)
     return MOE_EINVAL;
   if (c->hidden % 32 || c->expert_ff % 32 || c->shared_ff % 32) return MOE_EUNSUPPORTED;
+  // rows of at most 8 x 64 16-byte pieces per lane set in the few-token kernels
+  const int dmax = c->x_dtype == MOE_DTYPE_F32 ? 2048 : 4096;
+  if (c->hidden > dmax || c->expert_ff > dmax || c->shared_ff > dmax) return MOE_EUNSUPPORTED;
   if (c->x_dtype == MOE_DTYPE_F32 && c->w_dtype != MOE_DTYPE_F32) return MOE_EUNSUPPORTED;
   if (c->x_dtype == MOE_DTYPE_BF16 && c->w_dtype == MOE_DTYPE_F32) return MOE_EUNSUPPORTED;
   // MXFP4 experts come in the fused interleaved gate_up layout only
@@ -56,6 +59,11 @@ int make_plan(const moe_config* c, int32_t T, Plan* p) {
   p->off_h = o; o += up256((size_t)(p->n_assign * c->expert_ff + (p->shared ? (int64_t)T * c->shared_ff : 0)) * p->elem_x);
   p->off_y = o; o += p->y_bytes;
   p->total = o;
+  // the few-token kernels address activations and h with 32-bit buffer offsets
+  const size_t act_bytes = (size_t)(p->n_assign * c->expert_ff + (p->shared ? (int64_t)T * c->shared_ff : 0)) * p->elem_x;
+  if (!(T > kGemvMaxT && mfma_shapes_ok(c)) &&
+      ((size_t)T * c->hidden * p->elem_x >= ((size_t)1 << 31) || act_bytes >= ((size_t)1 << 31)))
+    return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 

@@ -1,12 +1,17 @@
 // Expert kernels for few tokens per expert (decode-sized batches): each
-// weight row is streamed from HBM once per expert and applied to every token
-// routed to that expert.
+// weight row is streamed from HBM once and applied to every token routed to
+// its expert.
 //
-// Work unit: (active expert segment, tile of 32 row pairs).  The segment's
-// activation rows (x of its tokens, or its h rows) are staged in LDS, up to
-// 8 at a time.  A group of 8 lanes owns one row pair and splits the input
-// dimension in 16-byte pieces, 4 pieces per row in flight plus the next 4
-// prefetched, so a wavefront streams 16 rows in 128-byte segments.
+// Work unit: one wavefront owns RPW consecutive weight rows of one non-empty
+// expert segment (gate/up: RPW feature row pairs; down: RPW output rows).
+// It issues every load of its rows at once -- a 64-lane load instruction
+// reads 1 KiB of one row, 16 bytes per lane -- then loads the segment's
+// activation rows (L2-resident) while the weights are in flight, and reduces
+// each (row, token) dot product across the wavefront.  Many short
+// wavefronts, each with one burst of loads, keep HBM busier than long
+// software-pipelined ones for this access pattern; there is no LDS and no
+// barrier.  Activation rows are processed two tokens at a time, the next
+// pair prefetched while the current one is reduced.
 //
 // Sources: "qwen35moe - Forward-Pass Design", section "Shared-expert MoE
 // FFN" (SwiGLU experts, shared expert); "Phase 19: MoE - gpt-oss-20b",
@@ -17,164 +22,149 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kGroup = 8;                          // lanes per row pair
-constexpr int kPairsPerBlock = kThreads / kGroup;  // 32
-constexpr int kStage = 8;                          // activation rows staged at once
-constexpr int kU = 4;                              // pieces per row per pipeline step
+constexpr int kWaves = 4;  // wavefronts per workgroup
 
 enum { W_F32 = 0, W_BF16 = 1, W_MXFP4 = 2 };
 
-// s-th non-empty segment among nseg (offsets has nseg + 1 entries), or -1.
-__device__ int find_segment(const int32_t* __restrict__ offsets, int nseg, int s) {
-  const int lane = threadIdx.x & (kWave - 1);
-  for (int base = 0; base < nseg; base += kWave) {
-    const int e = base + lane;
-    const bool ne = e < nseg && offsets[e + 1] > offsets[e];
-    const uint64_t m = __ballot(ne);
-    const int c = __popcll(m);
-    if (s < c) {
-      const bool hit = ne && __popcll(m & (lane ? (~0ull >> (64 - lane)) : 0ull)) == s;
-      return base + __ffsll((unsigned long long)__ballot(hit)) - 1;
-    }
-    s -= c;
-  }
-  return -1;
+// Bytes of one weight row with `cols` inputs.
+template <int WK> __host__ __device__ constexpr size_t row_bytes(int cols) {
+  return WK == W_F32 ? (size_t)cols * 4 : WK == W_BF16 ? (size_t)cols * 2 : (size_t)cols / 2;
 }
 
-template <int WK> struct Piece;
-
-// bf16 weights: 8 elements per 16-byte piece, products summed in pairs.
-template <> struct Piece<W_BF16> {
-  static constexpr int kElems = 8;
-  __device__ static float dot(uint4 w, const uint16_t* xp, float acc, float) {
-    const uint4 xv = *reinterpret_cast<const uint4*>(xp);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), __builtin_bit_cast(bf16x2_t, xv.x), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), __builtin_bit_cast(bf16x2_t, xv.y), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), __builtin_bit_cast(bf16x2_t, xv.z), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), __builtin_bit_cast(bf16x2_t, xv.w), acc, false);
+// A 16-byte weight piece and the activation bytes it multiplies.
+template <int WK> struct Wp;
+template <> struct Wp<W_BF16> {
+  static constexpr int kElems = 8, kXq = 1;  // elements; 16-byte activation words
+  __device__ static float dot(uint4 w, const uint4* x, float acc, uint32_t) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), __builtin_bit_cast(bf16x2_t, x[0].x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), __builtin_bit_cast(bf16x2_t, x[0].y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), __builtin_bit_cast(bf16x2_t, x[0].z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), __builtin_bit_cast(bf16x2_t, x[0].w), acc, false);
     return acc;
   }
 };
-
-template <> struct Piece<W_F32> {
-  static constexpr int kElems = 4;
-  __device__ static float dot(uint4 w, const float* xp, float acc, float) {
-    const float4 xv = *reinterpret_cast<const float4*>(xp);
-    acc = fmaf(__uint_as_float(w.x), xv.x, acc);
-    acc = fmaf(__uint_as_float(w.y), xv.y, acc);
-    acc = fmaf(__uint_as_float(w.z), xv.z, acc);
-    acc = fmaf(__uint_as_float(w.w), xv.w, acc);
+template <> struct Wp<W_F32> {
+  static constexpr int kElems = 4, kXq = 1;
+  __device__ static float dot(uint4 w, const uint4* x, float acc, uint32_t) {
+    acc = fmaf(__uint_as_float(w.x), __uint_as_float(x[0].x), acc);
+    acc = fmaf(__uint_as_float(w.y), __uint_as_float(x[0].y), acc);
+    acc = fmaf(__uint_as_float(w.z), __uint_as_float(x[0].z), acc);
+    acc = fmaf(__uint_as_float(w.w), __uint_as_float(x[0].w), acc);
     return acc;
   }
 };
-
-// MXFP4: a piece is one 32-element block (16 code bytes); the block's E8M0
-// exponent is applied while converting the codes to bf16 (exact for the
-// E2M1 values times 2^(e-127) that bf16 represents).
-template <> struct Piece<W_MXFP4> {
-  static constexpr int kElems = 32;
-  __device__ static float dot(uint4 w, const uint16_t* xp, float acc, float scale) {
-    const uint4* xq = reinterpret_cast<const uint4*>(xp);
+// MXFP4: a piece is one 32-element block (16 code bytes, low nibble first);
+// its E8M0 exponent is applied while converting the codes to bf16 (exact:
+// E2M1 values times 2^(e-127) are bf16 numbers for the exponents in use).
+template <> struct Wp<W_MXFP4> {
+  static constexpr int kElems = 32, kXq = 4;
+  __device__ static float dot(uint4 w, const uint4* x, float acc, uint32_t e8m0) {
+    const float scale = e8m0_to_f32(e8m0 & 0xFFu);
     const uint32_t words[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint4 xv = xq[q];
       const uint32_t cw = words[q];
       acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, scale, 0),
-                                            __builtin_bit_cast(bf16x2_t, xv.x), acc, false);
+                                            __builtin_bit_cast(bf16x2_t, x[q].x), acc, false);
       acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, scale, 1),
-                                            __builtin_bit_cast(bf16x2_t, xv.y), acc, false);
+                                            __builtin_bit_cast(bf16x2_t, x[q].y), acc, false);
       acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, scale, 2),
-                                            __builtin_bit_cast(bf16x2_t, xv.z), acc, false);
+                                            __builtin_bit_cast(bf16x2_t, x[q].z), acc, false);
       acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, scale, 3),
-                                            __builtin_bit_cast(bf16x2_t, xv.w), acc, false);
+                                            __builtin_bit_cast(bf16x2_t, x[q].w), acc, false);
     }
     return acc;
   }
 };
 
-template <typename XT> __device__ __forceinline__ float xscalar(const XT* p, size_t i);
-template <> __device__ __forceinline__ float xscalar<float>(const float* p, size_t i) { return p[i]; }
-template <> __device__ __forceinline__ float xscalar<uint16_t>(const uint16_t* p, size_t i) {
-  return __uint_as_float((uint32_t)p[i] << 16);
+// Weight rows per wavefront for NP pieces per lane per row: about 8 pieces
+// (8 KiB) in flight per wavefront.
+// MXFP4 pieces hold 32 elements (64 activation bytes each), so fewer rows
+// and one token per chunk keep the registers in check.
+__host__ __device__ constexpr int rows_per_wave(int wk, int np) {
+  return wk == W_MXFP4 ? (np == 1 ? 4 : 2) : np >= 6 ? 1 : 8 / np;
 }
-template <typename XT> __device__ __forceinline__ void xstore(XT* p, size_t i, float v);
-template <> __device__ __forceinline__ void xstore<float>(float* p, size_t i, float v) { p[i] = v; }
-template <> __device__ __forceinline__ void xstore<uint16_t>(uint16_t* p, size_t i, float v) {
-  p[i] = (uint16_t)f32_to_bf16(v);
+// gate/up: a row pair per feature, about 16 pieces in flight
+__host__ __device__ constexpr int gateup_rows_per_wave(int wk, int np) {
+  return wk == W_MXFP4 ? (np == 1 ? 2 : 1) : np >= 6 ? 1 : np == 4 ? 2 : 4;
+}
+// tokens per register chunk
+__host__ __device__ constexpr int chunk_tokens(int wk) { return wk == W_MXFP4 ? 1 : 2; }
+
+struct Seg {
+  int e, p0, n;
+};
+
+// The s-th non-empty segment of offsets[0 .. nseg] with its first sorted
+// position and row count (one wavefront; the offsets of 512 segments are
+// loaded per round trip), or e = -1.
+__device__ Seg find_segment(const int32_t* __restrict__ off, int nseg, int s) {
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int base = 0; base < nseg; base += 8 * kWave) {
+    int lo[8], hi[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int e = base + c * kWave + lane;
+      lo[c] = e < nseg ? off[e] : 0;
+      hi[c] = e < nseg ? off[e + 1] : 0;
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const bool ne = hi[c] > lo[c];
+      const uint64_t m = __ballot(ne);
+      const int cnt = __popcll(m);
+      if (s < cnt) {
+        const bool hit = ne && __popcll(m & ((1ull << lane) - 1ull)) == s;
+        const int l = __ffsll((unsigned long long)__ballot(hit)) - 1;
+        const int p0 = __builtin_amdgcn_readlane(lo[c], l);
+        return Seg{base + c * kWave + l, p0, __builtin_amdgcn_readlane(hi[c], l) - p0};
+      }
+      s -= cnt;
+    }
+  }
+  return Seg{-1, 0, 0};
 }
 
-// acc[r][i] += row r . xs[i] over K inputs, this lane's share (pieces
-// lig, lig+8, ...).  Rows are streamed with the next kU pieces prefetched.
-template <typename XT, int WK, int NT>
-__device__ __forceinline__ void rows2_dot(const uint4* r0, const uint4* r1, const uint8_t* s0, const uint8_t* s1,
-                                          const XT* xs, int K, int lig, float (&acc)[2][kStage]) {
-  using P = Piece<WK>;
-  const int npieces = K / P::kElems;
-  uint4 w0[kU], w1[kU];
-  uint8_t c0[kU], c1[kU];
-  auto fetch = [&](int pc, uint4 (&a)[kU], uint4 (&b)[kU], uint8_t (&sa)[kU], uint8_t (&sb)[kU]) {
+// The segment a workgroup works on: the blockIdx.x-th non-empty one among
+// the routed experts (and the shared expert unless seg_mode == 1), or the
+// shared expert alone (seg_mode == 2).
+__device__ __forceinline__ Seg block_segment(const int32_t* off, int E, int shared, int seg_mode) {
+  if (seg_mode == 2) {
+    const int p0 = __builtin_amdgcn_readfirstlane(off[E]);
+    return Seg{E, p0, __builtin_amdgcn_readfirstlane(off[E + 1]) - p0};
+  }
+  const Seg s = find_segment(off, E + (seg_mode == 0 ? shared : 0), blockIdx.x);
+  return Seg{__builtin_amdgcn_readfirstlane(s.e), __builtin_amdgcn_readfirstlane(s.p0),
+             __builtin_amdgcn_readfirstlane(s.n)};
+}
+
+// Activation pieces of one token: NP pieces of the row starting at byte
+// `base` (kOutOfRange: zeros), matching the weight pieces of this lane.
+template <typename XT, int WK, int NP>
+__device__ __forceinline__ void load_act(__amdgpu_buffer_rsrc_t r, uint32_t base, bool valid, int P,
+                                         uint4 (&xv)[NP][Wp<WK>::kXq]) {
+  const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int q = pc + u * kGroup;
-      const bool ok = q < npieces;
-      a[u] = ok ? r0[q] : make_uint4(0, 0, 0, 0);
-      b[u] = ok ? r1[q] : make_uint4(0, 0, 0, 0);
-      if (WK == W_MXFP4) {
-        sa[u] = ok ? s0[q] : 0;
-        sb[u] = ok ? s1[q] : 0;
-      }
-    }
-  };
-  fetch(lig, w0, w1, c0, c1);
-  for (int pc = lig; pc < npieces; pc += kU * kGroup) {
-    uint4 n0[kU], n1[kU];
-    uint8_t d0[kU], d1[kU];
-    fetch(pc + kU * kGroup, n0, n1, d0, d1);
+  for (int p = 0; p < NP; ++p) {
+    const int q = lane + p * kWave;
+    const bool ok = valid && q < P;
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int q = pc + u * kGroup;
-      if (q < npieces) {
-        const float sc0 = WK == W_MXFP4 ? e8m0_to_f32(c0[u]) : 1.f;
-        const float sc1 = WK == W_MXFP4 ? e8m0_to_f32(c1[u]) : 1.f;
-#pragma unroll
-        for (int i = 0; i < NT; ++i) {
-          const XT* xp = xs + (size_t)i * K + (size_t)q * P::kElems;
-          acc[0][i] = P::dot(w0[u], xp, acc[0][i], sc0);
-          acc[1][i] = P::dot(w1[u], xp, acc[1][i], sc1);
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      w0[u] = n0[u];
-      w1[u] = n1[u];
-      c0[u] = d0[u];
-      c1[u] = d1[u];
-    }
+    for (int j = 0; j < Wp<WK>::kXq; ++j)
+      xv[p][j] = buf_load16(r, ok ? base + (uint32_t)(q * Wp<WK>::kElems * sizeof(XT) + j * 16) : kOutOfRange, 0);
   }
 }
 
-template <typename XT, int WK>
-__device__ __forceinline__ void rows2_dot_n(int nt, const uint4* r0, const uint4* r1, const uint8_t* s0,
-                                            const uint8_t* s1, const XT* xs, int K, int lig,
-                                            float (&acc)[2][kStage]) {
-  switch (nt) {
-    case 1: rows2_dot<XT, WK, 1>(r0, r1, s0, s1, xs, K, lig, acc); break;
-    case 2: rows2_dot<XT, WK, 2>(r0, r1, s0, s1, xs, K, lig, acc); break;
-    case 3: rows2_dot<XT, WK, 3>(r0, r1, s0, s1, xs, K, lig, acc); break;
-    case 4: rows2_dot<XT, WK, 4>(r0, r1, s0, s1, xs, K, lig, acc); break;
-    case 5: rows2_dot<XT, WK, 5>(r0, r1, s0, s1, xs, K, lig, acc); break;
-    case 6: rows2_dot<XT, WK, 6>(r0, r1, s0, s1, xs, K, lig, acc); break;
-    case 7: rows2_dot<XT, WK, 7>(r0, r1, s0, s1, xs, K, lig, acc); break;
-    default: rows2_dot<XT, WK, 8>(r0, r1, s0, s1, xs, K, lig, acc); break;
-  }
+template <typename XT> __device__ __forceinline__ void store_elem(void* p, size_t i, float v) {
+  if (sizeof(XT) == 4)
+    reinterpret_cast<float*>(p)[i] = v;
+  else
+    reinterpret_cast<uint16_t*>(p)[i] = (uint16_t)f32_to_bf16(v);
 }
 
-// Row byte pitch of a weight matrix with `cols` inputs.
-template <int WK> __device__ __forceinline__ size_t row_bytes(int cols) {
-  return WK == W_F32 ? (size_t)cols * 4 : WK == W_BF16 ? (size_t)cols * 2 : (size_t)cols / 2;
+// Element i of a bias row held as raw words (bf16: two per word).
+template <typename XT> __device__ __forceinline__ float bias_elem(uint32_t word, int i) {
+  if (sizeof(XT) == 4) return __uint_as_float(word);
+  return __uint_as_float((i & 1) ? (word & 0xFFFF0000u) : (word << 16));
 }
 
 struct GateUpArgs {
@@ -188,95 +178,148 @@ struct GateUpArgs {
   const int32_t* offsets;
   const int32_t* sorted_assign;
   void* h;
-  int32_t T, k, H, E, F, Fs, shared, oai;
+  int32_t T, k, H, E, F, Fs, shared, oai, seg_mode;
   float alpha, limit;
 };
 
 // h[p][f] = act(gate row f . x_t, up row f . x_t) for every sorted position
-// p of the block's expert segment.  Grid: (segment slot, tile of 32 features).
-template <typename XT, int WK>
-__global__ __launch_bounds__(kThreads) void k_gateup_gemv(GateUpArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  XT* xs = reinterpret_cast<XT*>(smem);
-  const int nseg = a.E + a.shared;
-  const int e = find_segment(a.offsets, nseg, blockIdx.x);
-  if (e < 0) return;
-  const bool sh = e == a.E;
+// p of the workgroup's segment.  Grid: (segment slot, groups of
+// kWaves * RPW features).
+// sorted_assign is passed on its own, read-only and unaliased, so the
+// uniform reads of it are scalar loads that never wait behind weight loads.
+template <typename XT, int WK, int NP>
+__global__ __launch_bounds__(kWaves * kWave) void k_gateup_gemv(GateUpArgs a, const int32_t* __restrict__ sorted) {
+  constexpr int RPW = gateup_rows_per_wave(WK, NP);
+  constexpr int XQ = Wp<WK>::kXq;
+  constexpr int kCh = chunk_tokens(WK);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const Seg sg = block_segment(a.offsets, a.E, a.shared, a.seg_mode);
+  if (sg.e < 0) return;
+  const bool sh = sg.e == a.E;
   const int Fe = sh ? a.Fs : a.F;
-  if (blockIdx.y * kPairsPerBlock >= Fe) return;
-  const int grp = threadIdx.x / kGroup, lig = threadIdx.x & (kGroup - 1);
-  const int f = blockIdx.y * kPairsPerBlock + grp;
-  const bool active = f < Fe;
-  const int fr = active ? f : Fe - 1;
-  const uint8_t *rg, *ru, *sg = nullptr, *su = nullptr;
-  constexpr int WS = WK == W_MXFP4 ? W_BF16 : WK;  // shared-expert element kind
+  const int f0 = (blockIdx.y * kWaves + wv) * RPW;
+  if (f0 >= Fe) return;
+  const int nr = min(RPW, Fe - f0);
+  const size_t rb = row_bytes<WK>(a.H);
+  const int P = (int)(rb / 16);
+  const bool oai = a.oai && !sh;
+  const size_t e = (size_t)sg.e;
+  // rows of feature f0 + r: gate at gb + r * stride, up at ub + r * stride
+  const uint8_t *gb, *ub;
+  size_t stride = rb;
   if (sh) {
-    rg = (const uint8_t*)a.sh_gate_w + (size_t)fr * row_bytes<WS>(a.H);
-    ru = (const uint8_t*)a.sh_up_w + (size_t)fr * row_bytes<WS>(a.H);
-  } else if (a.oai) {
-    const size_t rb = row_bytes<WK>(a.H);
-    rg = (const uint8_t*)a.gate_w + ((size_t)e * 2 * a.F + 2 * fr) * rb;
-    ru = rg + rb;
-    if (WK == W_MXFP4) {
-      sg = a.scales + ((size_t)e * 2 * a.F + 2 * fr) * (a.H / 32);
-      su = sg + a.H / 32;
-    }
+    gb = (const uint8_t*)a.sh_gate_w + (size_t)f0 * rb;
+    ub = (const uint8_t*)a.sh_up_w + (size_t)f0 * rb;
+  } else if (oai) {
+    gb = (const uint8_t*)a.gate_w + (e * 2 * a.F + 2 * f0) * rb;
+    ub = gb + rb;
+    stride = 2 * rb;
   } else {
-    const size_t rb = row_bytes<WK>(a.H);
-    rg = (const uint8_t*)a.gate_w + ((size_t)e * a.F + fr) * rb;
-    ru = (const uint8_t*)a.up_w + ((size_t)e * a.F + fr) * rb;
+    gb = (const uint8_t*)a.gate_w + (e * a.F + f0) * rb;
+    ub = (const uint8_t*)a.up_w + (e * a.F + f0) * rb;
   }
-  const int p0 = a.offsets[e];
-  const int n = a.offsets[e + 1] - p0;
-  const int64_t nas = (int64_t)a.T * a.k;
-  float bg = 0.f, bu = 0.f;
-  if (a.oai && !sh && a.gate_up_b) {
-    bg = xscalar<XT>((const XT*)a.gate_up_b, (size_t)e * 2 * a.F + 2 * fr);
-    bu = xscalar<XT>((const XT*)a.gate_up_b, (size_t)e * 2 * a.F + 2 * fr + 1);
+  const uint32_t span = (uint32_t)((nr - 1) * stride + rb);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(gb, span), ru = make_rsrc(ub, span);
+  const int nas = a.T * a.k;
+  // gate/up biases of the rows: one word per row (bf16 pair) or two (fp32)
+  uint32_t bw[RPW][2];
+  {
+    const void* bb = oai && a.gate_up_b ? (const void*)((const XT*)a.gate_up_b + e * 2 * a.F + 2 * f0) : a.x;
+    const __amdgpu_buffer_rsrc_t rbias = make_rsrc(bb, oai && a.gate_up_b ? (uint32_t)(nr * 2 * sizeof(XT)) : 0u);
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bw[r][j] = (sizeof(XT) == 4 || j == 0)
+                       ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rbias, (int)(r * 2 * sizeof(XT) + j * 4), 0, 0)
+                       : 0u;
   }
-  const int xpieces = a.H * (int)sizeof(XT) / 16;  // 16-byte pieces per x row
-  for (int tb = 0; tb < n; tb += kStage) {
-    const int nt = min(kStage, n - tb);
-    if (tb) __syncthreads();
-    for (int i = threadIdx.x; i < nt * xpieces; i += kThreads) {
-      const int j = i / xpieces, q = i - j * xpieces;
-      const int sa = a.sorted_assign[p0 + tb + j];
-      const int t = sa < nas ? sa / a.k : (int)(sa - nas);
-      reinterpret_cast<uint4*>(xs)[i] = reinterpret_cast<const uint4*>((const XT*)a.x + (size_t)t * a.H)[q];
+  uint4 G[RPW][NP], U[RPW][NP];
+  uint32_t SG[RPW][NP], SU[RPW][NP];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int q = lane + p * kWave;
+      const uint32_t off = q < P ? (uint32_t)(r * stride + q * 16) : kOutOfRange;
+      G[r][p] = buf_load16(rg, off, 0);
+      U[r][p] = buf_load16(ru, off, 0);
     }
-    __syncthreads();
-    float acc[2][kStage];
+  if (WK == W_MXFP4) {
+    const size_t srow = (size_t)a.H / 32;
+    const uint8_t* sgb = a.scales + (e * 2 * a.F + 2 * f0) * srow;
+    const uint32_t sspan = (uint32_t)((nr - 1) * 2 * srow + srow);
+    const __amdgpu_buffer_rsrc_t rsg = make_rsrc(sgb, sspan), rsu = make_rsrc(sgb + srow, sspan);
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int r = 0; r < RPW; ++r)
 #pragma unroll
-      for (int i = 0; i < kStage; ++i) acc[r][i] = 0.f;
-    if (sh || WK != W_MXFP4)
-      rows2_dot_n<XT, WS>(nt, (const uint4*)rg, (const uint4*)ru, sg, su, xs, a.H, lig, acc);
-    else
-      rows2_dot_n<XT, WK>(nt, (const uint4*)rg, (const uint4*)ru, sg, su, xs, a.H, lig, acc);
-#pragma unroll
-    for (int i = 0; i < kStage; ++i) {
-      acc[0][i] = group8_sum(acc[0][i]);
-      acc[1][i] = group8_sum(acc[1][i]);
-    }
-    if (active) {
-#pragma unroll
-      for (int i = 0; i < kStage; ++i) {
-        if (i < nt && i == lig) {
-          float hv;
-          if (a.oai && !sh) {
-            const float g = fminf(acc[0][i] + bg, a.limit);
-            const float u = fminf(fmaxf(acc[1][i] + bu, -a.limit), a.limit);
-            hv = (u + 1.f) * (g / (1.f + expf(-a.alpha * g)));
-          } else {
-            const float g = acc[0][i];
-            hv = g / (1.f + expf(-g)) * acc[1][i];
-          }
-          const int p = p0 + tb + i;
-          const size_t row = p < nas ? (size_t)p * a.F : (size_t)nas * a.F + (size_t)(p - nas) * a.Fs;
-          xstore<XT>((XT*)a.h, row + f, hv);
-        }
+      for (int p = 0; p < NP; ++p) {
+        const int q = lane + p * kWave;
+        const uint32_t off = q < P ? (uint32_t)(r * 2 * srow + q) : kOutOfRange;
+        SG[r][p] = buf_load_u8(rsg, off, 0);
+        SU[r][p] = buf_load_u8(rsu, off, 0);
       }
+  }
+  const size_t xrb = (size_t)a.H * sizeof(XT);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)((size_t)a.T * xrb));
+  uint4 X0[kCh][NP][XQ], X1[kCh][NP][XQ];
+  auto load_chunk = [&](int i0, uint4 (&X)[kCh][NP][XQ]) {
+#pragma unroll
+    for (int i = 0; i < kCh; ++i) {
+      const int ii = i0 + i;
+      const int as = ii < sg.n ? sorted[sg.p0 + ii] : 0;
+      const int t = as < nas ? as / a.k : as - nas;
+      load_act<XT, WK, NP>(rx, (uint32_t)(t * xrb), ii < sg.n, P, X[i]);
+    }
+  };
+  auto compute_chunk = [&](int i0, const uint4 (&X)[kCh][NP][XQ]) {
+    float ag[RPW][kCh], au[RPW][kCh];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+      for (int i = 0; i < kCh; ++i) {
+        float g = 0.f, u = 0.f;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          g = Wp<WK>::dot(G[r][p], X[i][p], g, WK == W_MXFP4 ? SG[r][p] : 0u);
+          u = Wp<WK>::dot(U[r][p], X[i][p], u, WK == W_MXFP4 ? SU[r][p] : 0u);
+        }
+        ag[r][i] = g;
+        au[r][i] = u;
+      }
+#pragma unroll
+    for (int i = 0; i < kCh; ++i) {
+      const int p = sg.p0 + i0 + i;
+      if (i0 + i < sg.n) {
+        float hv = 0.f;
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+          float gs = wave_sum(ag[r][i]), us = wave_sum(au[r][i]);
+          float v;
+          if (oai) {
+            gs += bias_elem<XT>(bw[r][0], 0);
+            us += sizeof(XT) == 4 ? __uint_as_float(bw[r][1]) : bias_elem<XT>(bw[r][0], 1);
+            const float g = fminf(gs, a.limit);
+            const float u = fminf(fmaxf(us, -a.limit), a.limit);
+            v = (u + 1.f) * (g / (1.f + expf(-a.alpha * g)));
+          } else {
+            v = gs / (1.f + expf(-gs)) * us;
+          }
+          hv = lane == r ? v : hv;
+        }
+        const size_t row = p < nas ? (size_t)p * a.F : (size_t)nas * a.F + (size_t)(p - nas) * a.Fs;
+        if (lane < nr) store_elem<XT>(a.h, row + f0 + lane, hv);
+      }
+    }
+  };
+  load_chunk(0, X0);
+  for (int i0 = 0; i0 < sg.n; i0 += 2 * kCh) {
+    if (i0 + kCh < sg.n) load_chunk(i0 + kCh, X1);
+    compute_chunk(i0, X0);
+    if (i0 + kCh < sg.n) {
+      if (i0 + 2 * kCh < sg.n) load_chunk(i0 + 2 * kCh, X0);
+      compute_chunk(i0 + kCh, X1);
     }
   }
 }
@@ -290,78 +333,109 @@ struct DownArgs {
   const int32_t* offsets;
   const int32_t* sorted_assign;
   float* y;                 // [T*k (+T)][H], row = assignment id
-  int32_t T, k, H, E, F, Fs, shared;
+  int32_t T, k, H, E, F, Fs, shared, seg_mode;
 };
 
 // y[a][o] = down row o . h[p] (+ bias) for every sorted position p of the
 // segment, written at the row of its assignment id a.  Grid: (segment slot,
-// tile of 64 output rows); a group of 8 lanes owns rows o and o + 32.
-template <typename XT, int WK>
-__global__ __launch_bounds__(kThreads) void k_down_gemv(DownArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  XT* hs = reinterpret_cast<XT*>(smem);
-  const int nseg = a.E + a.shared;
-  const int e = find_segment(a.offsets, nseg, blockIdx.x);
-  if (e < 0) return;
-  const bool sh = e == a.E;
+// groups of kWaves * RPW output rows).
+template <typename XT, int WK, int NP>
+__global__ __launch_bounds__(kWaves * kWave) void k_down_gemv(DownArgs a, const int32_t* __restrict__ sorted) {
+  constexpr int RPW = rows_per_wave(WK, NP);
+  constexpr int XQ = Wp<WK>::kXq;
+  constexpr int kCh = chunk_tokens(WK);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const Seg sg = block_segment(a.offsets, a.E, a.shared, a.seg_mode);
+  if (sg.e < 0) return;
+  const bool sh = sg.e == a.E;
   const int Fe = sh ? a.Fs : a.F;
-  const int obase = blockIdx.y * 2 * kPairsPerBlock;
-  if (obase >= a.H) return;
-  const int grp = threadIdx.x / kGroup, lig = threadIdx.x & (kGroup - 1);
-  const int o0 = obase + grp, o1 = obase + kPairsPerBlock + grp;
-  const int q0 = min(o0, a.H - 1), q1 = min(o1, a.H - 1);
-  constexpr int WS = WK == W_MXFP4 ? W_BF16 : WK;
-  const uint8_t *r0, *r1, *s0 = nullptr, *s1 = nullptr;
-  if (sh) {
-    r0 = (const uint8_t*)a.sh_down_w + (size_t)q0 * row_bytes<WS>(a.Fs);
-    r1 = (const uint8_t*)a.sh_down_w + (size_t)q1 * row_bytes<WS>(a.Fs);
-  } else {
-    const size_t rb = row_bytes<WK>(a.F);
-    r0 = (const uint8_t*)a.down_w + ((size_t)e * a.H + q0) * rb;
-    r1 = (const uint8_t*)a.down_w + ((size_t)e * a.H + q1) * rb;
-    if (WK == W_MXFP4) {
-      s0 = a.scales + ((size_t)e * a.H + q0) * (a.F / 32);
-      s1 = a.scales + ((size_t)e * a.H + q1) * (a.F / 32);
-    }
+  const int o0 = (blockIdx.y * kWaves + wv) * RPW;
+  if (o0 >= a.H) return;
+  const int nr = min(RPW, a.H - o0);
+  const size_t rb = row_bytes<WK>(Fe);
+  const int P = (int)(rb / 16);
+  const size_t e = (size_t)sg.e;
+  const uint8_t* wb = sh ? (const uint8_t*)a.sh_down_w + (size_t)o0 * rb
+                         : (const uint8_t*)a.down_w + (e * a.H + o0) * rb;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wb, (uint32_t)(nr * rb));
+  const int nas = a.T * a.k;
+  // bias words of the rows (bf16: element o0 + r in word (o0 + r) / 2)
+  uint32_t bw[RPW];
+  {
+    const bool hb = !sh && a.down_b;
+    const size_t first = hb ? (e * a.H + o0) & ~(size_t)(sizeof(XT) == 4 ? 0 : 1) : 0;
+    const void* bb = hb ? (const void*)((const XT*)a.down_b + first) : a.h;
+    const uint32_t bbytes = sizeof(XT) == 4 ? (uint32_t)nr * 4 : (uint32_t)(((o0 & 1) + nr - 1) / 2 * 4 + 4);
+    const __amdgpu_buffer_rsrc_t rbias = make_rsrc(bb, hb ? bbytes : 0u);
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+      bw[r] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+          rbias, (int)(sizeof(XT) == 4 ? r * 4 : ((o0 & 1) + r) / 2 * 4), 0, 0);
   }
-  const int p0 = a.offsets[e];
-  const int n = a.offsets[e + 1] - p0;
-  const int64_t nas = (int64_t)a.T * a.k;
-  const XT* hb = (const XT*)a.h;
-  const XT* hbase = sh ? hb + (size_t)nas * a.F + (size_t)(p0 - nas) * a.Fs : hb + (size_t)p0 * a.F;
-  float b0 = 0.f, b1 = 0.f;
-  if (!sh && a.down_b) {
-    b0 = xscalar<XT>((const XT*)a.down_b, (size_t)e * a.H + q0);
-    b1 = xscalar<XT>((const XT*)a.down_b, (size_t)e * a.H + q1);
-  }
-  const int hpieces = Fe * (int)sizeof(XT) / 16;
-  for (int tb = 0; tb < n; tb += kStage) {
-    const int nt = min(kStage, n - tb);
-    if (tb) __syncthreads();
-    for (int i = threadIdx.x; i < nt * hpieces; i += kThreads)
-      reinterpret_cast<uint4*>(hs)[i] = reinterpret_cast<const uint4*>(hbase + (size_t)tb * Fe)[i];
-    __syncthreads();
-    float acc[2][kStage];
+  uint4 W[RPW][NP];
+  uint32_t S[RPW][NP];
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+  for (int r = 0; r < RPW; ++r)
 #pragma unroll
-      for (int i = 0; i < kStage; ++i) acc[r][i] = 0.f;
-    if (sh || WK != W_MXFP4)
-      rows2_dot_n<XT, WS>(nt, (const uint4*)r0, (const uint4*)r1, s0, s1, hs, Fe, lig, acc);
-    else
-      rows2_dot_n<XT, WK>(nt, (const uint4*)r0, (const uint4*)r1, s0, s1, hs, Fe, lig, acc);
-#pragma unroll
-    for (int i = 0; i < kStage; ++i) {
-      acc[0][i] = group8_sum(acc[0][i]);
-      acc[1][i] = group8_sum(acc[1][i]);
+    for (int p = 0; p < NP; ++p) {
+      const int q = lane + p * kWave;
+      W[r][p] = buf_load16(rw, q < P ? (uint32_t)(r * rb + q * 16) : kOutOfRange, 0);
     }
+  if (WK == W_MXFP4) {
+    const size_t srow = (size_t)a.F / 32;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + (e * a.H + o0) * srow, (uint32_t)(nr * srow));
 #pragma unroll
-    for (int i = 0; i < kStage; ++i)
-      if (i < nt && i == lig) {
-        const int asg = a.sorted_assign[p0 + tb + i];
-        if (o0 < a.H) a.y[(size_t)asg * a.H + o0] = acc[0][i] + b0;
-        if (o1 < a.H) a.y[(size_t)asg * a.H + o1] = acc[1][i] + b1;
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int q = lane + p * kWave;
+        S[r][p] = buf_load_u8(rs, q < P ? (uint32_t)(r * srow + q) : kOutOfRange, 0);
       }
+  }
+  const size_t hrb = (size_t)Fe * sizeof(XT);
+  const XT* hseg = sh ? (const XT*)a.h + (size_t)nas * a.F + (size_t)(sg.p0 - nas) * a.Fs
+                      : (const XT*)a.h + (size_t)sg.p0 * a.F;
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(hseg, (uint32_t)((size_t)sg.n * hrb));
+  uint4 X0[kCh][NP][XQ], X1[kCh][NP][XQ];
+  auto load_chunk = [&](int i0, uint4 (&X)[kCh][NP][XQ]) {
+#pragma unroll
+    for (int i = 0; i < kCh; ++i)
+      load_act<XT, WK, NP>(rh, (uint32_t)((i0 + i) * hrb), i0 + i < sg.n, P, X[i]);
+  };
+  auto compute_chunk = [&](int i0, const uint4 (&X)[kCh][NP][XQ]) {
+    float acc[RPW][kCh];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+      for (int i = 0; i < kCh; ++i) {
+        float v = 0.f;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) v = Wp<WK>::dot(W[r][p], X[i][p], v, WK == W_MXFP4 ? S[r][p] : 0u);
+        acc[r][i] = v;
+      }
+#pragma unroll
+    for (int i = 0; i < kCh; ++i) {
+      if (i0 + i < sg.n) {
+        float yv = 0.f;
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+          const float v = wave_sum(acc[r][i]) + bias_elem<XT>(bw[r], o0 + r);
+          yv = lane == r ? v : yv;
+        }
+        const int as = sorted[sg.p0 + i0 + i];
+        if (lane < nr) a.y[(size_t)as * a.H + o0 + lane] = yv;
+      }
+    }
+  };
+  load_chunk(0, X0);
+  for (int i0 = 0; i0 < sg.n; i0 += 2 * kCh) {
+    if (i0 + kCh < sg.n) load_chunk(i0 + kCh, X1);
+    compute_chunk(i0, X0);
+    if (i0 + kCh < sg.n) {
+      if (i0 + 2 * kCh < sg.n) load_chunk(i0 + 2 * kCh, X0);
+      compute_chunk(i0 + kCh, X1);
+    }
   }
 }
 
@@ -402,12 +476,68 @@ hipError_t launch_down_mfma(const moe_config* c, const moe_weights* w, const voi
                             const int32_t* sorted_assign, int32_t T, float* y, hipStream_t s);
 bool mfma_shapes_ok(const moe_config* c);
 
-static int max_segments(const moe_config* c, int32_t T) {
+static int max_routed_segments(const moe_config* c, int32_t T) {
   const int64_t nk = (int64_t)T * c->top_k;
-  return (int)(nk < c->n_expert ? nk : c->n_expert) + (c->shared_ff > 0 ? 1 : 0);
+  return (int)(nk < c->n_expert ? nk : c->n_expert);
 }
 
-static size_t stage_rows(int32_t T) { return (size_t)(T < kStage ? T : kStage); }
+// 16-byte pieces per lane for rows of `cols` inputs: 1, 2, 4, 6 or 8.
+static int pieces_per_lane(size_t row_bytes) {
+  const size_t np = (row_bytes / 16 + kWave - 1) / kWave;
+  return np <= 1 ? 1 : np <= 2 ? 2 : np <= 4 ? 4 : np <= 6 ? 6 : 8;
+}
+static size_t row_bytes_of(int wdt, int cols) {
+  return wdt == MOE_DTYPE_F32 ? (size_t)cols * 4 : wdt == MOE_DTYPE_BF16 ? (size_t)cols * 2 : (size_t)cols / 2;
+}
+
+template <typename XT, int WK, int NP> static void gateup_launch(dim3 g, const GateUpArgs& a, hipStream_t s) {
+  k_gateup_gemv<XT, WK, NP><<<g, kWaves * kWave, 0, s>>>(a, a.sorted_assign);
+}
+template <typename XT, int WK, int NP> static void down_launch(dim3 g, const DownArgs& a, hipStream_t s) {
+  k_down_gemv<XT, WK, NP><<<g, kWaves * kWave, 0, s>>>(a, a.sorted_assign);
+}
+
+#define MOE_NP_SWITCH(FN, XT, WK, np, grid, args, s) \
+  switch (np) {                                      \
+    case 1: FN<XT, WK, 1>(grid, args, s); break;     \
+    case 2: FN<XT, WK, 2>(grid, args, s); break;     \
+    case 4: FN<XT, WK, 4>(grid, args, s); break;     \
+    case 6: FN<XT, WK, 6>(grid, args, s); break;     \
+    default: FN<XT, WK, 8>(grid, args, s); break;    \
+  }
+
+// One gate/up launch over the segments seg_mode selects, with routed-weight
+// kind wdt.
+static void gateup_dispatch(const moe_config* c, const GateUpArgs& a, int wdt, int nslots, int fe, hipStream_t s) {
+  const int np = pieces_per_lane(row_bytes_of(wdt, c->hidden));
+  const int rpw = gateup_rows_per_wave(wdt == MOE_DTYPE_F32 ? W_F32 : wdt == MOE_DTYPE_BF16 ? W_BF16 : W_MXFP4, np);
+  const dim3 grid(nslots, (fe + kWaves * rpw - 1) / (kWaves * rpw));
+  if (c->x_dtype == MOE_DTYPE_F32) {
+    MOE_NP_SWITCH(gateup_launch, float, W_F32, np, grid, a, s)
+  } else if (wdt == MOE_DTYPE_BF16) {
+    MOE_NP_SWITCH(gateup_launch, uint16_t, W_BF16, np, grid, a, s)
+  } else if (np <= 1) {
+    gateup_launch<uint16_t, W_MXFP4, 1>(grid, a, s);
+  } else {
+    gateup_launch<uint16_t, W_MXFP4, 2>(grid, a, s);
+  }
+}
+
+static void down_dispatch(const moe_config* c, const DownArgs& a, int wdt, int nslots, int cols, hipStream_t s) {
+  const int np = pieces_per_lane(row_bytes_of(wdt, cols));
+  const int rpw = rows_per_wave(wdt == MOE_DTYPE_F32 ? W_F32 : wdt == MOE_DTYPE_BF16 ? W_BF16 : W_MXFP4, np);
+  const dim3 grid(nslots, (c->hidden + kWaves * rpw - 1) / (kWaves * rpw));
+  if (c->x_dtype == MOE_DTYPE_F32) {
+    MOE_NP_SWITCH(down_launch, float, W_F32, np, grid, a, s)
+  } else if (wdt == MOE_DTYPE_BF16) {
+    MOE_NP_SWITCH(down_launch, uint16_t, W_BF16, np, grid, a, s)
+  } else if (np <= 1) {
+    down_launch<uint16_t, W_MXFP4, 1>(grid, a, s);
+  } else {
+    down_launch<uint16_t, W_MXFP4, 2>(grid, a, s);
+  }
+}
+#undef MOE_NP_SWITCH
 
 hipError_t launch_expert_ffn(const moe_config* c, const moe_weights* w, const void* x, const int32_t* offsets,
                              const int32_t* sorted_assign, int32_t T, void* h, hipStream_t s) {
@@ -427,16 +557,19 @@ hipError_t launch_expert_ffn(const moe_config* c, const moe_weights* w, const vo
   a.h = h;
   a.T = T; a.k = c->top_k; a.H = c->hidden; a.E = c->n_expert; a.F = c->expert_ff; a.Fs = c->shared_ff;
   a.shared = c->shared_ff > 0; a.oai = oai; a.alpha = c->act_alpha; a.limit = c->act_limit;
-  const int fmax = c->expert_ff > c->shared_ff ? c->expert_ff : c->shared_ff;
-  dim3 grid(max_segments(c, T), (fmax + kPairsPerBlock - 1) / kPairsPerBlock);
-  const size_t esz = c->x_dtype == MOE_DTYPE_F32 ? 4 : 2;
-  const size_t lds = stage_rows(T) * c->hidden * esz;
-  if (c->x_dtype == MOE_DTYPE_F32)
-    k_gateup_gemv<float, W_F32><<<grid, kThreads, lds, s>>>(a);
-  else if (c->w_dtype == MOE_DTYPE_BF16)
-    k_gateup_gemv<uint16_t, W_BF16><<<grid, kThreads, lds, s>>>(a);
-  else
-    k_gateup_gemv<uint16_t, W_MXFP4><<<grid, kThreads, lds, s>>>(a);
+  const int routed = max_routed_segments(c, T);
+  if (c->w_dtype != MOE_DTYPE_MXFP4 || !a.shared) {
+    // routed and shared segments share one launch (same weight element kind)
+    a.seg_mode = 0;
+    const int fmax = c->expert_ff > c->shared_ff ? c->expert_ff : c->shared_ff;
+    gateup_dispatch(c, a, c->w_dtype, routed + a.shared, fmax, s);
+  } else {
+    // MXFP4 routed experts, bf16 shared expert: one launch each
+    a.seg_mode = 1;
+    gateup_dispatch(c, a, MOE_DTYPE_MXFP4, routed, c->expert_ff, s);
+    a.seg_mode = 2;
+    gateup_dispatch(c, a, MOE_DTYPE_BF16, 1, c->shared_ff, s);
+  }
   return hipGetLastError();
 }
 
@@ -455,16 +588,19 @@ hipError_t launch_down(const moe_config* c, const moe_weights* w, const void* h,
   a.y = y;
   a.T = T; a.k = c->top_k; a.H = c->hidden; a.E = c->n_expert; a.F = c->expert_ff; a.Fs = c->shared_ff;
   a.shared = c->shared_ff > 0;
-  dim3 grid(max_segments(c, T), (c->hidden + 2 * kPairsPerBlock - 1) / (2 * kPairsPerBlock));
-  const size_t esz = c->x_dtype == MOE_DTYPE_F32 ? 4 : 2;
-  const int fmax = c->expert_ff > c->shared_ff ? c->expert_ff : c->shared_ff;
-  const size_t lds = stage_rows(T) * fmax * esz;
-  if (c->x_dtype == MOE_DTYPE_F32)
-    k_down_gemv<float, W_F32><<<grid, kThreads, lds, s>>>(a);
-  else if (c->w_dtype == MOE_DTYPE_BF16)
-    k_down_gemv<uint16_t, W_BF16><<<grid, kThreads, lds, s>>>(a);
-  else
-    k_down_gemv<uint16_t, W_MXFP4><<<grid, kThreads, lds, s>>>(a);
+  const int routed = max_routed_segments(c, T);
+  if (c->w_dtype != MOE_DTYPE_MXFP4 || !a.shared) {
+    a.seg_mode = 0;
+    // one piece count for both: the wider of the routed and shared rows
+    const int cols = row_bytes_of(c->w_dtype, c->expert_ff) >= row_bytes_of(c->w_dtype, c->shared_ff)
+                         ? c->expert_ff : c->shared_ff;
+    down_dispatch(c, a, c->w_dtype, routed + a.shared, cols, s);
+  } else {
+    a.seg_mode = 1;
+    down_dispatch(c, a, MOE_DTYPE_MXFP4, routed, c->expert_ff, s);
+    a.seg_mode = 2;
+    down_dispatch(c, a, MOE_DTYPE_BF16, 1, c->shared_ff, s);
+  }
   return hipGetLastError();
 }
 

@@ -111,6 +111,38 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return r;
 }
 
+// Raw buffer resource over [base, base + bytes): loads at offsets past the
+// end return zero (gfx9 descriptor word 3: 32-bit data format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ uint32_t buf_load_u8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
+}
+constexpr uint32_t kOutOfRange = 0x80000000u;  // an offset past every buffer: loads give 0
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Direct buffer -> LDS load of 16 bytes per lane: lane l of the wave writes
+// LDS bytes [lds + 16 l, lds + 16 l + 16) (lds must be wave-uniform).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, (int)voff, 0, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter limited (gfx9 encoding).
+template <int N> __device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier for the K pipeline: LDS writes of this wave complete,
+// then s_barrier.  Unlike __syncthreads it is not a release fence, so the
+// buffer->LDS loads still in flight for later steps are not waited for; the
+// loads of the step about to be read are waited for explicitly (wait_vm).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // E8M0 exponent byte -> 2^(s-127) as fp32 (s = 0 gives 2^-127, subnormal).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
   return s ? __uint_as_float(s << 23) : __uint_as_float(0x00400000u);

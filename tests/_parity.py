@@ -4,7 +4,6 @@ Output tolerances are normwise, max|gpu - ref| <= tol * max|ref|: 1e-4 for
 fp32 layers, 2e-2 for bf16 weights, 3e-2 for MXFP4 weights.  Routing weights
 and the shared gate: <= 1e-5 relative per element (softmax / sigmoid in
 fp32, "qwen35moe CPU-reference golden vectors", Kernel 4 tolerance)."""
-import functools
 import sys
 
 import numpy as np
@@ -23,9 +22,21 @@ def log(msg):
     sys.stdout.flush()
 
 
-@functools.lru_cache(maxsize=6)
+_WEIGHTS = {}
+
+
 def cached_case(name, T, only=None):
-    return synth.make_case(name, T=T, only=None if only is None else set(only))
+    """make_case(name, T), with the weights of each named case generated once
+    per process (they do not depend on T; tokens and drawn logits do)."""
+    if only is not None or name == "tiny_fp32":
+        return synth.make_case(name, T=T, only=None if only is None else set(only))
+    if name not in _WEIGHTS:
+        c = synth.make_case(name, T=T)
+        _WEIGHTS[name] = {k: v for k, v in c.t.items() if k not in ("x", "logits")}
+        return c
+    c = synth.make_case(name, T=T, only={"x", "logits"})
+    c.t.update(_WEIGHTS[name])
+    return c
 
 
 def normwise(got, ref):

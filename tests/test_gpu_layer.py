@@ -31,6 +31,9 @@ LAYERS = [
     ("gptoss20b_mxfp4", 16, None, {}),
     ("gptoss20b_mxfp4", 150, None, dict(E=8, H=320, F=192, k=2)),
     ("gptoss20b_mxfp4", 2048, 20, {}),
+    ("gptoss20b_mxfp4", 16, None, dict(E=8, H=320, F=192, k=2)),  # fused down + combine, MXFP4 rows
+    ("gptoss20b_bf16", 2, None, {}),                          # fused down + combine, 6 pieces per lane
+    ("gptoss20b_mxfp4", 2, None, {}),                         # fused down + combine, 2 pieces per lane
 ]
 
 
@@ -144,7 +147,7 @@ def _h_row(case, h_flat, p):
     return h_flat[q:q + case.Fs]
 
 
-STEP = [LAYERS[i] for i in (0, 1, 4, 5, 6, 8, 9, 11, 12)]
+STEP = [LAYERS[i] for i in (0, 1, 4, 5, 6, 8, 9, 11, 12, 13, 14, 15)]
 
 
 @pytest.mark.parametrize("p", STEP, ids=_ids)
