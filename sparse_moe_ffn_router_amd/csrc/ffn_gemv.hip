@@ -440,21 +440,34 @@ __global__ __launch_bounds__(kWaves * kWave) void k_down_gemv(DownArgs a, const 
 }
 
 // out[t][o] = sum_j w[t][j] y[t*k + j][o] (+ sgate[t] y[T*k + t][o]), the
-// picks summed in pick order.
+// picks summed in pick order.  The y rows of up to 8 picks are loaded
+// together before the sums, so the loads overlap.
 __global__ __launch_bounds__(256) void k_combine_gather(const float* __restrict__ y, const float* __restrict__ topk_w,
                                                         const float* __restrict__ sgate, int32_t T, int32_t k,
                                                         int32_t H, float* __restrict__ out) {
+  constexpr int kBatch = 8;
   const int t = blockIdx.y;
   const int o4 = blockIdx.x * 256 + threadIdx.x;  // float4 index
   if (o4 * 4 >= H) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const float wj = topk_w[(size_t)t * k + j];
-    const float4 v = reinterpret_cast<const float4*>(y + ((size_t)t * k + j) * H)[o4];
-    acc.x = fmaf(wj, v.x, acc.x);
-    acc.y = fmaf(wj, v.y, acc.y);
-    acc.z = fmaf(wj, v.z, acc.z);
-    acc.w = fmaf(wj, v.w, acc.w);
+  for (int j0 = 0; j0 < k; j0 += kBatch) {
+    float4 v[kBatch];
+    float wj[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const bool ok = j0 + j < k;
+      wj[j] = ok ? topk_w[(size_t)t * k + j0 + j] : 0.f;
+      v[j] = ok ? reinterpret_cast<const float4*>(y + ((size_t)t * k + j0 + j) * H)[o4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (j0 + j < k) {
+        acc.x = fmaf(wj[j], v[j].x, acc.x);
+        acc.y = fmaf(wj[j], v[j].y, acc.y);
+        acc.z = fmaf(wj[j], v[j].z, acc.z);
+        acc.w = fmaf(wj[j], v[j].w, acc.w);
+      }
+    }
   }
   if (sgate) {
     const float g = sgate[t];

@@ -33,7 +33,7 @@ __device__ __forceinline__ int gate_token_n(const float* __restrict__ l, int E, 
   }
   uint32_t used = 0;
   int my_idx = 0;
-  float my_val = 0.f;
+  uint32_t my_key = 0;
   for (int j = 0; j < k; ++j) {
     uint64_t best = 0;
 #pragma unroll
@@ -42,9 +42,14 @@ __device__ __forceinline__ int gate_token_n(const float* __restrict__ l, int E, 
     best = wave_max_u64(best);
     const int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
     if ((e & (kWave - 1)) == lane) used |= 1u << (e / kWave);
-    if (lane == j) my_idx = e;
+    if (lane == j) {
+      my_idx = e;
+      my_key = (uint32_t)(best >> 32);
+    }
   }
-  my_val = l[my_idx];
+  // the pick's logit back from its key (order_key is invertible; a -0 logit
+  // comes back as +0, which exp() treats the same)
+  const float my_val = __uint_as_float((my_key & 0x80000000u) ? (my_key & 0x7FFFFFFFu) : ~my_key);
   // pick 0 holds the largest logit, the softmax shift for both gatings
   const float m = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_val), 0));
   const float ej = lane < k ? expf(my_val - m) : 0.f;

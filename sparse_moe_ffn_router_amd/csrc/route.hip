@@ -11,7 +11,7 @@ namespace moe {
 namespace {
 
 constexpr int kRouterTokens = 8;  // tokens per pass of a wave
-constexpr int kRouterWaves = 4;   // router rows per workgroup (one per wave)
+constexpr int kRouterWaves = 1;   // router rows per workgroup (one per wave)
 constexpr int kMaxPieces = 8;     // 16-byte pieces per lane held at once
 
 template <typename XT> struct Vec;
