@@ -13,10 +13,13 @@
 // barrier.  Activation rows are processed two tokens at a time, the next
 // pair prefetched while the current one is reduced.
 //
+// These kernels serve fp32 and bf16 experts; MXFP4 experts have their own
+// (ffn_gemv_mx.hip).
+//
 // Sources: "qwen35moe - Forward-Pass Design", section "Shared-expert MoE
 // FFN" (SwiGLU experts, shared expert); "Phase 19: MoE - gpt-oss-20b",
 // section 2 Experts (interleaved gate_up with bias, clamps, (up+1) * gate *
-// sigmoid(alpha gate), down + bias) and section 3 (MXFP4 decode).
+// sigmoid(alpha gate), down + bias).
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -24,11 +27,11 @@ namespace {
 
 constexpr int kWaves = 4;  // wavefronts per workgroup
 
-enum { W_F32 = 0, W_BF16 = 1, W_MXFP4 = 2 };
+enum { W_F32 = 0, W_BF16 = 1 };
 
 // Bytes of one weight row with `cols` inputs.
 template <int WK> __host__ __device__ constexpr size_t row_bytes(int cols) {
-  return WK == W_F32 ? (size_t)cols * 4 : WK == W_BF16 ? (size_t)cols * 2 : (size_t)cols / 2;
+  return WK == W_F32 ? (size_t)cols * 4 : (size_t)cols * 2;
 }
 
 // A 16-byte weight piece and the activation bytes it multiplies.
@@ -53,43 +56,13 @@ template <> struct Wp<W_F32> {
     return acc;
   }
 };
-// MXFP4: a piece is one 32-element block (16 code bytes, low nibble first);
-// its E8M0 exponent is applied while converting the codes to bf16 (exact:
-// E2M1 values times 2^(e-127) are bf16 numbers for the exponents in use).
-template <> struct Wp<W_MXFP4> {
-  static constexpr int kElems = 32, kXq = 4;
-  __device__ static float dot(uint4 w, const uint4* x, float acc, uint32_t e8m0) {
-    const float scale = e8m0_to_f32(e8m0 & 0xFFu);
-    const uint32_t words[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t cw = words[q];
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, scale, 0),
-                                            __builtin_bit_cast(bf16x2_t, x[q].x), acc, false);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, scale, 1),
-                                            __builtin_bit_cast(bf16x2_t, x[q].y), acc, false);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, scale, 2),
-                                            __builtin_bit_cast(bf16x2_t, x[q].z), acc, false);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, scale, 3),
-                                            __builtin_bit_cast(bf16x2_t, x[q].w), acc, false);
-    }
-    return acc;
-  }
-};
-
-// Weight rows per wavefront for NP pieces per lane per row: about 8 pieces
-// (8 KiB) in flight per wavefront.
-// MXFP4 pieces hold 32 elements (64 activation bytes each), so fewer rows
-// and one token per chunk keep the registers in check.
-__host__ __device__ constexpr int rows_per_wave(int wk, int np) {
-  return wk == W_MXFP4 ? (np == 1 ? 4 : 2) : np >= 6 ? 1 : 8 / np;
-}
-// gate/up: a row pair per feature, about 16 pieces in flight
-__host__ __device__ constexpr int gateup_rows_per_wave(int wk, int np) {
-  return wk == W_MXFP4 ? (np == 1 ? 2 : 1) : np >= 6 ? 1 : np == 4 ? 2 : 4;
-}
+// Weight rows per wavefront for NP 16-byte pieces per lane per row: about
+// 8-16 KiB of weights each.
+__host__ __device__ constexpr int rows_per_wave(int np) { return np >= 6 ? 1 : 8 / np; }
+// gate/up: a row pair per feature
+__host__ __device__ constexpr int gateup_rows_per_wave(int np) { return np >= 6 ? 1 : np == 4 ? 2 : 4; }
 // tokens per register chunk
-__host__ __device__ constexpr int chunk_tokens(int wk) { return wk == W_MXFP4 ? 1 : 2; }
+constexpr int kCh = 2;
 
 struct Seg {
   int e, p0, n;
@@ -125,15 +98,9 @@ __device__ Seg find_segment(const int32_t* __restrict__ off, int nseg, int s) {
   return Seg{-1, 0, 0};
 }
 
-// The segment a workgroup works on: the blockIdx.x-th non-empty one among
-// the routed experts (and the shared expert unless seg_mode == 1), or the
-// shared expert alone (seg_mode == 2).
-__device__ __forceinline__ Seg block_segment(const int32_t* off, int E, int shared, int seg_mode) {
-  if (seg_mode == 2) {
-    const int p0 = __builtin_amdgcn_readfirstlane(off[E]);
-    return Seg{E, p0, __builtin_amdgcn_readfirstlane(off[E + 1]) - p0};
-  }
-  const Seg s = find_segment(off, E + (seg_mode == 0 ? shared : 0), blockIdx.x);
+// The segment a workgroup works on: the blockIdx.x-th non-empty one.
+__device__ __forceinline__ Seg block_segment(const int32_t* off, int nseg) {
+  const Seg s = find_segment(off, nseg, blockIdx.x);
   return Seg{__builtin_amdgcn_readfirstlane(s.e), __builtin_amdgcn_readfirstlane(s.p0),
              __builtin_amdgcn_readfirstlane(s.n)};
 }
@@ -171,14 +138,13 @@ struct GateUpArgs {
   const void* x;
   const void* gate_w;      // SWIGLU [E][F][H]  | OAI gate_up [E][2F][H]
   const void* up_w;        // SWIGLU [E][F][H]  | unused
-  const uint8_t* scales;   // MXFP4 gate_up scales [E][2F][H/32]
   const void* gate_up_b;   // OAI [E][2F]
   const void* sh_gate_w;   // [Fs][H]
   const void* sh_up_w;     // [Fs][H]
   const int32_t* offsets;
   const int32_t* sorted_assign;
   void* h;
-  int32_t T, k, H, E, F, Fs, shared, oai, seg_mode;
+  int32_t T, k, H, E, F, Fs, shared, oai;
   float alpha, limit;
 };
 
@@ -189,12 +155,11 @@ struct GateUpArgs {
 // uniform reads of it are scalar loads that never wait behind weight loads.
 template <typename XT, int WK, int NP>
 __global__ __launch_bounds__(kWaves * kWave) void k_gateup_gemv(GateUpArgs a, const int32_t* __restrict__ sorted) {
-  constexpr int RPW = gateup_rows_per_wave(WK, NP);
+  constexpr int RPW = gateup_rows_per_wave(NP);
   constexpr int XQ = Wp<WK>::kXq;
-  constexpr int kCh = chunk_tokens(WK);
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const Seg sg = block_segment(a.offsets, a.E, a.shared, a.seg_mode);
+  const Seg sg = block_segment(a.offsets, a.E + a.shared);
   if (sg.e < 0) return;
   const bool sh = sg.e == a.E;
   const int Fe = sh ? a.Fs : a.F;
@@ -236,7 +201,6 @@ __global__ __launch_bounds__(kWaves * kWave) void k_gateup_gemv(GateUpArgs a, co
                        : 0u;
   }
   uint4 G[RPW][NP], U[RPW][NP];
-  uint32_t SG[RPW][NP], SU[RPW][NP];
 #pragma unroll
   for (int r = 0; r < RPW; ++r)
 #pragma unroll
@@ -246,21 +210,6 @@ __global__ __launch_bounds__(kWaves * kWave) void k_gateup_gemv(GateUpArgs a, co
       G[r][p] = buf_load16(rg, off, 0);
       U[r][p] = buf_load16(ru, off, 0);
     }
-  if (WK == W_MXFP4) {
-    const size_t srow = (size_t)a.H / 32;
-    const uint8_t* sgb = a.scales + (e * 2 * a.F + 2 * f0) * srow;
-    const uint32_t sspan = (uint32_t)((nr - 1) * 2 * srow + srow);
-    const __amdgpu_buffer_rsrc_t rsg = make_rsrc(sgb, sspan), rsu = make_rsrc(sgb + srow, sspan);
-#pragma unroll
-    for (int r = 0; r < RPW; ++r)
-#pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        const int q = lane + p * kWave;
-        const uint32_t off = q < P ? (uint32_t)(r * 2 * srow + q) : kOutOfRange;
-        SG[r][p] = buf_load_u8(rsg, off, 0);
-        SU[r][p] = buf_load_u8(rsu, off, 0);
-      }
-  }
   const size_t xrb = (size_t)a.H * sizeof(XT);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)((size_t)a.T * xrb));
   uint4 X0[kCh][NP][XQ], X1[kCh][NP][XQ];
@@ -282,8 +231,8 @@ __global__ __launch_bounds__(kWaves * kWave) void k_gateup_gemv(GateUpArgs a, co
         float g = 0.f, u = 0.f;
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-          g = Wp<WK>::dot(G[r][p], X[i][p], g, WK == W_MXFP4 ? SG[r][p] : 0u);
-          u = Wp<WK>::dot(U[r][p], X[i][p], u, WK == W_MXFP4 ? SU[r][p] : 0u);
+          g = Wp<WK>::dot(G[r][p], X[i][p], g, 0u);
+          u = Wp<WK>::dot(U[r][p], X[i][p], u, 0u);
         }
         ag[r][i] = g;
         au[r][i] = u;
@@ -327,13 +276,12 @@ __global__ __launch_bounds__(kWaves * kWave) void k_gateup_gemv(GateUpArgs a, co
 struct DownArgs {
   const void* h;
   const void* down_w;       // [E][H][F]
-  const uint8_t* scales;    // MXFP4 [E][H][F/32]
   const void* down_b;       // [E][H] or null
   const void* sh_down_w;    // [H][Fs]
   const int32_t* offsets;
   const int32_t* sorted_assign;
   float* y;                 // [T*k (+T)][H], row = assignment id
-  int32_t T, k, H, E, F, Fs, shared, seg_mode;
+  int32_t T, k, H, E, F, Fs, shared;
 };
 
 // y[a][o] = down row o . h[p] (+ bias) for every sorted position p of the
@@ -341,12 +289,11 @@ struct DownArgs {
 // groups of kWaves * RPW output rows).
 template <typename XT, int WK, int NP>
 __global__ __launch_bounds__(kWaves * kWave) void k_down_gemv(DownArgs a, const int32_t* __restrict__ sorted) {
-  constexpr int RPW = rows_per_wave(WK, NP);
+  constexpr int RPW = rows_per_wave(NP);
   constexpr int XQ = Wp<WK>::kXq;
-  constexpr int kCh = chunk_tokens(WK);
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const Seg sg = block_segment(a.offsets, a.E, a.shared, a.seg_mode);
+  const Seg sg = block_segment(a.offsets, a.E + a.shared);
   if (sg.e < 0) return;
   const bool sh = sg.e == a.E;
   const int Fe = sh ? a.Fs : a.F;
@@ -374,7 +321,6 @@ __global__ __launch_bounds__(kWaves * kWave) void k_down_gemv(DownArgs a, const 
           rbias, (int)(sizeof(XT) == 4 ? r * 4 : ((o0 & 1) + r) / 2 * 4), 0, 0);
   }
   uint4 W[RPW][NP];
-  uint32_t S[RPW][NP];
 #pragma unroll
   for (int r = 0; r < RPW; ++r)
 #pragma unroll
@@ -382,17 +328,6 @@ __global__ __launch_bounds__(kWaves * kWave) void k_down_gemv(DownArgs a, const 
       const int q = lane + p * kWave;
       W[r][p] = buf_load16(rw, q < P ? (uint32_t)(r * rb + q * 16) : kOutOfRange, 0);
     }
-  if (WK == W_MXFP4) {
-    const size_t srow = (size_t)a.F / 32;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + (e * a.H + o0) * srow, (uint32_t)(nr * srow));
-#pragma unroll
-    for (int r = 0; r < RPW; ++r)
-#pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        const int q = lane + p * kWave;
-        S[r][p] = buf_load_u8(rs, q < P ? (uint32_t)(r * srow + q) : kOutOfRange, 0);
-      }
-  }
   const size_t hrb = (size_t)Fe * sizeof(XT);
   const XT* hseg = sh ? (const XT*)a.h + (size_t)nas * a.F + (size_t)(sg.p0 - nas) * a.Fs
                       : (const XT*)a.h + (size_t)sg.p0 * a.F;
@@ -411,7 +346,7 @@ __global__ __launch_bounds__(kWaves * kWave) void k_down_gemv(DownArgs a, const 
       for (int i = 0; i < kCh; ++i) {
         float v = 0.f;
 #pragma unroll
-        for (int p = 0; p < NP; ++p) v = Wp<WK>::dot(W[r][p], X[i][p], v, WK == W_MXFP4 ? S[r][p] : 0u);
+        for (int p = 0; p < NP; ++p) v = Wp<WK>::dot(W[r][p], X[i][p], v, 0u);
         acc[r][i] = v;
       }
 #pragma unroll
@@ -488,6 +423,11 @@ hipError_t launch_gateup_mfma(const moe_config* c, const moe_weights* w, const v
 hipError_t launch_down_mfma(const moe_config* c, const moe_weights* w, const void* h, const int32_t* offsets,
                             const int32_t* sorted_assign, int32_t T, float* y, hipStream_t s);
 bool mfma_shapes_ok(const moe_config* c);
+// Defined in ffn_gemv_mx.hip (MXFP4 experts).
+hipError_t launch_expert_ffn_mx(const moe_config* c, const moe_weights* w, const void* x, const int32_t* offsets,
+                                const int32_t* sorted_assign, int32_t T, void* h, hipStream_t s);
+hipError_t launch_down_mx(const moe_config* c, const moe_weights* w, const void* h, const int32_t* offsets,
+                          const int32_t* sorted_assign, int32_t T, float* y, hipStream_t s);
 
 static int max_routed_segments(const moe_config* c, int32_t T) {
   const int64_t nk = (int64_t)T * c->top_k;
@@ -519,35 +459,26 @@ template <typename XT, int WK, int NP> static void down_launch(dim3 g, const Dow
     default: FN<XT, WK, 8>(grid, args, s); break;    \
   }
 
-// One gate/up launch over the segments seg_mode selects, with routed-weight
-// kind wdt.
+// One gate/up launch over every segment slot.
 static void gateup_dispatch(const moe_config* c, const GateUpArgs& a, int wdt, int nslots, int fe, hipStream_t s) {
   const int np = pieces_per_lane(row_bytes_of(wdt, c->hidden));
-  const int rpw = gateup_rows_per_wave(wdt == MOE_DTYPE_F32 ? W_F32 : wdt == MOE_DTYPE_BF16 ? W_BF16 : W_MXFP4, np);
+  const int rpw = gateup_rows_per_wave(np);
   const dim3 grid(nslots, (fe + kWaves * rpw - 1) / (kWaves * rpw));
   if (c->x_dtype == MOE_DTYPE_F32) {
     MOE_NP_SWITCH(gateup_launch, float, W_F32, np, grid, a, s)
-  } else if (wdt == MOE_DTYPE_BF16) {
-    MOE_NP_SWITCH(gateup_launch, uint16_t, W_BF16, np, grid, a, s)
-  } else if (np <= 1) {
-    gateup_launch<uint16_t, W_MXFP4, 1>(grid, a, s);
   } else {
-    gateup_launch<uint16_t, W_MXFP4, 2>(grid, a, s);
+    MOE_NP_SWITCH(gateup_launch, uint16_t, W_BF16, np, grid, a, s)
   }
 }
 
 static void down_dispatch(const moe_config* c, const DownArgs& a, int wdt, int nslots, int cols, hipStream_t s) {
   const int np = pieces_per_lane(row_bytes_of(wdt, cols));
-  const int rpw = rows_per_wave(wdt == MOE_DTYPE_F32 ? W_F32 : wdt == MOE_DTYPE_BF16 ? W_BF16 : W_MXFP4, np);
+  const int rpw = rows_per_wave(np);
   const dim3 grid(nslots, (c->hidden + kWaves * rpw - 1) / (kWaves * rpw));
   if (c->x_dtype == MOE_DTYPE_F32) {
     MOE_NP_SWITCH(down_launch, float, W_F32, np, grid, a, s)
-  } else if (wdt == MOE_DTYPE_BF16) {
-    MOE_NP_SWITCH(down_launch, uint16_t, W_BF16, np, grid, a, s)
-  } else if (np <= 1) {
-    down_launch<uint16_t, W_MXFP4, 1>(grid, a, s);
   } else {
-    down_launch<uint16_t, W_MXFP4, 2>(grid, a, s);
+    MOE_NP_SWITCH(down_launch, uint16_t, W_BF16, np, grid, a, s)
   }
 }
 #undef MOE_NP_SWITCH
@@ -556,12 +487,12 @@ hipError_t launch_expert_ffn(const moe_config* c, const moe_weights* w, const vo
                              const int32_t* sorted_assign, int32_t T, void* h, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (T > kGemvMaxT && mfma_shapes_ok(c)) return launch_gateup_mfma(c, w, x, offsets, sorted_assign, T, h, s);
+  if (c->w_dtype == MOE_DTYPE_MXFP4) return launch_expert_ffn_mx(c, w, x, offsets, sorted_assign, T, h, s);
   GateUpArgs a;
   const bool oai = c->act == MOE_ACT_SWIGLU_OAI;
   a.x = x;
   a.gate_w = oai ? w->gate_up_w : w->gate_w;
   a.up_w = w->up_w;
-  a.scales = w->gate_up_scales;
   a.gate_up_b = w->gate_up_b;
   a.sh_gate_w = w->sh_gate_w;
   a.sh_up_w = w->sh_up_w;
@@ -570,19 +501,8 @@ hipError_t launch_expert_ffn(const moe_config* c, const moe_weights* w, const vo
   a.h = h;
   a.T = T; a.k = c->top_k; a.H = c->hidden; a.E = c->n_expert; a.F = c->expert_ff; a.Fs = c->shared_ff;
   a.shared = c->shared_ff > 0; a.oai = oai; a.alpha = c->act_alpha; a.limit = c->act_limit;
-  const int routed = max_routed_segments(c, T);
-  if (c->w_dtype != MOE_DTYPE_MXFP4 || !a.shared) {
-    // routed and shared segments share one launch (same weight element kind)
-    a.seg_mode = 0;
-    const int fmax = c->expert_ff > c->shared_ff ? c->expert_ff : c->shared_ff;
-    gateup_dispatch(c, a, c->w_dtype, routed + a.shared, fmax, s);
-  } else {
-    // MXFP4 routed experts, bf16 shared expert: one launch each
-    a.seg_mode = 1;
-    gateup_dispatch(c, a, MOE_DTYPE_MXFP4, routed, c->expert_ff, s);
-    a.seg_mode = 2;
-    gateup_dispatch(c, a, MOE_DTYPE_BF16, 1, c->shared_ff, s);
-  }
+  const int fmax = c->expert_ff > c->shared_ff ? c->expert_ff : c->shared_ff;
+  gateup_dispatch(c, a, c->w_dtype, max_routed_segments(c, T) + a.shared, fmax, s);
   return hipGetLastError();
 }
 
@@ -590,10 +510,10 @@ hipError_t launch_down(const moe_config* c, const moe_weights* w, const void* h,
                        const int32_t* sorted_assign, int32_t T, float* y, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (T > kGemvMaxT && mfma_shapes_ok(c)) return launch_down_mfma(c, w, h, offsets, sorted_assign, T, y, s);
+  if (c->w_dtype == MOE_DTYPE_MXFP4) return launch_down_mx(c, w, h, offsets, sorted_assign, T, y, s);
   DownArgs a;
   a.h = h;
   a.down_w = w->down_w;
-  a.scales = w->down_scales;
   a.down_b = c->act == MOE_ACT_SWIGLU_OAI ? w->down_b : nullptr;
   a.sh_down_w = w->sh_down_w;
   a.offsets = offsets;
@@ -601,19 +521,9 @@ hipError_t launch_down(const moe_config* c, const moe_weights* w, const void* h,
   a.y = y;
   a.T = T; a.k = c->top_k; a.H = c->hidden; a.E = c->n_expert; a.F = c->expert_ff; a.Fs = c->shared_ff;
   a.shared = c->shared_ff > 0;
-  const int routed = max_routed_segments(c, T);
-  if (c->w_dtype != MOE_DTYPE_MXFP4 || !a.shared) {
-    a.seg_mode = 0;
-    // one piece count for both: the wider of the routed and shared rows
-    const int cols = row_bytes_of(c->w_dtype, c->expert_ff) >= row_bytes_of(c->w_dtype, c->shared_ff)
-                         ? c->expert_ff : c->shared_ff;
-    down_dispatch(c, a, c->w_dtype, routed + a.shared, cols, s);
-  } else {
-    a.seg_mode = 1;
-    down_dispatch(c, a, MOE_DTYPE_MXFP4, routed, c->expert_ff, s);
-    a.seg_mode = 2;
-    down_dispatch(c, a, MOE_DTYPE_BF16, 1, c->shared_ff, s);
-  }
+  // one piece count for both: the wider of the routed and shared rows
+  const int cols = c->expert_ff >= c->shared_ff ? c->expert_ff : c->shared_ff;
+  down_dispatch(c, a, c->w_dtype, max_routed_segments(c, T) + a.shared, cols, s);
   return hipGetLastError();
 }
 
