@@ -161,7 +161,7 @@ int moe_combine(const moe_config* cfg, const moe_weights* w, const void* h, cons
   if (!h || !offsets || !sorted_assign || !topk_w || !out || !aligned16(h) || !aligned16(out)) return MOE_EINVAL;
   if (p.shared && !sgate) return MOE_EINVAL;
   if (!ws || ws_bytes < p.y_bytes || ((uintptr_t)ws & 255u)) return MOE_EWORKSPACE;
-  float* y = (float*)ws;
+  void* y = ws;
   hipError_t e = launch_down(cfg, w, h, offsets, sorted_assign, T, y, stream);
   if (e != hipSuccess) return MOE_EHIP;
   return hip_status(launch_combine_gather(cfg, y, topk_w, sgate, T, out, stream));
@@ -188,7 +188,7 @@ int moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, int3
   int32_t* pos = (int32_t*)(b + p.off_pos);
   int32_t* perm = (int32_t*)(b + p.off_perm);
   void* h = b + p.off_h;
-  float* y = (float*)(b + p.off_y);
+  void* y = b + p.off_y;
   hipError_t e;
   if ((e = launch_router_logits(cfg, w, x, T, lg, sg, stream)) != hipSuccess) return MOE_EHIP;
   if (can_fuse_gate_permute(T)) {

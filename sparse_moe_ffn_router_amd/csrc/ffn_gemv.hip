@@ -375,14 +375,24 @@ __global__ __launch_bounds__(kWaves * kWave) void k_down_gemv(DownArgs a, const 
 }
 
 // out[t][o] = sum_j w[t][j] y[t*k + j][o] (+ sgate[t] y[T*k + t][o]), the
-// picks summed in pick order.  The y rows of up to 8 picks are loaded
-// together before the sums, so the loads overlap.
-__global__ __launch_bounds__(256) void k_combine_gather(const float* __restrict__ y, const float* __restrict__ topk_w,
+// picks summed in pick order, in fp32 (y fp32 or bf16).  The y rows of up to
+// 8 picks are loaded together before the sums, so the loads overlap.
+template <typename YT> __device__ __forceinline__ float4 load_y4(const YT* y, size_t row, int o4, int H);
+template <> __device__ __forceinline__ float4 load_y4<float>(const float* y, size_t row, int o4, int H) {
+  return reinterpret_cast<const float4*>(y + row * H)[o4];
+}
+template <> __device__ __forceinline__ float4 load_y4<uint16_t>(const uint16_t* y, size_t row, int o4, int H) {
+  const uint2 v = reinterpret_cast<const uint2*>(y + row * H)[o4];
+  return make_float4(bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y));
+}
+
+template <typename YT>
+__global__ __launch_bounds__(256) void k_combine_gather(const YT* __restrict__ y, const float* __restrict__ topk_w,
                                                         const float* __restrict__ sgate, int32_t T, int32_t k,
                                                         int32_t H, float* __restrict__ out) {
   constexpr int kBatch = 8;
   const int t = blockIdx.y;
-  const int o4 = blockIdx.x * 256 + threadIdx.x;  // float4 index
+  const int o4 = blockIdx.x * 256 + threadIdx.x;  // index of 4 outputs
   if (o4 * 4 >= H) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j0 = 0; j0 < k; j0 += kBatch) {
@@ -392,7 +402,7 @@ __global__ __launch_bounds__(256) void k_combine_gather(const float* __restrict_
     for (int j = 0; j < kBatch; ++j) {
       const bool ok = j0 + j < k;
       wj[j] = ok ? topk_w[(size_t)t * k + j0 + j] : 0.f;
-      v[j] = ok ? reinterpret_cast<const float4*>(y + ((size_t)t * k + j0 + j) * H)[o4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[j] = ok ? load_y4<YT>(y, (size_t)t * k + j0 + j, o4, H) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
@@ -406,7 +416,7 @@ __global__ __launch_bounds__(256) void k_combine_gather(const float* __restrict_
   }
   if (sgate) {
     const float g = sgate[t];
-    const float4 v = reinterpret_cast<const float4*>(y + ((size_t)T * k + t) * H)[o4];
+    const float4 v = load_y4<YT>(y, (size_t)T * k + t, o4, H);
     acc.x = fmaf(g, v.x, acc.x);
     acc.y = fmaf(g, v.y, acc.y);
     acc.z = fmaf(g, v.z, acc.z);
@@ -421,7 +431,7 @@ __global__ __launch_bounds__(256) void k_combine_gather(const float* __restrict_
 hipError_t launch_gateup_mfma(const moe_config* c, const moe_weights* w, const void* x, const int32_t* offsets,
                               const int32_t* sorted_assign, int32_t T, void* h, hipStream_t s);
 hipError_t launch_down_mfma(const moe_config* c, const moe_weights* w, const void* h, const int32_t* offsets,
-                            const int32_t* sorted_assign, int32_t T, float* y, hipStream_t s);
+                            const int32_t* sorted_assign, int32_t T, uint16_t* y, hipStream_t s);
 bool mfma_shapes_ok(const moe_config* c);
 // Defined in ffn_gemv_mx.hip (MXFP4 experts).
 hipError_t launch_expert_ffn_mx(const moe_config* c, const moe_weights* w, const void* x, const int32_t* offsets,
@@ -506,10 +516,13 @@ hipError_t launch_expert_ffn(const moe_config* c, const moe_weights* w, const vo
   return hipGetLastError();
 }
 
+bool y_is_bf16(const moe_config* c, int32_t T) { return T > kGemvMaxT && mfma_shapes_ok(c); }
+
 hipError_t launch_down(const moe_config* c, const moe_weights* w, const void* h, const int32_t* offsets,
-                       const int32_t* sorted_assign, int32_t T, float* y, hipStream_t s) {
+                       const int32_t* sorted_assign, int32_t T, void* yv, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (T > kGemvMaxT && mfma_shapes_ok(c)) return launch_down_mfma(c, w, h, offsets, sorted_assign, T, y, s);
+  if (y_is_bf16(c, T)) return launch_down_mfma(c, w, h, offsets, sorted_assign, T, (uint16_t*)yv, s);
+  float* y = (float*)yv;
   if (c->w_dtype == MOE_DTYPE_MXFP4) return launch_down_mx(c, w, h, offsets, sorted_assign, T, y, s);
   DownArgs a;
   a.h = h;
@@ -527,12 +540,15 @@ hipError_t launch_down(const moe_config* c, const moe_weights* w, const void* h,
   return hipGetLastError();
 }
 
-hipError_t launch_combine_gather(const moe_config* c, const float* y, const float* topk_w, const float* sgate,
+hipError_t launch_combine_gather(const moe_config* c, const void* y, const float* topk_w, const float* sgate,
                                  int32_t T, float* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
   dim3 grid((c->hidden / 4 + 255) / 256, T);
-  k_combine_gather<<<grid, 256, 0, s>>>(y, topk_w, c->shared_ff > 0 ? sgate : nullptr, T, c->top_k, c->hidden,
-                                         out);
+  const float* sg = c->shared_ff > 0 ? sgate : nullptr;
+  if (y_is_bf16(c, T))
+    k_combine_gather<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)y, topk_w, sg, T, c->top_k, c->hidden, out);
+  else
+    k_combine_gather<float><<<grid, 256, 0, s>>>((const float*)y, topk_w, sg, T, c->top_k, c->hidden, out);
   return hipGetLastError();
 }
 

@@ -16,8 +16,8 @@
 //           a lane holds gate and up of the same (row, feature) in two
 //           accumulators and the activation runs in registers; h is bf16.
 //  down:    A = h rows; the 256 weight rows are output columns; the result
-//           (+ bias) is written as fp32 at the row of the assignment id,
-//           ready for the gather-combine.
+//           (+ bias, fp32 accumulate) is written as bf16 at the row of the
+//           assignment id, ready for the gather-combine (which sums in fp32).
 //  router:  A = x rows; weight rows = router rows; fp32 logits (+ bias).
 // MXFP4 weights are decoded to bf16 while staging (one 16-byte piece is one
 // 32-element block with its E8M0 exponent).
@@ -48,7 +48,7 @@ struct GemmArgs {
   const uint16_t* sh1;       // shared up_w
   const int32_t* offsets;
   const int32_t* sorted_assign;
-  void* out;                 // h (bf16) | y (fp32) | router logits (fp32)
+  void* out;                 // h (bf16) | y (bf16) | router logits (fp32)
   int32_t T, k, H, E, F, Fs, shared, oai;
   int32_t n_tiles;           // column tiles per segment (max over segments)
   int32_t m_tiles_max;       // grid bound on row tiles
@@ -425,7 +425,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
         }
     }
   } else {
-    float* y = (float*)a.out;
+    float* lg = (float*)a.out;
+    uint16_t* y = (uint16_t*)a.out;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int o = c0 + wn * 64 + j * 32 + colin;
@@ -439,8 +440,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
           for (int q = 0; q < 16; ++q) {
             const int r = wm * 64 + i * 32 + (q / 4) * 8 + (lane >> 5) * 4 + (q & 3);
             if (r < rows) {
-              const size_t orow = MODE == MODE_ROUTER ? (size_t)(p0 + r) : (size_t)a.sorted_assign[p0 + r];
-              y[orow * ncols + o] = acc[i][j][q] + bias;
+              if (MODE == MODE_ROUTER)
+                lg[(size_t)(p0 + r) * ncols + o] = acc[i][j][q] + bias;
+              else
+                y[(size_t)a.sorted_assign[p0 + r] * ncols + o] = (uint16_t)f32_to_bf16(acc[i][j][q] + bias);
             }
           }
       }
@@ -510,7 +513,7 @@ hipError_t launch_gateup_mfma(const moe_config* c, const moe_weights* w, const v
 }
 
 hipError_t launch_down_mfma(const moe_config* c, const moe_weights* w, const void* h, const int32_t* offsets,
-                            const int32_t* sorted_assign, int32_t T, float* y, hipStream_t s) {
+                            const int32_t* sorted_assign, int32_t T, uint16_t* y, hipStream_t s) {
   GemmArgs a = {};
   a.a_src = (const uint16_t*)h;
   a.w0 = w->down_w;

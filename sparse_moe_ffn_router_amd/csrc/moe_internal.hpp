@@ -185,10 +185,12 @@ hipError_t launch_gate_permute(const moe_config* c, const float* logits, const f
                                int32_t* sorted_assign, int32_t* assign_pos, hipStream_t s);
 hipError_t launch_expert_ffn(const moe_config* c, const moe_weights* w, const void* x, const int32_t* offsets,
                              const int32_t* sorted_assign, int32_t T, void* h, hipStream_t s);
+// y rows are indexed by assignment id a (routed a = t*k + j, shared a = T*k + t);
+// y is bf16 when the MFMA grouped GEMM computes it (y_is_bf16), fp32 otherwise.
+bool y_is_bf16(const moe_config* c, int32_t T);
 hipError_t launch_down(const moe_config* c, const moe_weights* w, const void* h, const int32_t* offsets,
-                       const int32_t* sorted_assign, int32_t T, float* y, hipStream_t s);
-// y rows are indexed by assignment id a (routed a = t*k + j, shared a = T*k + t).
-hipError_t launch_combine_gather(const moe_config* c, const float* y, const float* topk_w, const float* sgate,
+                       const int32_t* sorted_assign, int32_t T, void* y, hipStream_t s);
+hipError_t launch_combine_gather(const moe_config* c, const void* y, const float* topk_w, const float* sgate,
                                  int32_t T, float* out, hipStream_t s);
 
 }  // namespace moe
