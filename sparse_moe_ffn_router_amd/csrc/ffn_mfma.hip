@@ -83,6 +83,19 @@ __device__ int tile_lookup(const int32_t* __restrict__ offsets, int nseg, int mt
   return -1;
 }
 
+// Number of BM-row tiles over all segments (wave-uniform).
+__device__ int count_row_tiles(const int32_t* __restrict__ offsets, int nseg) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int acc = 0;
+  for (int base = 0; base < nseg; base += kWave) {
+    const int e = base + lane;
+    acc += e < nseg ? (offsets[e + 1] - offsets[e] + BM - 1) / BM : 0;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+  return acc;
+}
+
 // Byte offset of 16-byte piece c (of 8) in row r of a swizzled 128-byte-row
 // tile.  Two 128-byte rows span the 64 four-byte banks, so 16 consecutive
 // rows read at one logical piece (what 16 lanes of an MFMA operand read do)
@@ -222,20 +235,30 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
 
   // XCD-aware order: the hardware deals workgroups round-robin over 8 XCDs;
   // give each XCD a contiguous run of (column tile, row tiles) so the row
-  // tiles sharing one weight tile meet in the same L2.
-  const int nblk = gridDim.x;
-  const int per_xcd = nblk / 8;
-  const int lin = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  const int nt = lin / a.m_tiles_max;
-  const int mt = lin % a.m_tiles_max;
+  // tiles sharing one weight tile meet in the same L2.  The grid is sized
+  // for the worst-case number of row tiles; the real tiles (counted from the
+  // segment offsets) are dealt evenly over the XCDs, so none of them ends
+  // up with most of the empty slots.
   const int nseg = a.E + a.shared;
-  int p0, seg, rows;
+  int p0, seg, rows, nt, mt;
   if (MODE == MODE_ROUTER) {
+    const int per_xcd = gridDim.x / 8;
+    const int lin = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    nt = lin / a.m_tiles_max;
+    mt = lin % a.m_tiles_max;
     seg = 0;
     p0 = mt * BM;
     rows = min(BM, a.T - p0);
     if (rows <= 0) return;
   } else {
+    const int total_m = __builtin_amdgcn_readfirstlane(count_row_tiles(a.offsets, nseg));
+    const int total = total_m * a.n_tiles;
+    const int per_xcd = (total + 7) / 8;
+    const int slot = blockIdx.x / 8;
+    const int lin = (blockIdx.x % 8) * per_xcd + slot;
+    if (slot >= per_xcd || lin >= total) return;
+    nt = lin / total_m;
+    mt = lin % total_m;
     seg = tile_lookup(a.offsets, nseg, mt, &p0);
     // the lookup is wave-uniform: keep it in scalar registers so buffer
     // descriptors built from it stay scalar
