@@ -55,46 +55,6 @@ struct GemmArgs {
   float alpha, limit;
 };
 
-// Row tile mt -> (segment, first sorted position); -1 if past the last tile.
-__device__ int tile_lookup(const int32_t* __restrict__ offsets, int nseg, int mt, int* row0) {
-  const int lane = threadIdx.x & (kWave - 1);
-  int acc = 0;
-  for (int base = 0; base < nseg; base += kWave) {
-    const int e = base + lane;
-    const int cnt = e < nseg ? (offsets[e + 1] - offsets[e] + BM - 1) / BM : 0;
-    int incl = cnt;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int u = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += u;
-    }
-    const int total = __shfl(incl, kWave - 1, kWave);
-    if (mt < acc + total) {
-      const bool hit = (mt >= acc + incl - cnt) && (mt < acc + incl);
-      const uint64_t m = __ballot(hit);
-      const int src = __ffsll((unsigned long long)m) - 1;
-      const int excl = __shfl(acc + incl - cnt, src, kWave);
-      const int seg = base + src;
-      *row0 = offsets[seg] + (mt - excl) * BM;
-      return seg;
-    }
-    acc += total;
-  }
-  return -1;
-}
-
-// Number of BM-row tiles over all segments (wave-uniform).
-__device__ int count_row_tiles(const int32_t* __restrict__ offsets, int nseg) {
-  const int lane = threadIdx.x & (kWave - 1);
-  int acc = 0;
-  for (int base = 0; base < nseg; base += kWave) {
-    const int e = base + lane;
-    acc += e < nseg ? (offsets[e + 1] - offsets[e] + BM - 1) / BM : 0;
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, kWave);
-  return acc;
-}
 
 // Byte offset of 16-byte piece c (of 8) in row r of a swizzled 128-byte-row
 // tile.  Two 128-byte rows span the 64 four-byte banks, so 16 consecutive
@@ -124,27 +84,36 @@ struct CodeRegs {
   uint32_t sc;
 };
 
-// Per-thread state of the K pipeline.
+// One output tile: row tile of a segment (or of the tokens, router) by a
+// column tile.
+struct Tile {
+  int seg, p0, rows, c0, Fe, ncols, K;
+  bool sh;
+};
+
+// Per-thread state of the K pipeline of one tile.
 struct Pipe {
   __amdgpu_buffer_rsrc_t ra, rw0, rw1, rsc;
   uint32_t a_off[kAChunks], b_off[kBChunks], sc_off;
+  bool a_ok[kAChunks];      // gate/up: the staged row is a row of the tile
+  int32_t* ids;             // the tile's assignment ids in LDS (gate/up, down)
   bool two_mats, mx;
-  int nk, wid, tid, arow0, brow0, brow1, khalf;
+  int nk;
 };
 
 // Issue the loads of step s into stage (la, lb) (all lanes, always: a step
 // past the end reads at an out-of-range offset, i.e. zeros, so every step
 // has the same number of outstanding loads).
-__device__ __forceinline__ void pipe_issue(const Pipe& p, int s, uint8_t* __restrict__ la, uint8_t* __restrict__ lb,
-                                           CodeRegs& cr) {
+__device__ __forceinline__ void pipe_issue(const Pipe& p, int s, int wid, uint8_t* __restrict__ la,
+                                           uint8_t* __restrict__ lb, CodeRegs& cr) {
   const uint32_t kb = s < p.nk ? (uint32_t)s * BK * 2 : kOutOfRange;  // byte offset of the step in a bf16 row
 #pragma unroll
-  for (int i = 0; i < kAChunks; ++i) dma16(p.ra, la + (i * kThreads + p.wid * kWave) * 16, p.a_off[i] + kb);
+  for (int i = 0; i < kAChunks; ++i) dma16(p.ra, la + (i * kThreads + wid * kWave) * 16, p.a_off[i] + kb);
   if (!p.mx) {
 #pragma unroll
     for (int i = 0; i < kBChunks; ++i) {
       const bool up = p.two_mats && i >= kBChunks / 2;  // pieces i >= 2 are tile rows >= 128
-      dma16(up ? p.rw1 : p.rw0, lb + (i * kThreads + p.wid * kWave) * 16, p.b_off[i] + kb);
+      dma16(up ? p.rw1 : p.rw0, lb + (i * kThreads + wid * kWave) * 16, p.b_off[i] + kb);
     }
   } else {
     cr.codes = buf_load16(p.rw0, p.b_off[0], s < p.nk ? (uint32_t)s * BK / 2 : kOutOfRange);
@@ -153,277 +122,374 @@ __device__ __forceinline__ void pipe_issue(const Pipe& p, int s, uint8_t* __rest
 }
 
 // MXFP4: decode a step's block to bf16 and write it (swizzled) to lb.
-__device__ __forceinline__ void pipe_put_codes(const Pipe& p, const CodeRegs& cr, uint8_t* __restrict__ lb) {
+__device__ __forceinline__ void pipe_put_codes(const CodeRegs& cr, uint8_t* __restrict__ lb) {
   uint4 d[4];
   mxfp4_block_to_bf16(cr.codes, cr.sc, d);
-  const int r = p.tid / 2, blk = p.tid % 2;
+  const int r = threadIdx.x / 2, blk = threadIdx.x % 2;
 #pragma unroll
   for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(lb + swz(r, blk * 4 + q)) = d[q];
 }
 
-__device__ __forceinline__ void pipe_compute(const Pipe& p, f32x16_t (&acc)[2][2], const uint8_t* __restrict__ la,
-                                             const uint8_t* __restrict__ lb) {
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int c = kk * 2 + p.khalf;  // logical 16-byte piece of the row
-    bf16x8_t fa[2], fb[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(la + swz(p.arow0 + i * 32, c));
-    fb[0] = *reinterpret_cast<const bf16x8_t*>(lb + swz(p.brow0, c));
-    fb[1] = *reinterpret_cast<const bf16x8_t*>(lb + swz(p.brow1, c));
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-  }
+// Fragment rows of this thread: A rows arow0 (+32), B rows brow0 / brow1;
+// khalf = which 8-element half of each 16-element K slice the lane holds.
+struct Frag {
+  int arow0, brow0, brow1, khalf;
+};
+
+// Operand reads from LDS go through inline asm: the compiler then does not
+// see LDS reads that might alias the buffer->LDS loads in flight (which
+// target other stages) and adds no wait for those loads; lds_wait ties the
+// fragment registers to the wait for the reads themselves, so no MFMA can
+// use them earlier.
+__device__ __forceinline__ bf16x8_t ds_read16(const uint8_t* p) {
+  bf16x8_t r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"((uint32_t)(uintptr_t)p) : "memory");
+  return r;
+}
+// 4-byte LDS read through inline asm, completed by the s_waitcnt inside.
+__device__ __forceinline__ int32_t ds_read4_sync(const int32_t* p) {
+  int32_t r;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"((uint32_t)(uintptr_t)p) : "memory");
+  return r;
 }
 
-// The K loop over a ring of three LDS stages; the six stage buffers are
-// distinct restrict pointers so the loads landing in one stage are known
-// not to alias the reads of another.  Step s lives in stage s % 3 and its
-// loads are issued during step s - 2.  Per step: wait for this thread's
-// loads of step kt, barrier (all threads' loads landed; everyone finished
-// step kt - 1, whose stage the next loads reuse), issue step kt + 2,
-// compute step kt.
-__device__ __forceinline__ void mainloop(const Pipe& p, f32x16_t (&acc)[2][2], uint8_t* __restrict__ a0,
-                                         uint8_t* __restrict__ a1, uint8_t* __restrict__ a2,
-                                         uint8_t* __restrict__ b0, uint8_t* __restrict__ b1,
-                                         uint8_t* __restrict__ b2) {
+struct KFrag {
+  bf16x8_t a[2], b[2];
+};
+__device__ __forceinline__ void read_kfrag(const Frag& f, int kk, const uint8_t* la, const uint8_t* lb, KFrag& o) {
+  const int c = kk * 2 + f.khalf;  // logical 16-byte piece of the row
+  o.a[0] = ds_read16(la + swz(f.arow0, c));
+  o.a[1] = ds_read16(la + swz(f.arow0 + 32, c));
+  o.b[0] = ds_read16(lb + swz(f.brow0, c));
+  o.b[1] = ds_read16(lb + swz(f.brow1, c));
+}
+template <int N> __device__ __forceinline__ void lds_wait(KFrag& o) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(o.a[0]), "+v"(o.a[1]), "+v"(o.b[0]), "+v"(o.b[1]) : "n"(N));
+}
+__device__ __forceinline__ void mfma4(f32x16_t (&acc)[2][2], const KFrag& o) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-  // step s's MXFP4 block sits in code registers cr[s % 3] until converted
-  CodeRegs cr0 = {}, cr1 = {}, cr2 = {};
-  pipe_issue(p, 0, a0, b0, cr0);
-  pipe_issue(p, 1, a1, b1, cr1);
-  if (p.mx) {
-    wait_vm<2>();  // step 0's block (step 1's code and scale loads may remain)
-    pipe_put_codes(p, cr0, b0);
-  }
-  // loads per thread per step: 6 (bf16) or 4 (MXFP4: 2 DMA + codes + scale)
-#define MOE_STEP(KT, LA, LB, LA2, LB2, LB1, CRN, CRP) \
-  {                                                   \
-    if (p.mx)                                         \
-      wait_vm<4>();                                   \
-    else                                              \
-      wait_vm<6>();                                   \
-    lds_barrier();                                    \
-    pipe_issue(p, (KT) + 2, LA2, LB2, CRN);           \
-    pipe_compute(p, acc, LA, LB);                     \
-    if (p.mx) {                                       \
-      wait_vm<4>();                                   \
-      pipe_put_codes(p, CRP, LB1);                    \
-    }                                                 \
-  }
-  for (int kt = 0; kt < p.nk; kt += 3) {
-    MOE_STEP(kt, a0, b0, a2, b2, b1, cr2, cr1)
-    if (kt + 1 < p.nk) MOE_STEP(kt + 1, a1, b1, a0, b0, b2, cr0, cr2)
-    if (kt + 2 < p.nk) MOE_STEP(kt + 2, a2, b2, a1, b1, b0, cr1, cr0)
-  }
-#undef MOE_STEP
-  wait_vm<0>();
+    for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.a[i], o.b[j], acc[i][j], 0, 0, 0);
 }
 
-template <int MODE, bool MX>
-__global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_a0[BM * 128], lds_a1[BM * 128], lds_a2[BM * 128];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_b0[BN * 128], lds_b1[BN * 128], lds_b2[BN * 128];
+// One K step: four 16-deep sub-steps, the operand reads of sub-step kk + 1
+// in flight during the MFMAs of kk.
+__device__ __forceinline__ void pipe_compute(const Frag& f, f32x16_t (&acc)[2][2], const uint8_t* la,
+                                             const uint8_t* lb) {
+  KFrag k0, k1, k2, k3;
+  read_kfrag(f, 0, la, lb, k0);
+  read_kfrag(f, 1, la, lb, k1);
+  lds_wait<4>(k0);
+  read_kfrag(f, 2, la, lb, k2);
+  mfma4(acc, k0);
+  lds_wait<4>(k1);
+  read_kfrag(f, 3, la, lb, k3);
+  mfma4(acc, k1);
+  lds_wait<4>(k2);
+  mfma4(acc, k2);
+  lds_wait<0>(k3);
+  mfma4(acc, k3);
+}
 
-  // XCD-aware order: the hardware deals workgroups round-robin over 8 XCDs;
-  // give each XCD a contiguous run of (column tile, row tiles) so the row
-  // tiles sharing one weight tile meet in the same L2.  The grid is sized
-  // for the worst-case number of row tiles; the real tiles (counted from the
-  // segment offsets) are dealt evenly over the XCDs, so none of them ends
-  // up with most of the empty slots.
-  const int nseg = a.E + a.shared;
-  int p0, seg, rows, nt, mt;
-  if (MODE == MODE_ROUTER) {
-    const int per_xcd = gridDim.x / 8;
-    const int lin = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    nt = lin / a.m_tiles_max;
-    mt = lin % a.m_tiles_max;
-    seg = 0;
-    p0 = mt * BM;
-    rows = min(BM, a.T - p0);
-    if (rows <= 0) return;
-  } else {
-    const int total_m = __builtin_amdgcn_readfirstlane(count_row_tiles(a.offsets, nseg));
-    const int total = total_m * a.n_tiles;
-    const int per_xcd = (total + 7) / 8;
-    const int slot = blockIdx.x / 8;
-    const int lin = (blockIdx.x % 8) * per_xcd + slot;
-    if (slot >= per_xcd || lin >= total) return;
-    nt = lin / total_m;
-    mt = lin % total_m;
-    seg = tile_lookup(a.offsets, nseg, mt, &p0);
-    // the lookup is wave-uniform: keep it in scalar registers so buffer
-    // descriptors built from it stay scalar
-    seg = __builtin_amdgcn_readfirstlane(seg);
-    p0 = __builtin_amdgcn_readfirstlane(p0);
-    if (seg < 0) return;
-    rows = min(BM, __builtin_amdgcn_readfirstlane(a.offsets[seg + 1]) - p0);
+// Segment tables in LDS: offsets[0..nseg] and the exclusive prefix of the
+// BM-row tiles per segment (tpre[nseg] = all row tiles).
+struct SegTables {
+  int off[kMaxExperts + 2];
+  int tpre[kMaxExperts + 2];
+  int wsum[kThreads / kWave];
+};
+
+__device__ __forceinline__ int row_tiles(int n) { return (n + BM - 1) / BM; }
+
+// Fill the tables from the offsets in HBM; returns the number of row tiles.
+__device__ int build_tables(const int32_t* __restrict__ offsets, int nseg, SegTables& t) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  for (int e = tid; e <= nseg; e += kThreads) t.off[e] = offsets[e];
+  __syncthreads();
+  const int per = (nseg + kThreads - 1) / kThreads;  // consecutive segments per thread
+  int loc = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = tid * per + i;
+    if (e < nseg) loc += row_tiles(t.off[e + 1] - t.off[e]);
   }
-  const bool sh = MODE != MODE_ROUTER && seg == a.E;
-  const int64_t nas = (int64_t)a.T * a.k;
-  const int Fe = sh ? a.Fs : a.F;
-  const int ncols = MODE == MODE_GATEUP ? Fe : MODE == MODE_DOWN ? a.H : a.E;
+  int incl = loc;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int u = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += u;
+  }
+  if (lane == kWave - 1) t.wsum[wid] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / kWave; ++w) {
+    const int s = t.wsum[w];
+    before += w < wid ? s : 0;
+    all += s;
+  }
+  int run = before + incl - loc;
+  for (int i = 0; i < per; ++i) {
+    const int e = tid * per + i;
+    if (e < nseg) {
+      t.tpre[e] = run;
+      run += row_tiles(t.off[e + 1] - t.off[e]);
+    }
+  }
+  if (tid == 0) t.tpre[nseg] = all;
+  __syncthreads();
+  return all;
+}
+
+// Segment holding row tile mt (wave-uniform), from the LDS tables.
+__device__ int find_segment(const SegTables& t, int nseg, int mt) {
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int base = 0; base < nseg; base += kWave) {
+    const int e = base + lane;
+    const bool hit = e < nseg && t.tpre[e] <= mt && mt < t.tpre[e + 1];
+    const uint64_t m = __ballot(hit);
+    if (m) return base + __ffsll((unsigned long long)m) - 1;
+  }
+  return -1;
+}
+
+// Tile lin of the (column tile, row tile) space; false if its column tile
+// lies past the segment's columns (shared expert narrower than the routed).
+template <int MODE>
+__device__ bool tile_at(const GemmArgs& a, const SegTables& st, int lin, int total_m, Tile& t) {
+  const int nt = lin / total_m, mt = lin % total_m;
+  const int nseg = a.E + a.shared;
+  if (MODE == MODE_ROUTER) {
+    t.seg = 0;
+    t.p0 = mt * BM;
+    t.rows = min(BM, a.T - t.p0);
+  } else {
+    const int seg = __builtin_amdgcn_readfirstlane(find_segment(st, nseg, mt));
+    t.seg = seg;
+    t.p0 = __builtin_amdgcn_readfirstlane(st.off[seg] + (mt - st.tpre[seg]) * BM);
+    t.rows = min(BM, __builtin_amdgcn_readfirstlane(st.off[seg + 1]) - t.p0);
+  }
+  t.sh = MODE != MODE_ROUTER && t.seg == a.E;
+  t.Fe = t.sh ? a.Fs : a.F;
+  t.ncols = MODE == MODE_GATEUP ? t.Fe : MODE == MODE_DOWN ? a.H : a.E;
   const int col_tile = MODE == MODE_GATEUP ? BN / 2 : BN;  // features | outputs per tile
-  const int c0 = nt * col_tile;
-  if (c0 >= ncols) return;
-  const int K = MODE == MODE_DOWN ? Fe : a.H;
-  const bool mx = MX && !sh && MODE != MODE_ROUTER;
+  t.c0 = nt * col_tile;
+  t.K = MODE == MODE_DOWN ? t.Fe : a.H;
+  return t.c0 < t.ncols;
+}
 
+// Buffer descriptors and per-thread source offsets of a tile.  Piece
+// q = tid + i*512 of a step lands at LDS byte 16 q = row q/8, slot q%8; it
+// must hold the logical piece whose swizzled slot that is (the XOR is its
+// own inverse).  Rows past the tile's end read zeros.  Gate/up A rows are
+// gathered by token: the assignment ids are loaded here and turned into
+// offsets by finish_pipe, so the loads can be in flight meanwhile.
+template <int MODE, bool MX>
+__device__ void make_pipe(const GemmArgs& a, const Tile& t, int32_t* ids, Pipe& p) {
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int wm = wid >> 2, wn = wid & 3;
-
-  // ---- staging sources.  Piece q = tid + i*512 of a step lands at LDS
-  // byte 16 q = row q/8, slot q%8; it must hold the logical piece whose
-  // swizzled slot that is (the XOR is its own inverse).  Rows past the
-  // tile's end read zeros.
-  __amdgpu_buffer_rsrc_t ra;
-  uint32_t a_off[kAChunks];
+  const int64_t nas = (int64_t)a.T * a.k;
+  const bool mx = MX && !t.sh && MODE != MODE_ROUTER;
   {
     const uint16_t* abase;
     uint32_t abytes;
     if (MODE == MODE_DOWN) {
-      abase = sh ? a.a_src + (size_t)nas * a.F + (size_t)(p0 - nas) * a.Fs : a.a_src + (size_t)p0 * a.F;
-      abytes = (uint32_t)((size_t)rows * K * 2);
+      abase = t.sh ? a.a_src + (size_t)nas * a.F + (size_t)(t.p0 - nas) * a.Fs : a.a_src + (size_t)t.p0 * a.F;
+      abytes = (uint32_t)((size_t)t.rows * t.K * 2);
     } else {
       abase = a.a_src;
       abytes = (uint32_t)((size_t)a.T * a.H * 2);
     }
-    ra = make_rsrc(abase, abytes);
+    p.ra = make_rsrc(abase, abytes);
 #pragma unroll
     for (int i = 0; i < kAChunks; ++i) {
       const int q = tid + i * kThreads;
       const int r = q / 8;
       uint32_t off = kOutOfRange;
-      if (r < rows) {
-        if (MODE == MODE_ROUTER) {
-          off = (uint32_t)((size_t)(p0 + r) * a.H * 2);
-        } else if (MODE == MODE_GATEUP) {
-          const int asg = a.sorted_assign[p0 + r];
-          const int t = asg < nas ? asg / a.k : (int)(asg - nas);
-          off = (uint32_t)((size_t)t * a.H * 2);
-        } else {
-          off = (uint32_t)((size_t)r * K * 2);
-        }
-        off += swz_slot(r, q % 8) << 4;
+      p.a_ok[i] = r < t.rows;
+      if (MODE != MODE_GATEUP && r < t.rows) {
+        if (MODE == MODE_ROUTER)
+          off = (uint32_t)((size_t)(t.p0 + r) * a.H * 2) + (swz_slot(r, q % 8) << 4);
+        else
+          off = (uint32_t)((size_t)r * t.K * 2) + (swz_slot(r, q % 8) << 4);
       }
-      a_off[i] = off;
+      p.a_off[i] = off;
     }
+  }
+  // The assignment ids of the tile's rows (gate/up: which token each row
+  // gathers; down: which y row each row writes) go to LDS through
+  // buffer->LDS loads of waves 0 and 1.  The K loop's waits and barriers
+  // cover them before finish_pipe and the epilogue read them.
+  p.ids = ids;
+  if (MODE != MODE_ROUTER && tid < BM) {
+    const __amdgpu_buffer_rsrc_t ri = make_rsrc(a.sorted_assign + t.p0, (uint32_t)t.rows * 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ri, (lds_ptr_t)(ids + (tid & ~(kWave - 1))), 4, (int)(tid * 4), 0, 0, 0);
   }
   auto wrow = [&](int r) -> int {  // row of the segment's weight matrix for tile row r
     if (MODE == MODE_GATEUP) {
-      const int f = min(c0 + (r & (BN / 2 - 1)), Fe - 1);
-      if (a.oai && !sh) return 2 * f + (r >= BN / 2);
+      const int f = min(t.c0 + (r & (BN / 2 - 1)), t.Fe - 1);
+      if (a.oai && !t.sh) return 2 * f + (r >= BN / 2);
       return f;  // gate (r < BN/2) or up (r >= BN/2) matrix row f
     }
-    if (MODE == MODE_ROUTER) return min(c0 + r, a.E - 1);
-    return min(c0 + r, a.H - 1);
+    if (MODE == MODE_ROUTER) return min(t.c0 + r, a.E - 1);
+    return min(t.c0 + r, a.H - 1);
   };
   // weights: rw0 = the segment's first matrix (gate / fused gate_up / down /
   // router), rw1 = its up matrix (separate SwiGLU layout)
-  __amdgpu_buffer_rsrc_t rw0, rw1, rsc;
-  uint32_t b_off[kBChunks];
-  uint32_t sc_off = 0;
-  {
-    const uint8_t *w0, *w1 = nullptr;
-    size_t wbytes;
-    const size_t pack = mx ? 4 : 1;  // MXFP4 holds 4 bits per element instead of 16
-    if (MODE == MODE_ROUTER) {
-      w0 = (const uint8_t*)a.w0;
-      wbytes = (size_t)a.E * a.H * 2;
-    } else if (MODE == MODE_GATEUP) {
-      if (sh) {
-        w0 = (const uint8_t*)a.sh0;
-        w1 = (const uint8_t*)a.sh1;
-        wbytes = (size_t)a.Fs * a.H * 2;
-      } else if (a.oai) {
-        wbytes = (size_t)2 * a.F * a.H * 2 / pack;
-        w0 = (const uint8_t*)a.w0 + (size_t)seg * wbytes;
-      } else {
-        wbytes = (size_t)a.F * a.H * 2;
-        w0 = (const uint8_t*)a.w0 + (size_t)seg * wbytes;
-        w1 = (const uint8_t*)a.w1 + (size_t)seg * wbytes;
-      }
+  const uint8_t *w0, *w1 = nullptr;
+  size_t wbytes;
+  const size_t pack = mx ? 4 : 1;  // MXFP4 holds 4 bits per element instead of 16
+  if (MODE == MODE_ROUTER) {
+    w0 = (const uint8_t*)a.w0;
+    wbytes = (size_t)a.E * a.H * 2;
+  } else if (MODE == MODE_GATEUP) {
+    if (t.sh) {
+      w0 = (const uint8_t*)a.sh0;
+      w1 = (const uint8_t*)a.sh1;
+      wbytes = (size_t)a.Fs * a.H * 2;
+    } else if (a.oai) {
+      wbytes = (size_t)2 * a.F * a.H * 2 / pack;
+      w0 = (const uint8_t*)a.w0 + (size_t)t.seg * wbytes;
     } else {
-      if (sh) {
-        w0 = (const uint8_t*)a.sh0;
-        wbytes = (size_t)a.H * a.Fs * 2;
-      } else {
-        wbytes = (size_t)a.H * a.F * 2 / pack;
-        w0 = (const uint8_t*)a.w0 + (size_t)seg * wbytes;
-      }
+      wbytes = (size_t)a.F * a.H * 2;
+      w0 = (const uint8_t*)a.w0 + (size_t)t.seg * wbytes;
+      w1 = (const uint8_t*)a.w1 + (size_t)t.seg * wbytes;
     }
-    rw0 = make_rsrc(w0, (uint32_t)wbytes);
-    rw1 = make_rsrc(w1 ? w1 : w0, (uint32_t)wbytes);
-    rsc = rw0;
-    if (!mx) {
+  } else {
+    if (t.sh) {
+      w0 = (const uint8_t*)a.sh0;
+      wbytes = (size_t)a.H * a.Fs * 2;
+    } else {
+      wbytes = (size_t)a.H * a.F * 2 / pack;
+      w0 = (const uint8_t*)a.w0 + (size_t)t.seg * wbytes;
+    }
+  }
+  p.rw0 = make_rsrc(w0, (uint32_t)wbytes);
+  p.rw1 = make_rsrc(w1 ? w1 : w0, (uint32_t)wbytes);
+  p.rsc = p.rw0;
+  p.sc_off = 0;
+  if (!mx) {
 #pragma unroll
-      for (int i = 0; i < kBChunks; ++i) {
-        const int q = tid + i * kThreads;
-        const int r = q / 8;
-        b_off[i] = (uint32_t)((size_t)wrow(r) * K * 2) + (swz_slot(r, q % 8) << 4);
-      }
-    } else {
-      // one 32-element block per thread per step: tile row tid/2, block tid%2
-      const size_t row = wrow(tid / 2);
-      b_off[0] = (uint32_t)(row * (K / 2)) + (tid % 2) * 16;
-      const size_t srow0 = MODE == MODE_GATEUP ? (size_t)seg * 2 * a.F : (size_t)seg * a.H;
-      const size_t nrows = MODE == MODE_GATEUP ? (size_t)2 * a.F : (size_t)a.H;
-      rsc = make_rsrc(a.scales + srow0 * (K / 32), (uint32_t)(nrows * (K / 32)));
-      sc_off = (uint32_t)(row * (K / 32)) + (tid % 2);
+    for (int i = 0; i < kBChunks; ++i) {
+      const int q = tid + i * kThreads;
+      const int r = q / 8;
+      p.b_off[i] = (uint32_t)((size_t)wrow(r) * t.K * 2) + (swz_slot(r, q % 8) << 4);
     }
+  } else {
+    // one 32-element block per thread per step: tile row tid/2, block tid%2
+    const size_t row = wrow(tid / 2);
+    p.b_off[0] = (uint32_t)(row * (t.K / 2)) + (tid % 2) * 16;
+#pragma unroll
+    for (int i = 1; i < kBChunks; ++i) p.b_off[i] = 0;
+    const size_t srow0 = MODE == MODE_GATEUP ? (size_t)t.seg * 2 * a.F : (size_t)t.seg * a.H;
+    const size_t nrows = MODE == MODE_GATEUP ? (size_t)2 * a.F : (size_t)a.H;
+    p.rsc = make_rsrc(a.scales + srow0 * (t.K / 32), (uint32_t)(nrows * (t.K / 32)));
+    p.sc_off = (uint32_t)(row * (t.K / 32)) + (tid % 2);
   }
   // SwiGLU with separate gate and up matrices: B rows >= BN/2 read the up matrix
-  const bool two_mats = MODE == MODE_GATEUP && (sh || !a.oai);
-  const int nk = K / BK;
-
-  const int arow0 = wm * 64 + (lane & 31);
-  int brow[2];
-  if (MODE == MODE_GATEUP) {
-    brow[0] = wn * 32 + (lane & 31);           // gate rows
-    brow[1] = BN / 2 + wn * 32 + (lane & 31);  // matching up rows
-  } else {
-    brow[0] = wn * 64 + (lane & 31);
-    brow[1] = wn * 64 + 32 + (lane & 31);
-  }
-  Pipe p;
-  p.ra = ra; p.rw0 = rw0; p.rw1 = rw1; p.rsc = rsc;
-#pragma unroll
-  for (int i = 0; i < kAChunks; ++i) p.a_off[i] = a_off[i];
-#pragma unroll
-  for (int i = 0; i < kBChunks; ++i) p.b_off[i] = b_off[i];
-  p.sc_off = sc_off;
-  p.two_mats = two_mats;
+  p.two_mats = MODE == MODE_GATEUP && (t.sh || !a.oai);
   p.mx = mx;
-  p.nk = nk;
-  p.wid = wid;
-  p.tid = tid;
-  p.arow0 = arow0;
-  p.brow0 = brow[0];
-  p.brow1 = brow[1];
-  p.khalf = lane >> 5;
-  f32x16_t acc[2][2];
-  mainloop(p, acc, lds_a0, lds_a1, lds_a2, lds_b0, lds_b1, lds_b2);
+  p.nk = t.K / BK;
+}
 
-  // ---- epilogue.  Lane l of a 32x32 block holds column (l & 31) and rows
-  // (q / 4) * 8 + (l / 32) * 4 + (q % 4), q = 0..15.
+// Gate/up: token row offsets from the assignment ids that make_pipe sent to
+// LDS (the caller has waited for those loads and passed a barrier).
+template <int MODE>
+__device__ __forceinline__ void finish_pipe(const GemmArgs& a, Pipe& p) {
+  if (MODE != MODE_GATEUP) return;
+  const int64_t nas = (int64_t)a.T * a.k;
+#pragma unroll
+  for (int i = 0; i < kAChunks; ++i) {
+    const int q = threadIdx.x + i * kThreads;
+    const int asg = ds_read4_sync(p.ids + q / 8);
+    if (p.a_ok[i]) {
+      const int t = asg < nas ? asg / a.k : (int)(asg - nas);
+      p.a_off[i] = (uint32_t)((size_t)t * a.H * 2) + (swz_slot(q / 8, q % 8) << 4);
+    }
+  }
+}
+
+// A pipe with no steps: its loads all read zeros.
+__device__ __forceinline__ void null_pipe(const Pipe& like, Pipe& p) {
+  p = like;
+  p.nk = 0;
+#pragma unroll
+  for (int i = 0; i < kAChunks; ++i) {
+    p.a_ok[i] = false;
+    p.a_off[i] = kOutOfRange;
+  }
+}
+
+// The K loop of one tile over a ring of three LDS stages; the six stage
+// buffers are distinct restrict pointers so the loads landing in one stage
+// are known not to alias the reads of another.  Step s of the tile lives in
+// stage s % 3 of (a0, a1, a2) and its loads were issued during step s - 2;
+// the steps 0 and 1 were issued before the call (by the previous tile's
+// loop or the prologue), and the last two steps issue steps 0 and 1 of the
+// next tile q, so the ring runs on across tiles.  Per step: wait for this
+// thread's loads of step kt, barrier (all threads' loads landed; everyone
+// finished step kt - 1, whose stage the next loads reuse), issue step
+// kt + 2, compute step kt.
+template <int MODE>
+__device__ __forceinline__ void tile_loop(const GemmArgs& a, const Pipe& p, Pipe& q, const Frag& fr, int wid,
+                                          f32x16_t (&acc)[2][2], CodeRegs (&cr)[3], uint8_t* __restrict__ a0,
+                                          uint8_t* __restrict__ a1, uint8_t* __restrict__ a2,
+                                          uint8_t* __restrict__ b0, uint8_t* __restrict__ b1,
+                                          uint8_t* __restrict__ b2) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  // loads per thread per step: 6 (bf16) or 4 (MXFP4: 2 DMA + codes + scale).
+  // MXFP4 tiles are one per workgroup (no next tile), so the count of a
+  // step is that of the tile.
+#define MOE_STEP(KT, LA, LB, LA2, LB2, LB1, CRN, CRP)                   \
+  {                                                                     \
+    if (p.mx)                                                           \
+      wait_vm<4>();                                                     \
+    else                                                                \
+      wait_vm<6>();                                                     \
+    lds_barrier();                                                      \
+    const int s2 = (KT) + 2;                                            \
+    if (s2 < p.nk) {                                                    \
+      pipe_issue(p, s2, wid, LA2, LB2, CRN);                            \
+    } else {                                                            \
+      /* q's id loads went out before step 2's loads: with three or */  \
+      /* more steps (persistent launches) the wait and barrier above */ \
+      /* covered them; otherwise q is the empty pipe */                 \
+      if (s2 == p.nk) finish_pipe<MODE>(a, q);                          \
+      pipe_issue(q, s2 - p.nk, wid, LA2, LB2, CRN);                     \
+    }                                                                   \
+    pipe_compute(fr, acc, LA, LB);                                      \
+    if (p.mx) {                                                         \
+      wait_vm<4>();                                                     \
+      pipe_put_codes(CRP, LB1);                                         \
+    }                                                                   \
+  }
+  for (int kt = 0; kt < p.nk; kt += 3) {
+    MOE_STEP(kt, a0, b0, a2, b2, b1, cr[2], cr[1])
+    if (kt + 1 < p.nk) MOE_STEP(kt + 1, a1, b1, a0, b0, b2, cr[0], cr[2])
+    if (kt + 2 < p.nk) MOE_STEP(kt + 2, a2, b2, a1, b1, b0, cr[1], cr[0])
+  }
+#undef MOE_STEP
+}
+
+// Epilogue.  Lane l of a 32x32 block holds column (l & 31) and rows
+// (q / 4) * 8 + (l / 32) * 4 + (q % 4), q = 0..15.
+template <int MODE>
+__device__ __forceinline__ void epilogue(const GemmArgs& a, const Tile& t, const f32x16_t (&acc)[2][2], int wm,
+                                         int wn, const int32_t* ids) {
+  const int lane = threadIdx.x & (kWave - 1);
   const int colin = lane & 31;
+  const int64_t nas = (int64_t)a.T * a.k;
   if (MODE == MODE_GATEUP) {
-    const int f = c0 + wn * 32 + colin;
-    if (f < Fe) {
+    const int f = t.c0 + wn * 32 + colin;
+    if (f < t.Fe) {
       float bg = 0.f, bu = 0.f;
-      if (a.oai && !sh && a.bias) {
-        bg = __uint_as_float((uint32_t)a.bias[(size_t)seg * 2 * a.F + 2 * f] << 16);
-        bu = __uint_as_float((uint32_t)a.bias[(size_t)seg * 2 * a.F + 2 * f + 1] << 16);
+      if (a.oai && !t.sh && a.bias) {
+        bg = __uint_as_float((uint32_t)a.bias[(size_t)t.seg * 2 * a.F + 2 * f] << 16);
+        bu = __uint_as_float((uint32_t)a.bias[(size_t)t.seg * 2 * a.F + 2 * f + 1] << 16);
       }
       uint16_t* h = (uint16_t*)a.out;
 #pragma unroll
@@ -431,9 +497,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           const int r = wm * 64 + i * 32 + (q / 4) * 8 + (lane >> 5) * 4 + (q & 3);
-          if (r < rows) {
+          if (r < t.rows) {
             float hv;
-            if (a.oai && !sh) {
+            if (a.oai && !t.sh) {
               const float g = fminf(acc[i][0][q] + bg, a.limit);
               const float u = fminf(fmaxf(acc[i][1][q] + bu, -a.limit), a.limit);
               hv = (u + 1.f) * (g / (1.f + expf(-a.alpha * g)));
@@ -441,7 +507,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
               const float g = acc[i][0][q];
               hv = g / (1.f + expf(-g)) * acc[i][1][q];
             }
-            const int p = p0 + r;
+            const int p = t.p0 + r;
             const size_t rowoff = p < nas ? (size_t)p * a.F : (size_t)nas * a.F + (size_t)(p - nas) * a.Fs;
             h[rowoff + f] = (uint16_t)f32_to_bf16(hv);
           }
@@ -450,28 +516,132 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
   } else {
     float* lg = (float*)a.out;
     uint16_t* y = (uint16_t*)a.out;
+    // down: the y row of tile row wm*64 + i*32 + (q/4)*8 + h*4 + (q%4) is
+    // the assignment id that lane (row - wm*64) reads here
+    const int32_t ep_id = MODE == MODE_DOWN ? ds_read4_sync(ids + wm * 64 + lane) : 0;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int o = c0 + wn * 64 + j * 32 + colin;
-      if (o < ncols) {
+      const int o = t.c0 + wn * 64 + j * 32 + colin;
+      if (o < t.ncols) {
         float bias = 0.f;
         if (MODE == MODE_ROUTER && a.bias) bias = __uint_as_float((uint32_t)a.bias[o] << 16);
-        if (MODE == MODE_DOWN && !sh && a.bias) bias = __uint_as_float((uint32_t)a.bias[(size_t)seg * a.H + o] << 16);
+        if (MODE == MODE_DOWN && !t.sh && a.bias) bias = __uint_as_float((uint32_t)a.bias[(size_t)t.seg * a.H + o] << 16);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int q = 0; q < 16; ++q) {
             const int r = wm * 64 + i * 32 + (q / 4) * 8 + (lane >> 5) * 4 + (q & 3);
-            if (r < rows) {
+            if (r < t.rows) {
               if (MODE == MODE_ROUTER)
-                lg[(size_t)(p0 + r) * ncols + o] = acc[i][j][q] + bias;
-              else
-                y[(size_t)a.sorted_assign[p0 + r] * ncols + o] = (uint16_t)f32_to_bf16(acc[i][j][q] + bias);
+                lg[(size_t)(t.p0 + r) * t.ncols + o] = acc[i][j][q] + bias;
+              else {
+                const int src = i * 32 + (q / 4) * 8 + (q & 3);
+                const int id0 = __builtin_amdgcn_readlane(ep_id, src);
+                const int id1 = __builtin_amdgcn_readlane(ep_id, src + 4);
+                const int id = (lane >> 5) ? id1 : id0;
+                y[(size_t)id * t.ncols + o] = (uint16_t)f32_to_bf16(acc[i][j][q] + bias);
+              }
             }
           }
       }
     }
   }
+}
+
+// Next tile of this workgroup's run at or after lin (skipping column tiles
+// past a narrower segment); false when the run is done.
+template <int MODE>
+__device__ bool next_tile(const GemmArgs& a, const SegTables& st, int& lin, int lin_end, int step, int total_m,
+                          Tile& t) {
+  for (; lin < lin_end; lin += step)
+    if (tile_at<MODE>(a, st, lin, total_m, t)) return true;
+  return false;
+}
+
+template <int MODE, bool MX>
+__global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_a0[BM * 128], lds_a1[BM * 128], lds_a2[BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_b0[BN * 128], lds_b1[BN * 128], lds_b2[BN * 128];
+  __shared__ SegTables st;
+  __shared__ int32_t ids_s[3][BM];  // assignment ids of three consecutive tiles
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wid >> 2, wn = wid & 3;
+
+  // The run of tiles of this workgroup.  The hardware deals workgroups
+  // round-robin over the 8 XCDs; each XCD gets a contiguous range of the
+  // (column tile, row tile) space, column-tile-major, so the row tiles
+  // sharing one weight tile meet in the same L2, and its workgroups take
+  // the range's tiles in turn.  The range is cut from the real number of
+  // tiles (counted from the segment offsets), so the XCDs get equal shares.
+  // With one workgroup per CU a workgroup runs several tiles back to back.
+  const int total_m = MODE == MODE_ROUTER ? (a.T + BM - 1) / BM
+                                          : __builtin_amdgcn_readfirstlane(build_tables(a.offsets, a.E + a.shared, st));
+  const int total = total_m * a.n_tiles;
+  const int per_xcd = (total + 7) / 8;
+  const int nslots = gridDim.x / 8;
+  const int xcd = blockIdx.x % 8;
+  int lin = xcd * per_xcd + blockIdx.x / 8;
+  const int lin_end = min((xcd + 1) * per_xcd, total);
+  Tile tc, tn;
+  if (!next_tile<MODE>(a, st, lin, lin_end, nslots, total_m, tc)) return;
+
+  Frag fr;
+  fr.arow0 = wm * 64 + (lane & 31);
+  if (MODE == MODE_GATEUP) {
+    fr.brow0 = wn * 32 + (lane & 31);           // gate rows
+    fr.brow1 = BN / 2 + wn * 32 + (lane & 31);  // matching up rows
+  } else {
+    fr.brow0 = wn * 64 + (lane & 31);
+    fr.brow1 = wn * 64 + 32 + (lane & 31);
+  }
+  fr.khalf = lane >> 5;
+
+  Pipe pc, pn;
+  int ntile = 0;  // tiles made so far; tile n's ids live in ids_s[n % 3]
+  make_pipe<MODE, MX>(a, tc, ids_s[ntile++ % 3], pc);
+  wait_vm<0>();
+  __syncthreads();
+  finish_pipe<MODE>(a, pc);
+  // step s's MXFP4 block sits in code registers cr[s % 3] until converted
+  CodeRegs cr[3] = {};
+  pipe_issue(pc, 0, wid, lds_a0, lds_b0, cr[0]);
+  pipe_issue(pc, 1, wid, lds_a1, lds_b1, cr[1]);
+  if (MX && pc.mx) {
+    wait_vm<2>();  // step 0's block (step 1's code and scale loads may remain)
+    pipe_put_codes(cr[0], lds_b0);
+  }
+  lin += nslots;
+  bool more = next_tile<MODE>(a, st, lin, lin_end, nslots, total_m, tn);
+  if (more)
+    make_pipe<MODE, MX>(a, tn, ids_s[ntile++ % 3], pn);
+  else
+    null_pipe(pc, pn);
+
+  int phase = 0;  // stage of the current tile's step 0
+  f32x16_t acc[2][2];
+  for (;;) {
+    if (MX || phase == 0)
+      tile_loop<MODE>(a, pc, pn, fr, wid, acc, cr, lds_a0, lds_a1, lds_a2, lds_b0, lds_b1, lds_b2);
+    else if (phase == 1)
+      tile_loop<MODE>(a, pc, pn, fr, wid, acc, cr, lds_a1, lds_a2, lds_a0, lds_b1, lds_b2, lds_b0);
+    else
+      tile_loop<MODE>(a, pc, pn, fr, wid, acc, cr, lds_a2, lds_a0, lds_a1, lds_b2, lds_b0, lds_b1);
+    epilogue<MODE>(a, tc, acc, wm, wn, pc.ids);
+    if (!more) break;
+    phase = (phase + pc.nk) % 3;
+    tc = tn;
+    pc = pn;
+    lin += nslots;
+    more = next_tile<MODE>(a, st, lin, lin_end, nslots, total_m, tn);
+    if (more)
+      make_pipe<MODE, MX>(a, tn, ids_s[ntile++ % 3], pn);
+    else
+      null_pipe(pc, pn);
+  }
+  wait_vm<0>();  // the zero-reading loads of the steps past the last tile
 }
 
 int row_tiles_bound(const moe_config* c, int32_t T) {
@@ -482,14 +652,31 @@ int row_tiles_bound(const moe_config* c, int32_t T) {
   return (int)b;
 }
 
+// Workgroups of a launch: one per tile, or, when every tile has at least
+// three K steps (the ring hands steps 0 and 1 of the next tile over from the
+// previous one, and the next tile's ids must have landed two steps before
+// its end) and the weights are bf16, at most one per CU, each running its
+// share of the tiles.
+int grid_size(int64_t tiles, bool persistent) {
+  int64_t blocks = tiles;
+  if (persistent) {
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+      ncu = 256;
+    if (blocks > ncu) blocks = ncu;
+  }
+  return (int)((blocks + 7) / 8 * 8);
+}
+
 template <int MODE>
-hipError_t launch(const GemmArgs& a, bool mx, hipStream_t s) {
-  int64_t blocks = (int64_t)a.n_tiles * a.m_tiles_max;
-  blocks = (blocks + 7) / 8 * 8;
+hipError_t launch(const GemmArgs& a, bool mx, int min_k, hipStream_t s) {
+  const int64_t tiles = (int64_t)a.n_tiles * a.m_tiles_max;
+  const unsigned blocks = (unsigned)grid_size(tiles, !mx && min_k >= 3 * BK);
   if (mx)
-    k_grouped_gemm<MODE, true><<<(unsigned)blocks, kThreads, 0, s>>>(a);
+    k_grouped_gemm<MODE, true><<<blocks, kThreads, 0, s>>>(a);
   else
-    k_grouped_gemm<MODE, false><<<(unsigned)blocks, kThreads, 0, s>>>(a);
+    k_grouped_gemm<MODE, false><<<blocks, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -506,7 +693,7 @@ hipError_t launch_router_mfma(const moe_config* c, const moe_weights* w, const v
   a.T = T; a.k = c->top_k; a.H = c->hidden; a.E = c->n_expert; a.F = c->expert_ff; a.Fs = c->shared_ff;
   a.n_tiles = (c->n_expert + BN - 1) / BN;
   a.m_tiles_max = (T + BM - 1) / BM;
-  return launch<MODE_ROUTER>(a, false, s);
+  return launch<MODE_ROUTER>(a, false, c->hidden, s);
 }
 
 bool mfma_shapes_ok(const moe_config* c) {
@@ -532,7 +719,11 @@ hipError_t launch_gateup_mfma(const moe_config* c, const moe_weights* w, const v
   const int fmax = c->expert_ff > c->shared_ff ? c->expert_ff : c->shared_ff;
   a.n_tiles = (fmax + BN / 2 - 1) / (BN / 2);
   a.m_tiles_max = row_tiles_bound(c, T);
-  return launch<MODE_GATEUP>(a, c->w_dtype == MOE_DTYPE_MXFP4, s);
+#ifdef MOE_GATEUP_GRID_ALL
+  return launch<MODE_GATEUP>(a, c->w_dtype == MOE_DTYPE_MXFP4, 0, s);
+#else
+  return launch<MODE_GATEUP>(a, c->w_dtype == MOE_DTYPE_MXFP4, c->hidden, s);
+#endif
 }
 
 hipError_t launch_down_mfma(const moe_config* c, const moe_weights* w, const void* h, const int32_t* offsets,
@@ -550,7 +741,8 @@ hipError_t launch_down_mfma(const moe_config* c, const moe_weights* w, const voi
   a.shared = c->shared_ff > 0; a.oai = c->act == MOE_ACT_SWIGLU_OAI;
   a.n_tiles = (c->hidden + BN - 1) / BN;
   a.m_tiles_max = row_tiles_bound(c, T);
-  return launch<MODE_DOWN>(a, c->w_dtype == MOE_DTYPE_MXFP4, s);
+  const int min_k = c->shared_ff > 0 && c->shared_ff < c->expert_ff ? c->shared_ff : c->expert_ff;
+  return launch<MODE_DOWN>(a, c->w_dtype == MOE_DTYPE_MXFP4, min_k, s);
 }
 
 }  // namespace moe
