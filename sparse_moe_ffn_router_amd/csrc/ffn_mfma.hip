@@ -121,6 +121,28 @@ __device__ __forceinline__ void pipe_issue(const Pipe& p, int s, int wid, uint8_
   }
 }
 
+// Issue step s2 of the pair (p, q): p's step s2 while s2 < p.nk, else q's
+// step s2 - p.nk.  Every field is chosen with a select on a wave-uniform
+// condition, so a single copy of the loads is emitted.
+__device__ __forceinline__ void pipe_issue_pq(const Pipe& p, const Pipe& q, int s2, int wid, uint8_t* __restrict__ la,
+                                              uint8_t* __restrict__ lb, CodeRegs& cr) {
+  const bool uq = s2 >= p.nk;
+  Pipe x;
+  x.ra = uq ? q.ra : p.ra;
+  x.rw0 = uq ? q.rw0 : p.rw0;
+  x.rw1 = uq ? q.rw1 : p.rw1;
+  x.rsc = uq ? q.rsc : p.rsc;
+#pragma unroll
+  for (int i = 0; i < kAChunks; ++i) x.a_off[i] = uq ? q.a_off[i] : p.a_off[i];
+#pragma unroll
+  for (int i = 0; i < kBChunks; ++i) x.b_off[i] = uq ? q.b_off[i] : p.b_off[i];
+  x.sc_off = uq ? q.sc_off : p.sc_off;
+  x.two_mats = uq ? q.two_mats : p.two_mats;
+  x.mx = uq ? q.mx : p.mx;
+  x.nk = uq ? q.nk : p.nk;
+  pipe_issue(x, uq ? s2 - p.nk : s2, wid, la, lb, cr);
+}
+
 // MXFP4: decode a step's block to bf16 and write it (swizzled) to lb.
 __device__ __forceinline__ void pipe_put_codes(const CodeRegs& cr, uint8_t* __restrict__ lb) {
   uint4 d[4];
@@ -429,9 +451,10 @@ __device__ __forceinline__ void null_pipe(const Pipe& like, Pipe& p) {
 // thread's loads of step kt, barrier (all threads' loads landed; everyone
 // finished step kt - 1, whose stage the next loads reuse), issue step
 // kt + 2, compute step kt.
-template <int MODE>
+template <int MODE, bool MX>
 __device__ __forceinline__ void tile_loop(const GemmArgs& a, const Pipe& p, Pipe& q, const Frag& fr, int wid,
-                                          f32x16_t (&acc)[2][2], CodeRegs (&cr)[3], uint8_t* __restrict__ a0,
+                                          f32x16_t (&acc)[2][2], CodeRegs& c0, CodeRegs& c1, CodeRegs& c2,
+                                          uint8_t* __restrict__ a0,
                                           uint8_t* __restrict__ a1, uint8_t* __restrict__ a2,
                                           uint8_t* __restrict__ b0, uint8_t* __restrict__ b1,
                                           uint8_t* __restrict__ b2) {
@@ -441,36 +464,38 @@ __device__ __forceinline__ void tile_loop(const GemmArgs& a, const Pipe& p, Pipe
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  // loads per thread per step: 6 (bf16) or 4 (MXFP4: 2 DMA + codes + scale).
-  // MXFP4 tiles are one per workgroup (no next tile), so the count of a
-  // step is that of the tile.
+  // Loads per thread per step: 6 (bf16) or 4 (MXFP4: 2 DMA + codes + scale).
+  // A step's loads are complete once at most the next step's are in
+  // flight; kernels with MXFP4 experts wait down to 4, which also covers a
+  // bf16 step (the shared expert's) on either side.  An MXFP4 step's block
+  // is decoded into its stage during the step before it, from the codes
+  // loaded two steps before that (the next tile's first block during this
+  // tile's last step).  Steps 0 and 1 of the next tile q are issued by the
+  // last two steps; q's ids went out before this tile's step 2 loads, so
+  // with three or more steps (persistent launches) the wait and barrier of
+  // step nk - 2 covered them, and otherwise q is the empty pipe.  The issue
+  // picks p's or q's fields with selects, not branches, so the code
+  // registers are written by a single load.
 #define MOE_STEP(KT, LA, LB, LA2, LB2, LB1, CRN, CRP)                   \
   {                                                                     \
-    if (p.mx)                                                           \
+    if (MX)                                                             \
       wait_vm<4>();                                                     \
     else                                                                \
       wait_vm<6>();                                                     \
     lds_barrier();                                                      \
     const int s2 = (KT) + 2;                                            \
-    if (s2 < p.nk) {                                                    \
-      pipe_issue(p, s2, wid, LA2, LB2, CRN);                            \
-    } else {                                                            \
-      /* q's id loads went out before step 2's loads: with three or */  \
-      /* more steps (persistent launches) the wait and barrier above */ \
-      /* covered them; otherwise q is the empty pipe */                 \
-      if (s2 == p.nk) finish_pipe<MODE>(a, q);                          \
-      pipe_issue(q, s2 - p.nk, wid, LA2, LB2, CRN);                     \
-    }                                                                   \
+    if (s2 == p.nk) finish_pipe<MODE>(a, q);                            \
+    pipe_issue_pq(p, q, s2, wid, LA2, LB2, CRN);                        \
     pipe_compute(fr, acc, LA, LB);                                      \
-    if (p.mx) {                                                         \
+    if (MX && ((KT) + 1 < p.nk ? p.mx : q.mx)) {                        \
       wait_vm<4>();                                                     \
       pipe_put_codes(CRP, LB1);                                         \
     }                                                                   \
   }
   for (int kt = 0; kt < p.nk; kt += 3) {
-    MOE_STEP(kt, a0, b0, a2, b2, b1, cr[2], cr[1])
-    if (kt + 1 < p.nk) MOE_STEP(kt + 1, a1, b1, a0, b0, b2, cr[0], cr[2])
-    if (kt + 2 < p.nk) MOE_STEP(kt + 2, a2, b2, a1, b1, b0, cr[1], cr[0])
+    MOE_STEP(kt, a0, b0, a2, b2, b1, c2, c1)
+    if (kt + 1 < p.nk) MOE_STEP(kt + 1, a1, b1, a0, b0, b2, c0, c2)
+    if (kt + 2 < p.nk) MOE_STEP(kt + 2, a2, b2, a1, b1, b0, c1, c0)
   }
 #undef MOE_STEP
 }
@@ -605,7 +630,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
   wait_vm<0>();
   __syncthreads();
   finish_pipe<MODE>(a, pc);
-  // step s's MXFP4 block sits in code registers cr[s % 3] until converted
+  // step s's MXFP4 block sits in code registers cr[s % 3] (s counted over
+  // the workgroup's whole run of tiles) until converted
   CodeRegs cr[3] = {};
   pipe_issue(pc, 0, wid, lds_a0, lds_b0, cr[0]);
   pipe_issue(pc, 1, wid, lds_a1, lds_b1, cr[1]);
@@ -623,12 +649,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
   int phase = 0;  // stage of the current tile's step 0
   f32x16_t acc[2][2];
   for (;;) {
-    if (MX || phase == 0)
-      tile_loop<MODE>(a, pc, pn, fr, wid, acc, cr, lds_a0, lds_a1, lds_a2, lds_b0, lds_b1, lds_b2);
+    // stages and code registers rotate with the global step index
+    if (phase == 0)
+      tile_loop<MODE, MX>(a, pc, pn, fr, wid, acc, cr[0], cr[1], cr[2], lds_a0, lds_a1, lds_a2, lds_b0, lds_b1,
+                          lds_b2);
     else if (phase == 1)
-      tile_loop<MODE>(a, pc, pn, fr, wid, acc, cr, lds_a1, lds_a2, lds_a0, lds_b1, lds_b2, lds_b0);
+      tile_loop<MODE, MX>(a, pc, pn, fr, wid, acc, cr[1], cr[2], cr[0], lds_a1, lds_a2, lds_a0, lds_b1, lds_b2,
+                          lds_b0);
     else
-      tile_loop<MODE>(a, pc, pn, fr, wid, acc, cr, lds_a2, lds_a0, lds_a1, lds_b2, lds_b0, lds_b1);
+      tile_loop<MODE, MX>(a, pc, pn, fr, wid, acc, cr[2], cr[0], cr[1], lds_a2, lds_a0, lds_a1, lds_b2, lds_b0,
+                          lds_b1);
     epilogue<MODE>(a, tc, acc, wm, wn, pc.ids);
     if (!more) break;
     phase = (phase + pc.nk) % 3;
@@ -655,8 +685,7 @@ int row_tiles_bound(const moe_config* c, int32_t T) {
 // Workgroups of a launch: one per tile, or, when every tile has at least
 // three K steps (the ring hands steps 0 and 1 of the next tile over from the
 // previous one, and the next tile's ids must have landed two steps before
-// its end) and the weights are bf16, at most one per CU, each running its
-// share of the tiles.
+// its end), at most one per CU, each running its share of the tiles.
 int grid_size(int64_t tiles, bool persistent) {
   int64_t blocks = tiles;
   if (persistent) {
@@ -672,7 +701,7 @@ int grid_size(int64_t tiles, bool persistent) {
 template <int MODE>
 hipError_t launch(const GemmArgs& a, bool mx, int min_k, hipStream_t s) {
   const int64_t tiles = (int64_t)a.n_tiles * a.m_tiles_max;
-  const unsigned blocks = (unsigned)grid_size(tiles, !mx && min_k >= 3 * BK);
+  const unsigned blocks = (unsigned)grid_size(tiles, min_k >= 3 * BK);
   if (mx)
     k_grouped_gemm<MODE, true><<<blocks, kThreads, 0, s>>>(a);
   else
