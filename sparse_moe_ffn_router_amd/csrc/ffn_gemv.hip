@@ -392,8 +392,16 @@ __global__ __launch_bounds__(256) void k_combine_gather(const YT* __restrict__ y
                                                         int32_t H, float* __restrict__ out) {
   constexpr int kBatch = 8;
   const int t = blockIdx.y;
-  const int o4 = blockIdx.x * 256 + threadIdx.x;  // index of 4 outputs
+  const int o4 = blockIdx.x * blockDim.x + threadIdx.x;  // index of 4 outputs
   if (o4 * 4 >= H) return;
+  // the shared expert's row is loaded with the first batch of picks (one
+  // round trip for k <= 8) and added last
+  float g = 0.f;
+  float4 vs = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (sgate) {
+    g = sgate[t];
+    vs = load_y4<YT>(y, (size_t)T * k + t, o4, H);
+  }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j0 = 0; j0 < k; j0 += kBatch) {
     float4 v[kBatch];
@@ -415,12 +423,10 @@ __global__ __launch_bounds__(256) void k_combine_gather(const YT* __restrict__ y
     }
   }
   if (sgate) {
-    const float g = sgate[t];
-    const float4 v = load_y4<YT>(y, (size_t)T * k + t, o4, H);
-    acc.x = fmaf(g, v.x, acc.x);
-    acc.y = fmaf(g, v.y, acc.y);
-    acc.z = fmaf(g, v.z, acc.z);
-    acc.w = fmaf(g, v.w, acc.w);
+    acc.x = fmaf(g, vs.x, acc.x);
+    acc.y = fmaf(g, vs.y, acc.y);
+    acc.z = fmaf(g, vs.z, acc.z);
+    acc.w = fmaf(g, vs.w, acc.w);
   }
   reinterpret_cast<float4*>(out + (size_t)t * H)[o4] = acc;
 }
@@ -543,12 +549,14 @@ hipError_t launch_down(const moe_config* c, const moe_weights* w, const void* h,
 hipError_t launch_combine_gather(const moe_config* c, const void* y, const float* topk_w, const float* sgate,
                                  int32_t T, float* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  dim3 grid((c->hidden / 4 + 255) / 256, T);
+  // few tokens: 64-thread workgroups, so the loads spread over more CUs
+  const int threads = T <= kGemvMaxT ? 64 : 256;
+  dim3 grid((c->hidden / 4 + threads - 1) / threads, T);
   const float* sg = c->shared_ff > 0 ? sgate : nullptr;
   if (y_is_bf16(c, T))
-    k_combine_gather<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)y, topk_w, sg, T, c->top_k, c->hidden, out);
+    k_combine_gather<uint16_t><<<grid, threads, 0, s>>>((const uint16_t*)y, topk_w, sg, T, c->top_k, c->hidden, out);
   else
-    k_combine_gather<float><<<grid, 256, 0, s>>>((const float*)y, topk_w, sg, T, c->top_k, c->hidden, out);
+    k_combine_gather<float><<<grid, threads, 0, s>>>((const float*)y, topk_w, sg, T, c->top_k, c->hidden, out);
   return hipGetLastError();
 }
 

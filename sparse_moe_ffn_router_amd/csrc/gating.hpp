@@ -11,40 +11,77 @@
 
 namespace moe {
 
+// Wave-wide maximum / minimum of a 32-bit value, wave-uniform result.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<kDppXor1>(v));
+  v = max(v, dpp_u32<kDppXor2>(v));
+  v = max(v, dpp_u32<kDppHalfMirror>(v));
+  v = max(v, dpp_u32<kDppMirror>(v));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(a, b), max(c, d));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u32<kDppXor1>(v));
+  v = min(v, dpp_u32<kDppXor2>(v));
+  v = min(v, dpp_u32<kDppHalfMirror>(v));
+  v = min(v, dpp_u32<kDppMirror>(v));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return min(min(a, b), min(c, d));
+}
+
 // Returns, in lane j < k, the expert of pick j; writes topk_idx / topk_w of
-// the token.  The top-k runs k rounds of a wave-wide maximum of 64-bit keys
-// order_key(logit) << 32 | (2^32 - 1 - expert): the largest logit wins, and
-// among bit-equal logits the lowest expert id, as a left-to-right selection
-// sort with strict comparison keeps the first one it sees.
+// the token.  The top-k runs k rounds of: each lane's largest unpicked
+// order_key(logit) (order_key is monotone in the logit and folds -0 into
+// +0; expert e = i * 64 + lane sits in slot i of its lane, and a lane keeps
+// its lowest slot among equal keys), the wave-wide maximum of those, and,
+// among the lanes holding that maximum, the lowest expert id -- so the
+// largest logit wins and bit-equal logits go to the lowest index, as a
+// left-to-right selection sort with strict comparison keeps the first one
+// it sees.  A picked slot's key becomes 0, below every valid key.
 // NPER = experts held per lane (E <= 64 * NPER).
 template <int NPER>
 __device__ __forceinline__ int gate_token_n(const float* __restrict__ l, int E, int k, int softmax_first, int renorm,
                                             float scale, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
   const int lane = threadIdx.x & (kWave - 1);
-  uint64_t key[NPER];
+  uint32_t key[NPER];
   float val[NPER];
-  const int nper = NPER;
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
     const int e = i * kWave + lane;
-    const bool ok = i < nper && e < E;
+    const bool ok = e < E;
     val[i] = ok ? l[e] : -INFINITY;
-    key[i] = ok ? (((uint64_t)order_key(val[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e)) : 0ull;
+    key[i] = ok ? order_key(val[i]) : 0u;
   }
-  uint32_t used = 0;
   int my_idx = 0;
   uint32_t my_key = 0;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
+    uint32_t best = key[0];
+    int bi = 0;
 #pragma unroll
-    for (int i = 0; i < NPER; ++i)
-      if (!((used >> i) & 1u) && key[i] > best) best = key[i];
-    best = wave_max_u64(best);
-    const int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
-    if ((e & (kWave - 1)) == lane) used |= 1u << (e / kWave);
+    for (int i = 1; i < NPER; ++i)
+      if (key[i] > best) {
+        best = key[i];
+        bi = i;
+      }
+    const uint32_t wmax = wave_max_u32(best);
+    const uint64_t tied = __ballot(best == wmax);
+    int e;
+    if (__popcll(tied) == 1) {
+      const int wl = __ffsll((unsigned long long)tied) - 1;
+      e = __builtin_amdgcn_readlane(bi, wl) * kWave + wl;
+    } else {
+      e = (int)wave_min_u32(best == wmax ? (uint32_t)(bi * kWave + lane) : 0xFFFFFFFFu);
+    }
+    if ((e & (kWave - 1)) == lane) {
+#pragma unroll
+      for (int i = 0; i < NPER; ++i)
+        if (i == e / kWave) key[i] = 0u;
+    }
     if (lane == j) {
       my_idx = e;
-      my_key = (uint32_t)(best >> 32);
+      my_key = wmax;
     }
   }
   // the pick's logit back from its key (order_key is invertible; a -0 logit
@@ -76,6 +113,89 @@ __device__ __forceinline__ int gate_token(const float* __restrict__ l, int E, in
   if (E <= 256) return gate_token_n<4>(l, E, k, softmax_first, renorm, scale, topk_idx, topk_w);
   if (E <= 512) return gate_token_n<8>(l, E, k, softmax_first, renorm, scale, topk_idx, topk_w);
   return gate_token_n<16>(l, E, k, softmax_first, renorm, scale, topk_idx, topk_w);
+}
+
+constexpr int kRouterTokens = 8;  // tokens per pass of a wave
+
+template <typename XT> struct RouterVec;
+template <> struct RouterVec<uint16_t> {
+  static constexpr int N = 8;
+  __device__ static float dot(uint4 w, uint4 x, float acc) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), __builtin_bit_cast(bf16x2_t, x.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), __builtin_bit_cast(bf16x2_t, x.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), __builtin_bit_cast(bf16x2_t, x.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), __builtin_bit_cast(bf16x2_t, x.w), acc, false);
+    return acc;
+  }
+  __device__ static float scalar(const uint16_t* p, int i) { return __uint_as_float((uint32_t)p[i] << 16); }
+};
+template <> struct RouterVec<float> {
+  static constexpr int N = 4;
+  __device__ static float dot(uint4 w, uint4 x, float acc) {
+    acc = fmaf(__uint_as_float(w.x), __uint_as_float(x.x), acc);
+    acc = fmaf(__uint_as_float(w.y), __uint_as_float(x.y), acc);
+    acc = fmaf(__uint_as_float(w.z), __uint_as_float(x.z), acc);
+    acc = fmaf(__uint_as_float(w.w), __uint_as_float(x.w), acc);
+    return acc;
+  }
+  __device__ static float scalar(const float* p, int i) { return p[i]; }
+};
+
+// One extended router row by one wavefront: r < E is router_w[r] (written,
+// with the bias, to logits[t][r]), r == E the shared-expert gate row
+// (written to sgate_pre[t]).  Lane l holds 16-byte pieces l, l+64, ... of
+// the row and multiplies them with the same pieces of up to 8 tokens at a
+// time; every row is reduced in the same order, so bit-equal router rows
+// give bit-equal logits.  PIECES: 16-byte pieces per lane and token held at
+// once; all of a chunk's loads are issued before its first product.
+template <typename XT, int PIECES>
+__device__ __forceinline__ void router_row(const XT* __restrict__ x, const XT* __restrict__ wr,
+                                           const XT* __restrict__ br, const XT* __restrict__ wsg, int T, int H,
+                                           int E, int r, float* __restrict__ logits, float* __restrict__ sgate_pre) {
+  constexpr int N = RouterVec<XT>::N;
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint4* wrow = reinterpret_cast<const uint4*>(r < E ? wr + (size_t)r * H : wsg);
+  const int npieces = H / N;
+  const float bias = (r < E && br) ? RouterVec<XT>::scalar(br, r) : 0.f;
+  for (int t0 = 0; t0 < T; t0 += kRouterTokens) {
+    float acc[kRouterTokens];
+#pragma unroll
+    for (int j = 0; j < kRouterTokens; ++j) acc[j] = 0.f;
+    for (int p0 = 0; p0 < npieces; p0 += PIECES * kWave) {
+      // every load of the chunk (row pieces and the tokens' pieces) is
+      // issued before the first product, so the wave waits once per chunk
+      uint4 w[PIECES], xv[kRouterTokens][PIECES];
+#pragma unroll
+      for (int i = 0; i < PIECES; ++i) {
+        const int pc = p0 + i * kWave + lane;
+        w[i] = pc < npieces ? wrow[pc] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < kRouterTokens; ++j) {
+        const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)min(t0 + j, T - 1) * H);
+#pragma unroll
+        for (int i = 0; i < PIECES; ++i) {
+          const int pc = p0 + i * kWave + lane;
+          xv[j][i] = pc < npieces ? xr[pc] : make_uint4(0, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kRouterTokens; ++j)
+#pragma unroll
+        for (int i = 0; i < PIECES; ++i) acc[j] = RouterVec<XT>::dot(w[i], xv[j][i], acc[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < kRouterTokens; ++j) acc[j] = wave_sum(acc[j]);
+    if (lane < kRouterTokens && t0 + lane < T) {
+      float v = acc[0];
+#pragma unroll
+      for (int j = 1; j < kRouterTokens; ++j) v = lane == j ? acc[j] : v;
+      if (r < E)
+        logits[(size_t)(t0 + lane) * E + r] = v + bias;
+      else
+        sgate_pre[t0 + lane] = v;
+    }
+  }
 }
 
 // Shared-expert gate of token t computed by one wave: sigmoid(wsg . x[t]).

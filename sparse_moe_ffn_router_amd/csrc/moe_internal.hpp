@@ -84,33 +84,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
   return (a + b) + (c + d);
 }
-__device__ __forceinline__ uint64_t u64max(uint64_t a, uint64_t b) { return a > b ? a : b; }
-// Wave-wide maximum of a 64-bit key, wave-uniform result.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-#define MOE_U64_STEP(CTRL)                                              \
-  {                                                                    \
-    const uint32_t l2 = dpp_u32<CTRL>(lo), h2 = dpp_u32<CTRL>(hi);    \
-    const uint64_t o = ((uint64_t)h2 << 32) | l2;                      \
-    const uint64_t m = u64max(((uint64_t)hi << 32) | lo, o);           \
-    lo = (uint32_t)m;                                                  \
-    hi = (uint32_t)(m >> 32);                                          \
-  }
-  MOE_U64_STEP(kDppXor1)
-  MOE_U64_STEP(kDppXor2)
-  MOE_U64_STEP(kDppHalfMirror)
-  MOE_U64_STEP(kDppMirror)
-#undef MOE_U64_STEP
-  uint64_t r = 0;
-#pragma unroll
-  for (int row = 0; row < 4; ++row) {
-    const uint64_t x = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, row * 16) << 32) |
-                       (uint32_t)__builtin_amdgcn_readlane((int)lo, row * 16);
-    r = u64max(r, x);
-  }
-  return r;
-}
-
 // Raw buffer resource over [base, base + bytes): loads at offsets past the
 // end return zero (gfx9 descriptor word 3: 32-bit data format).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {

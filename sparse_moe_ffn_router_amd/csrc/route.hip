@@ -10,89 +10,19 @@
 namespace moe {
 namespace {
 
-constexpr int kRouterTokens = 8;  // tokens per pass of a wave
 constexpr int kRouterWaves = 1;   // router rows per workgroup (one per wave)
-constexpr int kMaxPieces = 8;     // 16-byte pieces per lane held at once
-
-template <typename XT> struct Vec;
-template <> struct Vec<uint16_t> {
-  static constexpr int N = 8;
-  __device__ static float dot(uint4 w, uint4 x, float acc) {
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), __builtin_bit_cast(bf16x2_t, x.x), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), __builtin_bit_cast(bf16x2_t, x.y), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), __builtin_bit_cast(bf16x2_t, x.z), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), __builtin_bit_cast(bf16x2_t, x.w), acc, false);
-    return acc;
-  }
-  __device__ static float scalar(const uint16_t* p, int i) { return __uint_as_float((uint32_t)p[i] << 16); }
-};
-template <> struct Vec<float> {
-  static constexpr int N = 4;
-  __device__ static float dot(uint4 w, uint4 x, float acc) {
-    acc = fmaf(__uint_as_float(w.x), __uint_as_float(x.x), acc);
-    acc = fmaf(__uint_as_float(w.y), __uint_as_float(x.y), acc);
-    acc = fmaf(__uint_as_float(w.z), __uint_as_float(x.z), acc);
-    acc = fmaf(__uint_as_float(w.w), __uint_as_float(x.w), acc);
-    return acc;
-  }
-  __device__ static float scalar(const float* p, int i) { return p[i]; }
-};
 
 // Extended router rows: r < E is router_w[r] (written to logits[t][r] with
 // the bias), r == E the shared-expert gate row (written to sgate_pre[t]).
-// One wave per row: lane l holds 16-byte pieces l, l+64, ... of the row and
-// multiplies them with the same pieces of up to 8 tokens at a time; every
-// row is reduced in the same order, so bit-equal router rows give bit-equal
-// logits.
+// One wave per row (router_row).
 template <typename XT>
 __global__ __launch_bounds__(kRouterWaves * kWave) void k_router_gemv(
     const XT* __restrict__ x, const XT* __restrict__ wr, const XT* __restrict__ br,
     const XT* __restrict__ wsg, int32_t T, int32_t H, int32_t E, int32_t row0, int32_t row1,
     float* __restrict__ logits, float* __restrict__ sgate_pre) {
-  constexpr int N = Vec<XT>::N;
-  const int lane = threadIdx.x & (kWave - 1);
   const int r = row0 + blockIdx.x * kRouterWaves + (threadIdx.x / kWave);
   if (r >= row1) return;
-  const uint4* wrow = reinterpret_cast<const uint4*>(r < E ? wr + (size_t)r * H : wsg);
-  const int npieces = H / N;
-  const float bias = (r < E && br) ? Vec<XT>::scalar(br, r) : 0.f;
-  for (int t0 = 0; t0 < T; t0 += kRouterTokens) {
-    float acc[kRouterTokens];
-#pragma unroll
-    for (int j = 0; j < kRouterTokens; ++j) acc[j] = 0.f;
-    for (int p0 = 0; p0 < npieces; p0 += kMaxPieces * kWave) {
-      uint4 w[kMaxPieces];
-#pragma unroll
-      for (int i = 0; i < kMaxPieces; ++i) {
-        const int pc = p0 + i * kWave + lane;
-        w[i] = pc < npieces ? wrow[pc] : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < kRouterTokens; ++j) {
-        const int t = min(t0 + j, T - 1);
-        const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)t * H);
-        uint4 xv[kMaxPieces];
-#pragma unroll
-        for (int i = 0; i < kMaxPieces; ++i) {
-          const int pc = p0 + i * kWave + lane;
-          xv[i] = pc < npieces ? xr[pc] : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < kMaxPieces; ++i) acc[j] = Vec<XT>::dot(w[i], xv[i], acc[j]);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kRouterTokens; ++j) acc[j] = wave_sum(acc[j]);
-    if (lane < kRouterTokens && t0 + lane < T) {
-      float v = acc[0];
-#pragma unroll
-      for (int j = 1; j < kRouterTokens; ++j) v = lane == j ? acc[j] : v;
-      if (r < E)
-        logits[(size_t)(t0 + lane) * E + r] = v + bias;
-      else
-        sgate_pre[t0 + lane] = v;
-    }
-  }
+  router_row<XT, 4>(x, wr, br, wsg, T, H, E, r, logits, sgate_pre);
 }
 
 constexpr int kGateWaves = 4;  // tokens per workgroup
