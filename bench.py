@@ -108,7 +108,7 @@ class Layer:
         """The same kernels through the four step entry points; optional
         events bracket the expert gate/up launch."""
         m, w = self.moe, self.weights[step % len(self.weights)]
-        m.moe_route(self.cfg, w, self.x, self.logits, self.idx, self.wt, self.sg, self.T)
+        m.moe_route(self.cfg, w, self.x, self.logits, self.idx, self.wt, self.sg, self.T, self.ws)
         m.moe_permute(self.cfg, self.idx, self.T, self.offsets, self.sorted, self.pos, self.ws)
         if ev_ffn:
             ev_ffn[0].record()
@@ -313,7 +313,7 @@ def main():
         # (this batch's tokens, the decode layer's router) and add it
         rt = Layer(dec, 1, T=T, x=pre.t["x"])
         r_ms, _ = time_loop(lambda s: rt.moe.moe_route(rt.cfg, rt.weights[0], rt.x, rt.logits, rt.idx, rt.wt,
-                                                        rt.sg, T), a.prefill_steps, 3)
+                                                        rt.sg, T, rt.ws), a.prefill_steps, 3)
         tot = p_ms + r_ms
         fl = layer_flops(pre, T)
         tf = fl / (tot * 1e-3) / 1e12

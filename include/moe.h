@@ -126,9 +126,14 @@ size_t moe_workspace_bytes(const moe_config* cfg, int32_t T);
  *            lowest index first among bit-equal logits; -0 == +0)
  *   topk_w   [T][k] fp32 routing weights
  *   sgate    [T] fp32 sigmoid shared-expert gate; required iff shared_ff > 0
+ *   ws       NULL, or scratch of ws_bytes >= moe_workspace_bytes(cfg, T)
+ *            bytes: with it, a large batch's router product is split over
+ *            ranges of the hidden dimension (more workgroups) whose partial
+ *            sums the gating adds up in a fixed order
  * Same logits in => bit-identical topk_idx, on every call. */
 int moe_route(const moe_config* cfg, const moe_weights* w, const void* x, float* logits,
-              int32_t* topk_idx, float* topk_w, float* sgate, int32_t T, hipStream_t stream);
+              int32_t* topk_idx, float* topk_w, float* sgate, int32_t T, void* ws, size_t ws_bytes,
+              hipStream_t stream);
 
 /* Token -> expert permutation: a stable counting sort of the T*k
  * assignments a = t*k + j by expert id (ascending a inside each segment).

@@ -79,7 +79,7 @@ def _load():
     L.moe_workspace_bytes.restype = sz
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_status_string.restype = ctypes.c_char_p
-    L.moe_route.argtypes = [C, W, vp, vp, vp, vp, vp, i32, vp]
+    L.moe_route.argtypes = [C, W, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     L.moe_permute.argtypes = [C, vp, i32, vp, vp, vp, vp, sz, vp]
     L.moe_expert_ffn.argtypes = [C, W, vp, vp, vp, i32, vp, vp, sz, vp]
     L.moe_combine.argtypes = [C, W, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
@@ -132,10 +132,11 @@ def moe_workspace_bytes(cfg: MoeConfig, T: int) -> int:
     return int(lib.moe_workspace_bytes(ctypes.byref(cfg._c()), T))
 
 
-def moe_route(cfg, w, x, logits, topk_idx, topk_w, sgate, T, stream=None):
+def moe_route(cfg, w, x, logits, topk_idx, topk_w, sgate, T, ws=None, stream=None, ws_bytes=None):
     c, ww = cfg._c(), _weights(w)
+    nb = _nbytes(ws) if ws_bytes is None else ws_bytes
     _check(lib.moe_route(ctypes.byref(c), ctypes.byref(ww), _ptr(x), _ptr(logits), _ptr(topk_idx), _ptr(topk_w),
-                         _ptr(sgate), T, _stream(stream)), "moe_route")
+                         _ptr(sgate), T, _ptr(ws), nb, _stream(stream)), "moe_route")
 
 
 def moe_permute(cfg, topk_idx, T, offsets, sorted_assign, assign_pos, ws, stream=None, ws_bytes=None):

@@ -58,6 +58,12 @@ int make_plan(const moe_config* c, int32_t T, Plan* p) {
   p->off_perm = o; o += p->perm_bytes;
   p->off_h = o; o += up256((size_t)(p->n_assign * c->expert_ff + (p->shared ? (int64_t)T * c->shared_ff : 0)) * p->elem_x);
   p->off_y = o; o += p->y_bytes;
+  p->nsplit = 1;
+  if (T > kGemvMaxT && mfma_shapes_ok(c)) {
+    int steps;
+    router_split(c, T, &p->nsplit, &steps);
+  }
+  p->off_part = o; o += p->nsplit > 1 ? up256((size_t)p->nsplit * T * c->n_expert * 4) : 0;
   p->total = o;
   // the few-token kernels address activations and h with 32-bit buffer offsets
   const size_t act_bytes = (size_t)(p->n_assign * c->expert_ff + (p->shared ? (int64_t)T * c->shared_ff : 0)) * p->elem_x;
@@ -110,7 +116,7 @@ const char* moe_status_string(int status) {
 }
 
 int moe_route(const moe_config* cfg, const moe_weights* w, const void* x, float* logits, int32_t* topk_idx,
-              float* topk_w, float* sgate, int32_t T, hipStream_t stream) {
+              float* topk_w, float* sgate, int32_t T, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_config(cfg);
   if (st) return st;
   if (T < 0) return MOE_EINVAL;
@@ -120,10 +126,19 @@ int moe_route(const moe_config* cfg, const moe_weights* w, const void* x, float*
   if (!logits || !topk_idx || !topk_w || !aligned16(logits)) return MOE_EINVAL;
   if ((w->router_w || shared) && (!x || !aligned16(x))) return MOE_EINVAL;
   if (shared && !sgate) return MOE_EINVAL;
+  Plan p = {};
+  p.nsplit = 1;
+  if (ws) {
+    if ((st = make_plan(cfg, T, &p))) return st;
+    if (ws_bytes < p.total || ((uintptr_t)ws & 255u)) return MOE_EWORKSPACE;
+  }
+  // split router product: partial sums in the workspace's partials area
+  float* part = (ws && p.nsplit > 1 && w->router_w) ? (float*)((char*)ws + p.off_part) : nullptr;
   // the pre-sigmoid shared-gate dot is staged in sgate itself
-  hipError_t e = launch_router_logits(cfg, w, x, T, logits, sgate, stream);
+  hipError_t e = launch_router_logits(cfg, w, x, T, logits, sgate, stream, part);
   if (e != hipSuccess) return MOE_EHIP;
-  return hip_status(launch_gating(cfg, w, x, logits, sgate, T, topk_idx, topk_w, sgate, stream));
+  return hip_status(
+      launch_gating(cfg, w, x, logits, sgate, T, topk_idx, topk_w, sgate, stream, part, part ? p.nsplit : 1));
 }
 
 int moe_permute(const moe_config* cfg, const int32_t* topk_idx, int32_t T, int32_t* offsets, int32_t* sorted_assign,
@@ -189,13 +204,16 @@ int moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, int3
   int32_t* perm = (int32_t*)(b + p.off_perm);
   void* h = b + p.off_h;
   void* y = b + p.off_y;
+  // MFMA router product split over K ranges, summed by the gating kernel
+  float* part = (p.nsplit > 1 && w->router_w) ? (float*)(b + p.off_part) : nullptr;
   hipError_t e;
-  if ((e = launch_router_logits(cfg, w, x, T, lg, sg, stream)) != hipSuccess) return MOE_EHIP;
+  if ((e = launch_router_logits(cfg, w, x, T, lg, sg, stream, part)) != hipSuccess) return MOE_EHIP;
   if (can_fuse_gate_permute(T)) {
     if ((e = launch_gate_permute(cfg, lg, sg, T, idx, wt, sg, offsets, sorted, pos, stream)) != hipSuccess)
       return MOE_EHIP;
   } else {
-    if ((e = launch_gating(cfg, w, x, lg, sg, T, idx, wt, sg, stream)) != hipSuccess) return MOE_EHIP;
+    if ((e = launch_gating(cfg, w, x, lg, sg, T, idx, wt, sg, stream, part, part ? p.nsplit : 1)) != hipSuccess)
+      return MOE_EHIP;
     if ((e = launch_permute(cfg, idx, T, offsets, sorted, pos, perm, stream)) != hipSuccess) return MOE_EHIP;
   }
   if ((e = launch_expert_ffn(cfg, w, x, offsets, sorted, T, h, stream)) != hipSuccess) return MOE_EHIP;

@@ -50,7 +50,11 @@ struct GemmArgs {
   const int32_t* sorted_assign;
   void* out;                 // h (bf16) | y (bf16) | router logits (fp32)
   int32_t T, k, H, E, F, Fs, shared, oai;
-  int32_t n_tiles;           // column tiles per segment (max over segments)
+  int32_t n_tiles;           // column tiles per segment (max over segments); router: times ksplit
+  int32_t ksplit;            // router: K split into ksplit ranges of split_steps steps (1: no split)
+  int32_t split_steps;
+  int32_t col_tiles;         // router: column tiles of one K range
+  float* part;               // router with ksplit > 1: partial logits [ksplit][T][E]
   int32_t m_tiles_max;       // grid bound on row tiles
   float alpha, limit;
 };
@@ -88,6 +92,7 @@ struct CodeRegs {
 // column tile.
 struct Tile {
   int seg, p0, rows, c0, Fe, ncols, K;
+  int ks, k0, nk;  // K range (router split-K): index, first step, steps
   bool sh;
 };
 
@@ -97,6 +102,7 @@ struct Pipe {
   uint32_t a_off[kAChunks], b_off[kBChunks], sc_off;
   bool a_ok[kAChunks];      // gate/up: the staged row is a row of the tile
   int32_t* ids;             // the tile's assignment ids in LDS (gate/up, down)
+  int k0;                   // first K step of the tile
   bool two_mats, mx;
   int nk;
 };
@@ -106,7 +112,7 @@ struct Pipe {
 // has the same number of outstanding loads).
 __device__ __forceinline__ void pipe_issue(const Pipe& p, int s, int wid, uint8_t* __restrict__ la,
                                            uint8_t* __restrict__ lb, CodeRegs& cr) {
-  const uint32_t kb = s < p.nk ? (uint32_t)s * BK * 2 : kOutOfRange;  // byte offset of the step in a bf16 row
+  const uint32_t kb = s < p.nk ? (uint32_t)(p.k0 + s) * BK * 2 : kOutOfRange;  // byte offset of the step in a bf16 row
 #pragma unroll
   for (int i = 0; i < kAChunks; ++i) dma16(p.ra, la + (i * kThreads + wid * kWave) * 16, p.a_off[i] + kb);
   if (!p.mx) {
@@ -116,8 +122,8 @@ __device__ __forceinline__ void pipe_issue(const Pipe& p, int s, int wid, uint8_
       dma16(up ? p.rw1 : p.rw0, lb + (i * kThreads + wid * kWave) * 16, p.b_off[i] + kb);
     }
   } else {
-    cr.codes = buf_load16(p.rw0, p.b_off[0], s < p.nk ? (uint32_t)s * BK / 2 : kOutOfRange);
-    cr.sc = buf_load_u8(p.rsc, p.sc_off, s < p.nk ? (uint32_t)s * BK / 32 : kOutOfRange);
+    cr.codes = buf_load16(p.rw0, p.b_off[0], s < p.nk ? (uint32_t)(p.k0 + s) * BK / 2 : kOutOfRange);
+    cr.sc = buf_load_u8(p.rsc, p.sc_off, s < p.nk ? (uint32_t)(p.k0 + s) * BK / 32 : kOutOfRange);
   }
 }
 
@@ -140,6 +146,7 @@ __device__ __forceinline__ void pipe_issue_pq(const Pipe& p, const Pipe& q, int 
   x.two_mats = uq ? q.two_mats : p.two_mats;
   x.mx = uq ? q.mx : p.mx;
   x.nk = uq ? q.nk : p.nk;
+  x.k0 = uq ? q.k0 : p.k0;
   pipe_issue(x, uq ? s2 - p.nk : s2, wid, la, lb, cr);
 }
 
@@ -279,9 +286,13 @@ __device__ int find_segment(const SegTables& t, int nseg, int mt) {
 // lies past the segment's columns (shared expert narrower than the routed).
 template <int MODE>
 __device__ bool tile_at(const GemmArgs& a, const SegTables& st, int lin, int total_m, Tile& t) {
-  const int nt = lin / total_m, mt = lin % total_m;
+  int nt = lin / total_m;
+  const int mt = lin % total_m;
   const int nseg = a.E + a.shared;
+  t.ks = 0;
   if (MODE == MODE_ROUTER) {
+    t.ks = nt / a.col_tiles;
+    nt = nt % a.col_tiles;
     t.seg = 0;
     t.p0 = mt * BM;
     t.rows = min(BM, a.T - t.p0);
@@ -297,6 +308,8 @@ __device__ bool tile_at(const GemmArgs& a, const SegTables& st, int lin, int tot
   const int col_tile = MODE == MODE_GATEUP ? BN / 2 : BN;  // features | outputs per tile
   t.c0 = nt * col_tile;
   t.K = MODE == MODE_DOWN ? t.Fe : a.H;
+  t.k0 = t.ks * a.split_steps;
+  t.nk = min(t.K / BK - t.k0, a.split_steps);
   return t.c0 < t.ncols;
 }
 
@@ -410,7 +423,8 @@ __device__ void make_pipe(const GemmArgs& a, const Tile& t, int32_t* ids, Pipe& 
   // SwiGLU with separate gate and up matrices: B rows >= BN/2 read the up matrix
   p.two_mats = MODE == MODE_GATEUP && (t.sh || !a.oai);
   p.mx = mx;
-  p.nk = t.K / BK;
+  p.nk = t.nk;
+  p.k0 = t.k0;
 }
 
 // Gate/up: token row offsets from the assignment ids that make_pipe sent to
@@ -557,7 +571,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const Tile& t, const
           for (int q = 0; q < 16; ++q) {
             const int r = wm * 64 + i * 32 + (q / 4) * 8 + (lane >> 5) * 4 + (q & 3);
             if (r < t.rows) {
-              if (MODE == MODE_ROUTER)
+              if (MODE == MODE_ROUTER && a.ksplit > 1)
+                a.part[((size_t)t.ks * a.T + t.p0 + r) * t.ncols + o] = acc[i][j][q];
+              else if (MODE == MODE_ROUTER)
                 lg[(size_t)(t.p0 + r) * t.ncols + o] = acc[i][j][q] + bias;
               else {
                 const int src = i * 32 + (q / 4) * 8 + (q & 3);
@@ -711,8 +727,22 @@ hipError_t launch(const GemmArgs& a, bool mx, int min_k, hipStream_t s) {
 
 }  // namespace
 
+// Router split of the K steps: about one tile per CU over all splits, at
+// least three steps per range (persistent launches), ranges of equal length
+// but the last.
+void router_split(const moe_config* c, int32_t T, int* ksplit, int* steps) {
+  const int nk = c->hidden / BK;
+  const int tiles = ((c->n_expert + BN - 1) / BN) * ((T + BM - 1) / BM);
+  int ks = 256 / (tiles > 0 ? tiles : 1);
+  if (ks > nk / 3) ks = nk / 3;
+  if (ks < 1) ks = 1;
+  const int spp = (nk + ks - 1) / ks;
+  *steps = spp;
+  *ksplit = (nk + spp - 1) / spp;
+}
+
 hipError_t launch_router_mfma(const moe_config* c, const moe_weights* w, const void* x, int32_t T, float* logits,
-                              float* sgate_pre, hipStream_t s) {
+                              float* sgate_pre, hipStream_t s, float* part) {
   (void)sgate_pre;  // the shared-gate dot is taken by the gating kernel
   GemmArgs a = {};
   a.a_src = (const uint16_t*)x;
@@ -720,9 +750,16 @@ hipError_t launch_router_mfma(const moe_config* c, const moe_weights* w, const v
   a.bias = (const uint16_t*)w->router_b;
   a.out = logits;
   a.T = T; a.k = c->top_k; a.H = c->hidden; a.E = c->n_expert; a.F = c->expert_ff; a.Fs = c->shared_ff;
-  a.n_tiles = (c->n_expert + BN - 1) / BN;
+  a.col_tiles = (c->n_expert + BN - 1) / BN;
   a.m_tiles_max = (T + BM - 1) / BM;
-  return launch<MODE_ROUTER>(a, false, c->hidden, s);
+  a.ksplit = 1;
+  a.split_steps = c->hidden / BK;
+  if (part) router_split(c, T, &a.ksplit, &a.split_steps);
+  a.part = part;
+  a.n_tiles = a.col_tiles * a.ksplit;
+  const int nk = c->hidden / BK;
+  const int last = nk - (a.ksplit - 1) * a.split_steps;  // steps of the last range
+  return launch<MODE_ROUTER>(a, false, (last < a.split_steps ? last : a.split_steps) * BK, s);
 }
 
 bool mfma_shapes_ok(const moe_config* c) {
@@ -748,6 +785,8 @@ hipError_t launch_gateup_mfma(const moe_config* c, const moe_weights* w, const v
   const int fmax = c->expert_ff > c->shared_ff ? c->expert_ff : c->shared_ff;
   a.n_tiles = (fmax + BN / 2 - 1) / (BN / 2);
   a.m_tiles_max = row_tiles_bound(c, T);
+  a.ksplit = 1;
+  a.split_steps = c->hidden / BK;
 #ifdef MOE_GATEUP_GRID_ALL
   return launch<MODE_GATEUP>(a, c->w_dtype == MOE_DTYPE_MXFP4, 0, s);
 #else
@@ -770,6 +809,8 @@ hipError_t launch_down_mfma(const moe_config* c, const moe_weights* w, const voi
   a.shared = c->shared_ff > 0; a.oai = c->act == MOE_ACT_SWIGLU_OAI;
   a.n_tiles = (c->hidden + BN - 1) / BN;
   a.m_tiles_max = row_tiles_bound(c, T);
+  a.ksplit = 1;
+  a.split_steps = (c->expert_ff > c->shared_ff ? c->expert_ff : c->shared_ff) / BK;
   const int min_k = c->shared_ff > 0 && c->shared_ff < c->expert_ff ? c->shared_ff : c->expert_ff;
   return launch<MODE_DOWN>(a, c->w_dtype == MOE_DTYPE_MXFP4, min_k, s);
 }

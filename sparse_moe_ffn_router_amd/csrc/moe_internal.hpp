@@ -132,7 +132,8 @@ struct Plan {
   int nseg;           // E (+1)
   size_t elem_x;      // bytes per activation / h element
   size_t off_logits, off_idx, off_w, off_sgate, off_offsets, off_sorted, off_pos;
-  size_t off_perm, off_h, off_y, total;
+  size_t off_perm, off_h, off_y, off_part, total;
+  int32_t nsplit;     // router split-K ranges (1: none)
   size_t perm_bytes, y_bytes;  // scratch needed by moe_permute / moe_combine alone
 };
 
@@ -140,11 +141,15 @@ int make_plan(const moe_config* c, int32_t T, Plan* p);
 int check_config(const moe_config* c);
 
 // Launchers (return hipError_t of the last launch).
+// part: when the router product runs on MFMA (sgate_in_router false) and
+// part is given, it is split over K ranges (router_split) with the partial
+// sums in part [nsplit][T][E], which launch_gating then adds up into logits.
 hipError_t launch_router_logits(const moe_config* c, const moe_weights* w, const void* x, int32_t T,
-                                float* logits, float* sgate_pre, hipStream_t s);
-hipError_t launch_gating(const moe_config* c, const moe_weights* w, const void* x, const float* logits,
+                                float* logits, float* sgate_pre, hipStream_t s, float* part = nullptr);
+void router_split(const moe_config* c, int32_t T, int* nsplit, int* steps);
+hipError_t launch_gating(const moe_config* c, const moe_weights* w, const void* x, float* logits,
                          const float* sgate_pre, int32_t T, int32_t* topk_idx, float* topk_w, float* sgate,
-                         hipStream_t s);
+                         hipStream_t s, const float* part = nullptr, int32_t nsplit = 1);
 // Whether the shared-gate dot is computed by the router-product kernel
 // (few tokens) rather than by the gating kernel.
 bool sgate_in_router(const moe_config* c, int32_t T);

@@ -29,15 +29,27 @@ constexpr int kGateWaves = 4;  // tokens per workgroup
 
 // sg_mode: 0 no shared expert; 1 sigmoid of the dot staged in sgate_pre;
 // 2 the wave computes the dot itself from x and wsg.
+// part / nsplit > 1: the router product came as nsplit partial sums over
+// K ranges; the logits are their sum in range order plus the router bias,
+// written to logits before the gating reads them back.
 template <typename XT>
 __global__ __launch_bounds__(kGateWaves * kWave) void k_gating(
-    const float* __restrict__ logits, const float* __restrict__ sgate_pre, const XT* __restrict__ x,
+    float* __restrict__ logits, const float* __restrict__ sgate_pre, const XT* __restrict__ x,
     const XT* __restrict__ wsg, int32_t H, int32_t sg_mode, int32_t T, int32_t E, int32_t k,
     int32_t softmax_first, int32_t renorm, float scale, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w, float* __restrict__ sgate) {
+    float* __restrict__ topk_w, float* __restrict__ sgate, const float* __restrict__ part, int32_t nsplit,
+    const XT* __restrict__ br) {
   const int lane = threadIdx.x & (kWave - 1);
   const int t = blockIdx.x * kGateWaves + threadIdx.x / kWave;
   if (t >= T) return;
+  if (nsplit > 1) {
+    for (int e = lane; e < E; e += kWave) {
+      float v = part[(size_t)t * E + e];
+      for (int s = 1; s < nsplit; ++s) v += part[((size_t)s * T + t) * E + e];
+      if (br) v += RouterVec<XT>::scalar(br, e);
+      logits[(size_t)t * E + e] = v;
+    }
+  }
   gate_token(logits + (size_t)t * E, E, k, softmax_first, renorm, scale, topk_idx + (size_t)t * k,
              topk_w + (size_t)t * k);
   if (sg_mode == 2) {
@@ -51,20 +63,20 @@ __global__ __launch_bounds__(kGateWaves * kWave) void k_gating(
 }  // namespace
 
 hipError_t launch_router_mfma(const moe_config* c, const moe_weights* w, const void* x, int32_t T, float* logits,
-                              float* sgate_pre, hipStream_t s);  // ffn_mfma.hip
+                              float* sgate_pre, hipStream_t s, float* part);  // ffn_mfma.hip
 bool mfma_shapes_ok(const moe_config* c);
 
 bool sgate_in_router(const moe_config* c, int32_t T) { return !(T > kGemvMaxT && mfma_shapes_ok(c)); }
 
 hipError_t launch_router_logits(const moe_config* c, const moe_weights* w, const void* x, int32_t T,
-                                float* logits, float* sgate_pre, hipStream_t s) {
+                                float* logits, float* sgate_pre, hipStream_t s, float* part) {
   const int E = c->n_expert;
   const bool mfma = !sgate_in_router(c, T);
   const int row0 = w->router_w ? 0 : E;
   // with the MFMA router the shared-gate dot moves to the gating kernel
   const int row1 = (c->shared_ff > 0 && !mfma) ? E + 1 : E;
   if (row1 <= row0 || T == 0) return hipSuccess;
-  if (mfma) return launch_router_mfma(c, w, x, T, logits, sgate_pre, s);
+  if (mfma) return launch_router_mfma(c, w, x, T, logits, sgate_pre, s, part);
   dim3 grid((row1 - row0 + kRouterWaves - 1) / kRouterWaves);
   if (c->x_dtype == MOE_DTYPE_BF16)
     k_router_gemv<uint16_t><<<grid, kRouterWaves * kWave, 0, s>>>(
@@ -77,9 +89,9 @@ hipError_t launch_router_logits(const moe_config* c, const moe_weights* w, const
   return hipGetLastError();
 }
 
-hipError_t launch_gating(const moe_config* c, const moe_weights* w, const void* x, const float* logits,
+hipError_t launch_gating(const moe_config* c, const moe_weights* w, const void* x, float* logits,
                          const float* sgate_pre, int32_t T, int32_t* topk_idx, float* topk_w, float* sgate,
-                         hipStream_t s) {
+                         hipStream_t s, const float* part, int32_t nsplit) {
   if (T == 0) return hipSuccess;
   const int softmax_first = c->gating == MOE_GATING_SOFTMAX_TOPK;
   const int sg_mode = c->shared_ff <= 0 ? 0 : sgate_in_router(c, T) ? 1 : 2;
@@ -87,11 +99,13 @@ hipError_t launch_gating(const moe_config* c, const moe_weights* w, const void* 
   if (c->x_dtype == MOE_DTYPE_BF16)
     k_gating<uint16_t><<<grid, kGateWaves * kWave, 0, s>>>(
         logits, sgate_pre, (const uint16_t*)x, (const uint16_t*)w->sh_gate_inp, c->hidden, sg_mode, T, c->n_expert,
-        c->top_k, softmax_first, c->norm_topk_prob, c->weights_scale, topk_idx, topk_w, sgate);
+        c->top_k, softmax_first, c->norm_topk_prob, c->weights_scale, topk_idx, topk_w, sgate, part, nsplit,
+        (const uint16_t*)w->router_b);
   else
     k_gating<float><<<grid, kGateWaves * kWave, 0, s>>>(
         logits, sgate_pre, (const float*)x, (const float*)w->sh_gate_inp, c->hidden, sg_mode, T, c->n_expert,
-        c->top_k, softmax_first, c->norm_topk_prob, c->weights_scale, topk_idx, topk_w, sgate);
+        c->top_k, softmax_first, c->norm_topk_prob, c->weights_scale, topk_idx, topk_w, sgate, part, nsplit,
+        (const float*)w->router_b);
   return hipGetLastError();
 }
 

@@ -71,16 +71,18 @@ def test_entry_points_reject_bad_arguments_before_launch():
     full = moe._Weights(*([fake] * len(moe._WEIGHT_FIELDS)))
     fb = ctypes.byref(full)
     assert _raw("moe_expert_ffn", cb, fb, None, None, None, 0, None, None, 0, None) == moe.MOE_OK
-    assert _raw("moe_route", cb, fb, None, None, None, None, None, 0, None) == moe.MOE_OK
+    assert _raw("moe_route", cb, fb, None, None, None, None, None, 0, None, 0, None) == moe.MOE_OK
     assert _raw("moe_permute", cb, None, 0, None, None, None, None, 0, None) == moe.MOE_OK
     # negative T
-    assert _raw("moe_route", cb, fb, None, None, None, None, None, -1, None) == moe.MOE_EINVAL
+    assert _raw("moe_route", cb, fb, None, None, None, None, None, -1, None, 0, None) == moe.MOE_EINVAL
     # missing outputs
-    assert _raw("moe_route", cb, fb, fake, None, fake, fake, fake, 8, None) == moe.MOE_EINVAL
+    assert _raw("moe_route", cb, fb, fake, None, fake, fake, fake, 8, None, 0, None) == moe.MOE_EINVAL
     # shared expert needs sgate
-    assert _raw("moe_route", cb, fb, fake, fake, fake, fake, None, 8, None) == moe.MOE_EINVAL
+    assert _raw("moe_route", cb, fb, fake, fake, fake, fake, None, 8, None, 0, None) == moe.MOE_EINVAL
     # misaligned pointer
-    assert _raw("moe_route", cb, fb, fake + 2, fake, fake, fake, fake, 8, None) == moe.MOE_EINVAL
+    assert _raw("moe_route", cb, fb, fake + 2, fake, fake, fake, fake, 8, None, 0, None) == moe.MOE_EINVAL
+    # route scratch: optional, but when given at least moe_workspace_bytes
+    assert _raw("moe_route", cb, fb, fake, fake, fake, fake, fake, 4096, fake, 16, None) == moe.MOE_EWORKSPACE
     mis = moe._Weights(*([fake] * len(moe._WEIGHT_FIELDS)))
     mis.gate_w = fake + 4
     assert _raw("moe_expert_ffn", cb, ctypes.byref(mis), fake, fake, fake, 8, fake, None, 0, None) == moe.MOE_EINVAL
@@ -96,7 +98,7 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert _raw("moe_forward", cb, ctypes.byref(nr), fake, 8, fake, None, None, None, None, fake, need, None) == moe.MOE_EINVAL
     # unsupported combination
     c2 = _cfg(w_dtype=moe.DTYPE_MXFP4)._c()
-    assert _raw("moe_route", ctypes.byref(c2), fb, fake, fake, fake, fake, fake, 8, None) == moe.MOE_EUNSUPPORTED
+    assert _raw("moe_route", ctypes.byref(c2), fb, fake, fake, fake, fake, fake, 8, None, 0, None) == moe.MOE_EUNSUPPORTED
 
 
 def test_status_strings():

@@ -18,7 +18,7 @@ ROUTE_CASES = [("tiny_fp32", 8), ("qwen35moe_decode", 8), ("qwen35moe_prefill_zi
 ROUTE_ONLY = ("x", "router_w", "sh_gate_inp", "logits")
 
 
-def _route(case, logits_np, with_router):
+def _route(case, logits_np, with_router, ws=False):
     cfg = config_of(case)
     w = device_weights(case) if with_router else {k: v for k, v in device_weights(case).items()
                                                   if k not in ("router_w", "router_b")}
@@ -29,7 +29,8 @@ def _route(case, logits_np, with_router):
     idx = torch.empty((T, case.k), dtype=torch.int32, device="cuda")
     wt = torch.empty((T, case.k), dtype=torch.float32, device="cuda")
     sg = torch.empty(T, dtype=torch.float32, device="cuda") if case.has_shared else None
-    moe.moe_route(cfg, w, x, lg, idx, wt, sg, T)
+    scratch = torch.empty(moe.moe_workspace_bytes(cfg, T), dtype=torch.uint8, device="cuda") if ws else None
+    moe.moe_route(cfg, w, x, lg, idx, wt, sg, T, scratch)
     torch.cuda.synchronize()
     return lg.cpu().numpy(), idx.cpu().numpy(), wt.cpu().numpy(), None if sg is None else sg.cpu().numpy()
 
@@ -139,6 +140,37 @@ def test_router_product_keeps_planted_ties(dtype, T):
     # and on identical logits the indices are the oracle's
     ref_idx, _ = L.route(lg)
     assert np.array_equal(idx, ref_idx)
+
+
+def test_router_product_split_over_hidden():
+    """With scratch, a many-token bf16 router product runs in ranges of the
+    hidden dimension summed by the gating kernel in a fixed order: logits
+    within the fp32 bound of the oracle's, bit-equal router rows still give
+    bit-equal logits, the indices are the oracle's on those logits, and two
+    calls agree bit for bit."""
+    case = synth.make_case("qwen35moe_decode", T=333, only=set(ROUTE_ONLY))
+    rw = case.t["router_w"]
+    rw[9] = rw[4]
+    rw[13] = rw[4]
+    rw[12] = rw[7]
+    a = _route(case, None, with_router=True, ws=True)
+    b = _route(case, None, with_router=True, ws=True)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+    lg, idx = a[0], a[1]
+    assert np.array_equal(lg[:, 4], lg[:, 9]) and np.array_equal(lg[:, 4], lg[:, 13])
+    assert np.array_equal(lg[:, 7], lg[:, 12])
+    L = oracle.Layer(case)
+    ref = L.router_logits()
+    xa = np.abs(_f64(case.t["x"], case.x_dtype))
+    wa = np.abs(_f64(rw, case.router_dtype))
+    bound = case.H * 2.0 ** -24 * (xa @ wa.T) + 2.0 ** -24 * np.abs(ref)
+    assert np.all(np.abs(lg.astype(np.float64) - ref) <= bound)
+    ref_idx, _ = L.route(lg)
+    assert np.array_equal(idx, ref_idx)
+    # the unsplit product (no scratch) is within the same bound
+    c = _route(case, None, with_router=True)
+    assert np.all(np.abs(c[0].astype(np.float64) - ref) <= bound)
 
 
 def test_route_deterministic_and_T0():
