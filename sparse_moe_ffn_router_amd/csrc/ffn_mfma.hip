@@ -271,11 +271,13 @@ __device__ int build_tables(const int32_t* __restrict__ offsets, int nseg, SegTa
 }
 
 // Segment holding row tile mt (wave-uniform), from the LDS tables.
-__device__ int find_segment(const SegTables& t, int nseg, int mt) {
+// Segment holding tile lin when each segment's tiles are contiguous in lin
+// (scale = column tiles per row tile).
+__device__ int find_segment(const SegTables& t, int nseg, int lin, int scale) {
   const int lane = threadIdx.x & (kWave - 1);
   for (int base = 0; base < nseg; base += kWave) {
     const int e = base + lane;
-    const bool hit = e < nseg && t.tpre[e] <= mt && mt < t.tpre[e + 1];
+    const bool hit = e < nseg && t.tpre[e] * scale <= lin && lin < t.tpre[e + 1] * scale;
     const uint64_t m = __ballot(hit);
     if (m) return base + __ffsll((unsigned long long)m) - 1;
   }
@@ -284,10 +286,15 @@ __device__ int find_segment(const SegTables& t, int nseg, int mt) {
 
 // Tile lin of the (column tile, row tile) space; false if its column tile
 // lies past the segment's columns (shared expert narrower than the routed).
+// Expert GEMMs: the tiles of one segment are contiguous in lin, column-tile
+// major inside it (nt, then row tile), so the row tiles sharing a weight
+// tile run side by side and a small segment's column tiles, which share its
+// gathered activation rows, follow each other (same XCD, same L2).
+// Router: column tiles (and K ranges) outermost.
 template <int MODE>
 __device__ bool tile_at(const GemmArgs& a, const SegTables& st, int lin, int total_m, Tile& t) {
   int nt = lin / total_m;
-  const int mt = lin % total_m;
+  const int mt = lin % total_m;  // router row tile
   const int nseg = a.E + a.shared;
   t.ks = 0;
   if (MODE == MODE_ROUTER) {
@@ -297,9 +304,13 @@ __device__ bool tile_at(const GemmArgs& a, const SegTables& st, int lin, int tot
     t.p0 = mt * BM;
     t.rows = min(BM, a.T - t.p0);
   } else {
-    const int seg = __builtin_amdgcn_readfirstlane(find_segment(st, nseg, mt));
+    const int seg = __builtin_amdgcn_readfirstlane(find_segment(st, nseg, lin, a.n_tiles));
+    const int r0 = __builtin_amdgcn_readfirstlane(st.tpre[seg]);
+    const int nr = __builtin_amdgcn_readfirstlane(st.tpre[seg + 1]) - r0;  // row tiles of the segment
+    const int local = lin - r0 * a.n_tiles;
+    nt = local / nr;
     t.seg = seg;
-    t.p0 = __builtin_amdgcn_readfirstlane(st.off[seg] + (mt - st.tpre[seg]) * BM);
+    t.p0 = __builtin_amdgcn_readfirstlane(st.off[seg]) + (local % nr) * BM;
     t.rows = min(BM, __builtin_amdgcn_readfirstlane(st.off[seg + 1]) - t.p0);
   }
   t.sh = MODE != MODE_ROUTER && t.seg == a.E;
