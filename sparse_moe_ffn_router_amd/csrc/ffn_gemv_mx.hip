@@ -1,12 +1,13 @@
 // Few-token expert kernels for MXFP4 experts (bf16 activations).
 //
 // MXFP4 rows are a quarter of the bytes of the bf16 activation rows they
-// multiply, so here a workgroup owns many rows of one expert segment (32 row
-// pairs, or 64 output rows) and stages the segment's activation rows in LDS
-// once, up to 8 at a time; a group of 8 lanes streams one row (pair) in
+// multiply, so here a workgroup owns many rows of one expert segment (64 row
+// pairs, or 128 output rows) and stages the segment's activation rows in LDS
+// once, up to 8 at a time; a group of 4 lanes streams one row (pair) in
 // 16-byte pieces (one 32-element block with its E8M0 exponent each), 4
-// pieces in flight plus the next 4 prefetched, decoding each block to bf16
-// in registers with the scaled fp4 conversion.  The shared expert, when a
+// pieces in flight plus the next 4 prefetched (the first 4 issued before
+// the activations are staged), decoding each block to bf16 in registers
+// with the scaled fp4 conversion.  The shared expert, when a
 // layer has one, keeps bf16 weights and runs through the same kernels.
 //
 // Sources: "Phase 19: MoE - gpt-oss-20b", section 2 Experts (interleaved
@@ -19,8 +20,17 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kGroup = 8;                          // lanes per row pair
-constexpr int kPairsPerBlock = kThreads / kGroup;  // 32
+// Lanes per row pair: 4 (64 row pairs per workgroup) measured fastest
+// against 2, 8 and 16 at the gpt-oss MXFP4 T = 16 shape -- fewer, larger
+// workgroups spread the activation staging over more weight bytes.
+constexpr int kGroup = 4;
+constexpr int kPairsPerBlock = kThreads / kGroup;  // 64
+// Sum over each group of kGroup lanes, result in every lane of the group.
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  return v;
+}
 constexpr int kStage = 8;                          // activation rows staged at once
 constexpr int kU = 4;                              // pieces per row per pipeline step
 
@@ -92,33 +102,51 @@ template <> __device__ __forceinline__ void xstore<uint16_t>(uint16_t* p, size_t
   p[i] = (uint16_t)f32_to_bf16(v);
 }
 
+// The first kU pieces of a row pair (and their exponents), this lane's share.
+struct First {
+  uint4 w0[kU], w1[kU];
+  uint8_t c0[kU], c1[kU];
+};
+template <int WK>
+__device__ __forceinline__ void fetch_pieces(const uint4* r0, const uint4* r1, const uint8_t* s0, const uint8_t* s1,
+                                             int npieces, int pc, uint4 (&a)[kU], uint4 (&b)[kU], uint8_t (&sa)[kU],
+                                             uint8_t (&sb)[kU]) {
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const int q = pc + u * kGroup;
+    const bool ok = q < npieces;
+    a[u] = ok ? r0[q] : make_uint4(0, 0, 0, 0);
+    b[u] = ok ? r1[q] : make_uint4(0, 0, 0, 0);
+    if (WK == W_MXFP4) {
+      sa[u] = ok ? s0[q] : 0;
+      sb[u] = ok ? s1[q] : 0;
+    }
+  }
+}
+
 // acc[r][i] += row r . xs[i] over K inputs, this lane's share (pieces
-// lig, lig+8, ...).  Rows are streamed with the next kU pieces prefetched.
+// lig, lig+8, ...).  Rows are streamed with the next kU pieces prefetched;
+// the first kU pieces come in `first` (loaded before the activations were
+// staged, so their latency overlaps the staging).
 template <typename XT, int WK, int NT>
 __device__ __forceinline__ void rows2_dot(const uint4* r0, const uint4* r1, const uint8_t* s0, const uint8_t* s1,
-                                          const XT* xs, int K, int lig, float (&acc)[2][kStage]) {
+                                          const XT* xs, int K, int lig, const First& first,
+                                          float (&acc)[2][kStage]) {
   using P = Piece<WK>;
   const int npieces = K / P::kElems;
   uint4 w0[kU], w1[kU];
   uint8_t c0[kU], c1[kU];
-  auto fetch = [&](int pc, uint4 (&a)[kU], uint4 (&b)[kU], uint8_t (&sa)[kU], uint8_t (&sb)[kU]) {
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int q = pc + u * kGroup;
-      const bool ok = q < npieces;
-      a[u] = ok ? r0[q] : make_uint4(0, 0, 0, 0);
-      b[u] = ok ? r1[q] : make_uint4(0, 0, 0, 0);
-      if (WK == W_MXFP4) {
-        sa[u] = ok ? s0[q] : 0;
-        sb[u] = ok ? s1[q] : 0;
-      }
-    }
-  };
-  fetch(lig, w0, w1, c0, c1);
+  for (int u = 0; u < kU; ++u) {
+    w0[u] = first.w0[u];
+    w1[u] = first.w1[u];
+    c0[u] = first.c0[u];
+    c1[u] = first.c1[u];
+  }
   for (int pc = lig; pc < npieces; pc += kU * kGroup) {
     uint4 n0[kU], n1[kU];
     uint8_t d0[kU], d1[kU];
-    fetch(pc + kU * kGroup, n0, n1, d0, d1);
+    fetch_pieces<WK>(r0, r1, s0, s1, npieces, pc + kU * kGroup, n0, n1, d0, d1);
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int q = pc + u * kGroup;
@@ -145,17 +173,17 @@ __device__ __forceinline__ void rows2_dot(const uint4* r0, const uint4* r1, cons
 
 template <typename XT, int WK>
 __device__ __forceinline__ void rows2_dot_n(int nt, const uint4* r0, const uint4* r1, const uint8_t* s0,
-                                            const uint8_t* s1, const XT* xs, int K, int lig,
+                                            const uint8_t* s1, const XT* xs, int K, int lig, const First& f,
                                             float (&acc)[2][kStage]) {
   switch (nt) {
-    case 1: rows2_dot<XT, WK, 1>(r0, r1, s0, s1, xs, K, lig, acc); break;
-    case 2: rows2_dot<XT, WK, 2>(r0, r1, s0, s1, xs, K, lig, acc); break;
-    case 3: rows2_dot<XT, WK, 3>(r0, r1, s0, s1, xs, K, lig, acc); break;
-    case 4: rows2_dot<XT, WK, 4>(r0, r1, s0, s1, xs, K, lig, acc); break;
-    case 5: rows2_dot<XT, WK, 5>(r0, r1, s0, s1, xs, K, lig, acc); break;
-    case 6: rows2_dot<XT, WK, 6>(r0, r1, s0, s1, xs, K, lig, acc); break;
-    case 7: rows2_dot<XT, WK, 7>(r0, r1, s0, s1, xs, K, lig, acc); break;
-    default: rows2_dot<XT, WK, 8>(r0, r1, s0, s1, xs, K, lig, acc); break;
+    case 1: rows2_dot<XT, WK, 1>(r0, r1, s0, s1, xs, K, lig, f, acc); break;
+    case 2: rows2_dot<XT, WK, 2>(r0, r1, s0, s1, xs, K, lig, f, acc); break;
+    case 3: rows2_dot<XT, WK, 3>(r0, r1, s0, s1, xs, K, lig, f, acc); break;
+    case 4: rows2_dot<XT, WK, 4>(r0, r1, s0, s1, xs, K, lig, f, acc); break;
+    case 5: rows2_dot<XT, WK, 5>(r0, r1, s0, s1, xs, K, lig, f, acc); break;
+    case 6: rows2_dot<XT, WK, 6>(r0, r1, s0, s1, xs, K, lig, f, acc); break;
+    case 7: rows2_dot<XT, WK, 7>(r0, r1, s0, s1, xs, K, lig, f, acc); break;
+    default: rows2_dot<XT, WK, 8>(r0, r1, s0, s1, xs, K, lig, f, acc); break;
   }
 }
 
@@ -180,7 +208,7 @@ struct GateUpArgs {
 };
 
 // h[p][f] = act(gate row f . x_t, up row f . x_t) for every sorted position
-// p of the block's expert segment.  Grid: (segment slot, tile of 32 features).
+// p of the block's expert segment.  Grid: (segment slot, tile of kPairsPerBlock features).
 template <typename XT, int WK>
 __global__ __launch_bounds__(kThreads) void k_gateup_gemv_mx(GateUpArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -222,9 +250,23 @@ __global__ __launch_bounds__(kThreads) void k_gateup_gemv_mx(GateUpArgs a) {
     bu = xscalar<XT>((const XT*)a.gate_up_b, (size_t)e * 2 * a.F + 2 * fr + 1);
   }
   const int xpieces = a.H * (int)sizeof(XT) / 16;  // 16-byte pieces per x row
+  // the first weight pieces go out before the activations are staged
+  const bool plain = sh || WK != W_MXFP4;  // bf16 (or fp32) rows
+  const int npc = plain ? a.H / Piece<WS>::kElems : a.H / Piece<WK>::kElems;
+  First first;
+  if (plain)
+    fetch_pieces<WS>((const uint4*)rg, (const uint4*)ru, sg, su, npc, lig, first.w0, first.w1, first.c0, first.c1);
+  else
+    fetch_pieces<WK>((const uint4*)rg, (const uint4*)ru, sg, su, npc, lig, first.w0, first.w1, first.c0, first.c1);
   for (int tb = 0; tb < n; tb += kStage) {
     const int nt = min(kStage, n - tb);
-    if (tb) __syncthreads();
+    if (tb) {
+      __syncthreads();
+      if (plain)
+        fetch_pieces<WS>((const uint4*)rg, (const uint4*)ru, sg, su, npc, lig, first.w0, first.w1, first.c0, first.c1);
+      else
+        fetch_pieces<WK>((const uint4*)rg, (const uint4*)ru, sg, su, npc, lig, first.w0, first.w1, first.c0, first.c1);
+    }
     for (int i = threadIdx.x; i < nt * xpieces; i += kThreads) {
       const int j = i / xpieces, q = i - j * xpieces;
       const int sa = a.sorted_assign[p0 + tb + j];
@@ -237,19 +279,19 @@ __global__ __launch_bounds__(kThreads) void k_gateup_gemv_mx(GateUpArgs a) {
     for (int r = 0; r < 2; ++r)
 #pragma unroll
       for (int i = 0; i < kStage; ++i) acc[r][i] = 0.f;
-    if (sh || WK != W_MXFP4)
-      rows2_dot_n<XT, WS>(nt, (const uint4*)rg, (const uint4*)ru, sg, su, xs, a.H, lig, acc);
+    if (plain)
+      rows2_dot_n<XT, WS>(nt, (const uint4*)rg, (const uint4*)ru, sg, su, xs, a.H, lig, first, acc);
     else
-      rows2_dot_n<XT, WK>(nt, (const uint4*)rg, (const uint4*)ru, sg, su, xs, a.H, lig, acc);
+      rows2_dot_n<XT, WK>(nt, (const uint4*)rg, (const uint4*)ru, sg, su, xs, a.H, lig, first, acc);
 #pragma unroll
     for (int i = 0; i < kStage; ++i) {
-      acc[0][i] = group8_sum(acc[0][i]);
-      acc[1][i] = group8_sum(acc[1][i]);
+      acc[0][i] = group_sum(acc[0][i]);
+      acc[1][i] = group_sum(acc[1][i]);
     }
     if (active) {
 #pragma unroll
       for (int i = 0; i < kStage; ++i) {
-        if (i < nt && i == lig) {
+        if (i < nt && i % kGroup == lig) {
           float hv;
           if (a.oai && !sh) {
             const float g = fminf(acc[0][i] + bg, a.limit);
@@ -282,7 +324,8 @@ struct DownArgs {
 
 // y[a][o] = down row o . h[p] (+ bias) for every sorted position p of the
 // segment, written at the row of its assignment id a.  Grid: (segment slot,
-// tile of 64 output rows); a group of 8 lanes owns rows o and o + 32.
+// tile of 2 * kPairsPerBlock output rows); a group of kGroup lanes owns rows
+// o and o + kPairsPerBlock.
 template <typename XT, int WK>
 __global__ __launch_bounds__(kThreads) void k_down_gemv_mx(DownArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -322,9 +365,23 @@ __global__ __launch_bounds__(kThreads) void k_down_gemv_mx(DownArgs a) {
     b1 = xscalar<XT>((const XT*)a.down_b, (size_t)e * a.H + q1);
   }
   const int hpieces = Fe * (int)sizeof(XT) / 16;
+  // the first weight pieces go out before the activations are staged
+  const bool plain = sh || WK != W_MXFP4;
+  const int npc = plain ? Fe / Piece<WS>::kElems : Fe / Piece<WK>::kElems;
+  First first;
+  if (plain)
+    fetch_pieces<WS>((const uint4*)r0, (const uint4*)r1, s0, s1, npc, lig, first.w0, first.w1, first.c0, first.c1);
+  else
+    fetch_pieces<WK>((const uint4*)r0, (const uint4*)r1, s0, s1, npc, lig, first.w0, first.w1, first.c0, first.c1);
   for (int tb = 0; tb < n; tb += kStage) {
     const int nt = min(kStage, n - tb);
-    if (tb) __syncthreads();
+    if (tb) {
+      __syncthreads();
+      if (plain)
+        fetch_pieces<WS>((const uint4*)r0, (const uint4*)r1, s0, s1, npc, lig, first.w0, first.w1, first.c0, first.c1);
+      else
+        fetch_pieces<WK>((const uint4*)r0, (const uint4*)r1, s0, s1, npc, lig, first.w0, first.w1, first.c0, first.c1);
+    }
     for (int i = threadIdx.x; i < nt * hpieces; i += kThreads)
       reinterpret_cast<uint4*>(hs)[i] = reinterpret_cast<const uint4*>(hbase + (size_t)tb * Fe)[i];
     __syncthreads();
@@ -334,17 +391,17 @@ __global__ __launch_bounds__(kThreads) void k_down_gemv_mx(DownArgs a) {
 #pragma unroll
       for (int i = 0; i < kStage; ++i) acc[r][i] = 0.f;
     if (sh || WK != W_MXFP4)
-      rows2_dot_n<XT, WS>(nt, (const uint4*)r0, (const uint4*)r1, s0, s1, hs, Fe, lig, acc);
+      rows2_dot_n<XT, WS>(nt, (const uint4*)r0, (const uint4*)r1, s0, s1, hs, Fe, lig, first, acc);
     else
-      rows2_dot_n<XT, WK>(nt, (const uint4*)r0, (const uint4*)r1, s0, s1, hs, Fe, lig, acc);
+      rows2_dot_n<XT, WK>(nt, (const uint4*)r0, (const uint4*)r1, s0, s1, hs, Fe, lig, first, acc);
 #pragma unroll
     for (int i = 0; i < kStage; ++i) {
-      acc[0][i] = group8_sum(acc[0][i]);
-      acc[1][i] = group8_sum(acc[1][i]);
+      acc[0][i] = group_sum(acc[0][i]);
+      acc[1][i] = group_sum(acc[1][i]);
     }
 #pragma unroll
     for (int i = 0; i < kStage; ++i)
-      if (i < nt && i == lig) {
+      if (i < nt && i % kGroup == lig) {
         const int asg = a.sorted_assign[p0 + tb + i];
         if (o0 < a.H) a.y[(size_t)asg * a.H + o0] = acc[0][i] + b0;
         if (o1 < a.H) a.y[(size_t)asg * a.H + o1] = acc[1][i] + b1;
