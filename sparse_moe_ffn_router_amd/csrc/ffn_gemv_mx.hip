@@ -32,7 +32,7 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 constexpr int kStage = 8;                          // activation rows staged at once
-constexpr int kU = 4;                              // pieces per row per pipeline step
+constexpr int kU = 2;                              // pieces per row per pipeline step
 
 enum { W_F32 = 0, W_BF16 = 1, W_MXFP4 = 2 };
 

@@ -161,19 +161,31 @@ __global__ __launch_bounds__(kThreadsBig) void k_perm_scan(int32_t* __restrict__
                                                            int32_t* __restrict__ sorted_assign,
                                                            int32_t* __restrict__ assign_pos) {
   __shared__ int wsum[kThreadsBig / kWave];
+  constexpr int kU = 8;  // block counts loaded per round trip
   const int tid = threadIdx.x;
   int tot = 0;
   if (tid < E)
-    for (int g = 0; g < G; ++g) tot += counts[(size_t)g * E + tid];
+    for (int g0 = 0; g0 < G; g0 += kU) {
+      int c[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) c[u] = g0 + u < G ? counts[(size_t)(g0 + u) * E + tid] : 0;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) tot += c[u];
+    }
   int all;
   const int excl = block_excl_scan(tid < E ? tot : 0, wsum, &all);
   if (tid < E) {
     offsets[tid] = excl;
     int run = excl;
-    for (int g = 0; g < G; ++g) {
-      const int c = counts[(size_t)g * E + tid];
-      counts[(size_t)g * E + tid] = run;
-      run += c;
+    for (int g0 = 0; g0 < G; g0 += kU) {
+      int c[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) c[u] = g0 + u < G ? counts[(size_t)(g0 + u) * E + tid] : 0;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (g0 + u < G) counts[(size_t)(g0 + u) * E + tid] = run;
+        run += c[u];
+      }
     }
   }
   const int n = T * k;
