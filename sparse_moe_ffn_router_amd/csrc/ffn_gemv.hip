@@ -10,8 +10,9 @@
 // each (row, token) dot product across the wavefront.  Many short
 // wavefronts, each with one burst of loads, keep HBM busier than long
 // software-pipelined ones for this access pattern; there is no LDS and no
-// barrier.  Activation rows are processed two tokens at a time, the next
-// pair prefetched while the current one is reduced.
+// barrier.  Activation rows are processed one token at a time, the next
+// one prefetched while the current one is reduced.  Weight loads carry the
+// streaming cache policy (each byte is read once).
 //
 // These kernels serve fp32 and bf16 experts; MXFP4 experts have their own
 // (ffn_gemv_mx.hip).
@@ -61,8 +62,10 @@ template <> struct Wp<W_F32> {
 __host__ __device__ constexpr int rows_per_wave(int np) { return np >= 6 ? 1 : 8 / np; }
 // gate/up: a row pair per feature
 __host__ __device__ constexpr int gateup_rows_per_wave(int np) { return np >= 6 ? 1 : np == 4 ? 2 : 4; }
-// tokens per register chunk
-constexpr int kCh = 2;
+// tokens per register chunk: one keeps the gate/up kernel at 117 VGPRs (4
+// waves per SIMD) and the down kernel at 61 (8), so more weight bytes are in
+// flight per CU (two: 3 and 7 waves, 1.5% slower layer)
+constexpr int kCh = 1;
 
 struct Seg {
   int e, p0, n;
@@ -207,8 +210,8 @@ __global__ __launch_bounds__(kWaves * kWave) void k_gateup_gemv(GateUpArgs a, co
     for (int p = 0; p < NP; ++p) {
       const int q = lane + p * kWave;
       const uint32_t off = q < P ? (uint32_t)(r * stride + q * 16) : kOutOfRange;
-      G[r][p] = buf_load16(rg, off, 0);
-      U[r][p] = buf_load16(ru, off, 0);
+      G[r][p] = buf_load16_once(rg, off, 0);
+      U[r][p] = buf_load16_once(ru, off, 0);
     }
   const size_t xrb = (size_t)a.H * sizeof(XT);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)((size_t)a.T * xrb));
@@ -326,7 +329,7 @@ __global__ __launch_bounds__(kWaves * kWave) void k_down_gemv(DownArgs a, const 
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const int q = lane + p * kWave;
-      W[r][p] = buf_load16(rw, q < P ? (uint32_t)(r * rb + q * 16) : kOutOfRange, 0);
+      W[r][p] = buf_load16_once(rw, q < P ? (uint32_t)(r * rb + q * 16) : kOutOfRange, 0);
     }
   const size_t hrb = (size_t)Fe * sizeof(XT);
   const XT* hseg = sh ? (const XT*)a.h + (size_t)nas * a.F + (size_t)(sg.p0 - nas) * a.Fs
