@@ -101,9 +101,21 @@ __device__ Seg find_segment(const int32_t* __restrict__ off, int nseg, int s) {
   return Seg{-1, 0, 0};
 }
 
-// The segment a workgroup works on: the blockIdx.x-th non-empty one.
-__device__ __forceinline__ Seg block_segment(const int32_t* off, int nseg) {
-  const Seg s = find_segment(off, nseg, blockIdx.x);
+// The segment a workgroup works on.  Workgroups are dispatched in blockIdx
+// order, x fastest, so with the segment slot in blockIdx.y each segment's
+// row groups go out together, and slot 0 is the shared expert (the segment
+// with the most tokens, hence the longest compute), so it starts first and
+// does not trail at the end; slot s > 0 is the (s-1)-th non-empty routed
+// segment (the s-th without a shared expert).
+__device__ __forceinline__ Seg block_segment(const int32_t* off, int E, int shared) {
+  const int slot = blockIdx.y;
+  Seg s;
+  if (shared && slot == 0) {
+    const int p0 = off[E];
+    s = Seg{E, p0, off[E + 1] - p0};
+  } else {
+    s = find_segment(off, E, slot - shared);
+  }
   return Seg{__builtin_amdgcn_readfirstlane(s.e), __builtin_amdgcn_readfirstlane(s.p0),
              __builtin_amdgcn_readfirstlane(s.n)};
 }
@@ -152,8 +164,8 @@ struct GateUpArgs {
 };
 
 // h[p][f] = act(gate row f . x_t, up row f . x_t) for every sorted position
-// p of the workgroup's segment.  Grid: (segment slot, groups of
-// kWaves * RPW features).
+// p of the workgroup's segment.  Grid: (groups of kWaves * RPW features,
+// segment slot).
 // sorted_assign is passed on its own, read-only and unaliased, so the
 // uniform reads of it are scalar loads that never wait behind weight loads.
 template <typename XT, int WK, int NP>
@@ -162,11 +174,11 @@ __global__ __launch_bounds__(kWaves * kWave) void k_gateup_gemv(GateUpArgs a, co
   constexpr int XQ = Wp<WK>::kXq;
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const Seg sg = block_segment(a.offsets, a.E + a.shared);
+  const Seg sg = block_segment(a.offsets, a.E, a.shared);
   if (sg.e < 0) return;
   const bool sh = sg.e == a.E;
   const int Fe = sh ? a.Fs : a.F;
-  const int f0 = (blockIdx.y * kWaves + wv) * RPW;
+  const int f0 = (blockIdx.x * kWaves + wv) * RPW;
   if (f0 >= Fe) return;
   const int nr = min(RPW, Fe - f0);
   const size_t rb = row_bytes<WK>(a.H);
@@ -288,19 +300,19 @@ struct DownArgs {
 };
 
 // y[a][o] = down row o . h[p] (+ bias) for every sorted position p of the
-// segment, written at the row of its assignment id a.  Grid: (segment slot,
-// groups of kWaves * RPW output rows).
+// segment, written at the row of its assignment id a.  Grid: (groups of
+// kWaves * RPW output rows, segment slot).
 template <typename XT, int WK, int NP>
 __global__ __launch_bounds__(kWaves * kWave) void k_down_gemv(DownArgs a, const int32_t* __restrict__ sorted) {
   constexpr int RPW = rows_per_wave(NP);
   constexpr int XQ = Wp<WK>::kXq;
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const Seg sg = block_segment(a.offsets, a.E + a.shared);
+  const Seg sg = block_segment(a.offsets, a.E, a.shared);
   if (sg.e < 0) return;
   const bool sh = sg.e == a.E;
   const int Fe = sh ? a.Fs : a.F;
-  const int o0 = (blockIdx.y * kWaves + wv) * RPW;
+  const int o0 = (blockIdx.x * kWaves + wv) * RPW;
   if (o0 >= a.H) return;
   const int nr = min(RPW, a.H - o0);
   const size_t rb = row_bytes<WK>(Fe);
@@ -482,7 +494,7 @@ template <typename XT, int WK, int NP> static void down_launch(dim3 g, const Dow
 static void gateup_dispatch(const moe_config* c, const GateUpArgs& a, int wdt, int nslots, int fe, hipStream_t s) {
   const int np = pieces_per_lane(row_bytes_of(wdt, c->hidden));
   const int rpw = gateup_rows_per_wave(np);
-  const dim3 grid(nslots, (fe + kWaves * rpw - 1) / (kWaves * rpw));
+  const dim3 grid((fe + kWaves * rpw - 1) / (kWaves * rpw), nslots);
   if (c->x_dtype == MOE_DTYPE_F32) {
     MOE_NP_SWITCH(gateup_launch, float, W_F32, np, grid, a, s)
   } else {
@@ -493,7 +505,7 @@ static void gateup_dispatch(const moe_config* c, const GateUpArgs& a, int wdt, i
 static void down_dispatch(const moe_config* c, const DownArgs& a, int wdt, int nslots, int cols, hipStream_t s) {
   const int np = pieces_per_lane(row_bytes_of(wdt, cols));
   const int rpw = rows_per_wave(np);
-  const dim3 grid(nslots, (c->hidden + kWaves * rpw - 1) / (kWaves * rpw));
+  const dim3 grid((c->hidden + kWaves * rpw - 1) / (kWaves * rpw), nslots);
   if (c->x_dtype == MOE_DTYPE_F32) {
     MOE_NP_SWITCH(down_launch, float, W_F32, np, grid, a, s)
   } else {

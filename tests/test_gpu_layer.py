@@ -34,6 +34,8 @@ LAYERS = [
     ("gptoss20b_mxfp4", 16, None, dict(E=8, H=320, F=192, k=2)),  # fused down + combine, MXFP4 rows
     ("gptoss20b_bf16", 2, None, {}),                          # fused down + combine, 6 pieces per lane
     ("gptoss20b_mxfp4", 2, None, {}),                         # fused down + combine, 2 pieces per lane
+    ("qwen35moe_decode", 16, None, dict(E=512, k=32, H=64, F=64, Fs=64)),  # largest fused gating + permutation
+    ("qwen35moe_decode", 3, None, dict(E=40, k=5, H=64, F=64, Fs=64)),     # E, k not powers of two
 ]
 
 
