@@ -53,6 +53,16 @@ __device__ int find_segment(const int32_t* __restrict__ offsets, int nseg, int s
   return -1;
 }
 
+// Segment of a workgroup: the grid is (row tile, segment slot), so each
+// segment's row tiles are dispatched together; slot 0 is the shared expert
+// (the segment with the most tokens, started first), slot s > 0 the
+// (s-1)-th non-empty routed segment (the s-th without a shared expert).
+__device__ __forceinline__ int slot_segment(const int32_t* __restrict__ offsets, int E, int shared) {
+  const int slot = blockIdx.y;
+  if (shared) return slot == 0 ? E : find_segment(offsets, E, slot - 1);
+  return find_segment(offsets, E, slot);
+}
+
 template <int WK> struct Piece;
 
 // bf16 weights: 8 elements per 16-byte piece, products summed in pairs.
@@ -208,19 +218,18 @@ struct GateUpArgs {
 };
 
 // h[p][f] = act(gate row f . x_t, up row f . x_t) for every sorted position
-// p of the block's expert segment.  Grid: (segment slot, tile of kPairsPerBlock features).
+// p of the block's expert segment.  Grid: (tile of kPairsPerBlock features, segment slot).
 template <typename XT, int WK>
 __global__ __launch_bounds__(kThreads) void k_gateup_gemv_mx(GateUpArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   XT* xs = reinterpret_cast<XT*>(smem);
-  const int nseg = a.E + a.shared;
-  const int e = find_segment(a.offsets, nseg, blockIdx.x);
+  const int e = slot_segment(a.offsets, a.E, a.shared);
   if (e < 0) return;
   const bool sh = e == a.E;
   const int Fe = sh ? a.Fs : a.F;
-  if (blockIdx.y * kPairsPerBlock >= Fe) return;
+  if (blockIdx.x * kPairsPerBlock >= Fe) return;
   const int grp = threadIdx.x / kGroup, lig = threadIdx.x & (kGroup - 1);
-  const int f = blockIdx.y * kPairsPerBlock + grp;
+  const int f = blockIdx.x * kPairsPerBlock + grp;
   const bool active = f < Fe;
   const int fr = active ? f : Fe - 1;
   const uint8_t *rg, *ru, *sg = nullptr, *su = nullptr;
@@ -323,19 +332,18 @@ struct DownArgs {
 };
 
 // y[a][o] = down row o . h[p] (+ bias) for every sorted position p of the
-// segment, written at the row of its assignment id a.  Grid: (segment slot,
-// tile of 2 * kPairsPerBlock output rows); a group of kGroup lanes owns rows
+// segment, written at the row of its assignment id a.  Grid: (tile of
+// 2 * kPairsPerBlock output rows, segment slot); a group of kGroup lanes owns rows
 // o and o + kPairsPerBlock.
 template <typename XT, int WK>
 __global__ __launch_bounds__(kThreads) void k_down_gemv_mx(DownArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   XT* hs = reinterpret_cast<XT*>(smem);
-  const int nseg = a.E + a.shared;
-  const int e = find_segment(a.offsets, nseg, blockIdx.x);
+  const int e = slot_segment(a.offsets, a.E, a.shared);
   if (e < 0) return;
   const bool sh = e == a.E;
   const int Fe = sh ? a.Fs : a.F;
-  const int obase = blockIdx.y * 2 * kPairsPerBlock;
+  const int obase = blockIdx.x * 2 * kPairsPerBlock;
   if (obase >= a.H) return;
   const int grp = threadIdx.x / kGroup, lig = threadIdx.x & (kGroup - 1);
   const int o0 = obase + grp, o1 = obase + kPairsPerBlock + grp;
@@ -434,7 +442,7 @@ hipError_t launch_expert_ffn_mx(const moe_config* c, const moe_weights* w, const
   a.T = T; a.k = c->top_k; a.H = c->hidden; a.E = c->n_expert; a.F = c->expert_ff; a.Fs = c->shared_ff;
   a.shared = c->shared_ff > 0; a.oai = 1; a.alpha = c->act_alpha; a.limit = c->act_limit;
   const int fmax = c->expert_ff > c->shared_ff ? c->expert_ff : c->shared_ff;
-  dim3 grid(max_segments_mx(c, T), (fmax + kPairsPerBlock - 1) / kPairsPerBlock);
+  dim3 grid((fmax + kPairsPerBlock - 1) / kPairsPerBlock, max_segments_mx(c, T));
   const size_t lds = stage_rows_mx(T) * c->hidden * 2;
   k_gateup_gemv_mx<uint16_t, W_MXFP4><<<grid, kThreads, lds, s>>>(a);
   return hipGetLastError();
@@ -453,7 +461,7 @@ hipError_t launch_down_mx(const moe_config* c, const moe_weights* w, const void*
   a.y = y;
   a.T = T; a.k = c->top_k; a.H = c->hidden; a.E = c->n_expert; a.F = c->expert_ff; a.Fs = c->shared_ff;
   a.shared = c->shared_ff > 0;
-  dim3 grid(max_segments_mx(c, T), (c->hidden + 2 * kPairsPerBlock - 1) / (2 * kPairsPerBlock));
+  dim3 grid((c->hidden + 2 * kPairsPerBlock - 1) / (2 * kPairsPerBlock), max_segments_mx(c, T));
   const int fmax = c->expert_ff > c->shared_ff ? c->expert_ff : c->shared_ff;
   const size_t lds = stage_rows_mx(T) * fmax * 2;
   k_down_gemv_mx<uint16_t, W_MXFP4><<<grid, kThreads, lds, s>>>(a);
