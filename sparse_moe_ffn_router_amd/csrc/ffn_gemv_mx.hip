@@ -1,14 +1,15 @@
 // Few-token expert kernels for MXFP4 experts (bf16 activations).
 //
-// MXFP4 rows are a quarter of the bytes of the bf16 activation rows they
-// multiply, so here a workgroup owns many rows of one expert segment (64 row
-// pairs, or 128 output rows) and stages the segment's activation rows in LDS
-// once, up to 8 at a time; a group of 4 lanes streams one row (pair) in
-// 16-byte pieces (one 32-element block with its E8M0 exponent each), 4
-// pieces in flight plus the next 4 prefetched (the first 4 issued before
-// the activations are staged), decoding each block to bf16 in registers
-// with the scaled fp4 conversion.  The shared expert, when a
-// layer has one, keeps bf16 weights and runs through the same kernels.
+// Routed segments run through the burst kernels (k_gateup_mx_burst,
+// k_down_mx_burst): a wavefront owns 4 row pairs of one segment, 16 lanes
+// per pair, and issues the loads of all its pieces (16 bytes = one
+// 32-element block, with its E8M0 exponent) at once; the workgroup then
+// stages the segment's activation rows in LDS and every piece is decoded
+// to bf16 once, with the scaled fp4 conversion, and multiplied with each
+// staged token.  The shared expert, when a layer has one, keeps bf16
+// weights and runs through the streaming kernels (k_gateup_gemv_mx,
+// k_down_gemv_mx): 64 row pairs per workgroup, a group of 4 lanes streams
+// one row pair with two 16-byte pieces per row in flight.
 //
 // Sources: "Phase 19: MoE - gpt-oss-20b", section 2 Experts (interleaved
 // gate_up with bias, clamps, (up+1) * gate * sigmoid(alpha gate), down +
@@ -417,15 +418,278 @@ __global__ __launch_bounds__(kThreads) void k_down_gemv_mx(DownArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Routed MXFP4 segments: burst kernels.  A wavefront owns 4 row pairs of one
+// segment, 16 lanes per pair; a lane issues the loads of all its pieces of
+// both rows at once (pieces l, l + 16, ... of a row; 6 per row at K = 2880,
+// i.e. 11.5 KiB in flight per wavefront), like the bf16 decode kernels, and
+// only then does the workgroup stage the segment's activation rows in LDS
+// (kBStage at a time; the weights stay in registers for every batch).  Each
+// piece is decoded once and multiplied with every staged token; the (row,
+// token) sums are reduced over the pair's 16 lanes with DPP.  Against the
+// streaming kernels above this keeps about three times the weight bytes in
+// flight per CU.
+constexpr int kBWaves = 4;
+constexpr int kBThreads = kBWaves * kWave;
+constexpr int kBLanes = 16;                   // lanes per row pair
+constexpr int kBPairs = kBThreads / kBLanes;  // row pairs per workgroup
+constexpr int kBStage = 4;                    // activation rows staged at once
+
+// The s-th non-empty routed segment (blockIdx.y), or -1.
+__device__ __forceinline__ int routed_segment(const int32_t* __restrict__ offsets, int E) {
+  return __builtin_amdgcn_readfirstlane(find_segment(offsets, E, blockIdx.y));
+}
+
+// Both rows' pieces of this lane (codes and E8M0 exponents).  The buffer
+// descriptors are wave-uniform (they span the wavefront's rows; a
+// per-lane descriptor would make every load a loop over the distinct
+// descriptors); row r of this lane's pair starts at byte co[r] of rc and at
+// byte so[r] of rs (kOutOfRange: no such row).  Pieces past P read zeros.
+template <int NPL>
+__device__ __forceinline__ void burst_load(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs, const uint32_t (&co)[2],
+                                           const uint32_t (&so)[2], int P, int l, uint4 (&w)[2][NPL],
+                                           uint32_t (&sc)[2][NPL]) {
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int p = l + kBLanes * j;
+      const bool ok = p < P && co[r] != kOutOfRange;
+      w[r][j] = buf_load16_once(rc, ok ? co[r] + (uint32_t)p * 16 : kOutOfRange, 0);
+      sc[r][j] = buf_load_u8(rs, ok ? so[r] + (uint32_t)p : kOutOfRange, 0);
+    }
+}
+
+// acc[r][i] += row r . xs[i], this lane's pieces, NT staged tokens of K inputs.
+template <int NPL, int NT>
+__device__ __forceinline__ void burst_dot(const uint4 (&w)[2][NPL], const uint32_t (&sc)[2][NPL],
+                                          const uint16_t* xs, int K, int P, int l, float (&acc)[2][kBStage]) {
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const int p = l + kBLanes * j;
+    if (p < P) {
+      const float s0 = e8m0_to_f32(sc[0][j]), s1 = e8m0_to_f32(sc[1][j]);
+      const uint32_t c0[4] = {w[0][j].x, w[0][j].y, w[0][j].z, w[0][j].w};
+      const uint32_t c1[4] = {w[1][j].x, w[1][j].y, w[1][j].z, w[1][j].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bf16x2_t g0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c0[q], s0, 0);
+        const bf16x2_t g1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c0[q], s0, 1);
+        const bf16x2_t g2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c0[q], s0, 2);
+        const bf16x2_t g3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c0[q], s0, 3);
+        const bf16x2_t u0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c1[q], s1, 0);
+        const bf16x2_t u1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c1[q], s1, 1);
+        const bf16x2_t u2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c1[q], s1, 2);
+        const bf16x2_t u3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c1[q], s1, 3);
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+          const uint4 xv = reinterpret_cast<const uint4*>(xs + (size_t)i * K + (size_t)p * 32)[q];
+          const bf16x2_t x0 = __builtin_bit_cast(bf16x2_t, xv.x), x1 = __builtin_bit_cast(bf16x2_t, xv.y);
+          const bf16x2_t x2 = __builtin_bit_cast(bf16x2_t, xv.z), x3 = __builtin_bit_cast(bf16x2_t, xv.w);
+          float a0 = acc[0][i], a1 = acc[1][i];
+          a0 = __builtin_amdgcn_fdot2_f32_bf16(g0, x0, a0, false);
+          a1 = __builtin_amdgcn_fdot2_f32_bf16(u0, x0, a1, false);
+          a0 = __builtin_amdgcn_fdot2_f32_bf16(g1, x1, a0, false);
+          a1 = __builtin_amdgcn_fdot2_f32_bf16(u1, x1, a1, false);
+          a0 = __builtin_amdgcn_fdot2_f32_bf16(g2, x2, a0, false);
+          a1 = __builtin_amdgcn_fdot2_f32_bf16(u2, x2, a1, false);
+          a0 = __builtin_amdgcn_fdot2_f32_bf16(g3, x3, a0, false);
+          a1 = __builtin_amdgcn_fdot2_f32_bf16(u3, x3, a1, false);
+          acc[0][i] = a0;
+          acc[1][i] = a1;
+        }
+      }
+    }
+  }
+}
+
+template <int NPL>
+__device__ __forceinline__ void burst_dot_n(int nt, const uint4 (&w)[2][NPL], const uint32_t (&sc)[2][NPL],
+                                            const uint16_t* xs, int K, int P, int l, float (&acc)[2][kBStage]) {
+  switch (nt) {
+    case 1: burst_dot<NPL, 1>(w, sc, xs, K, P, l, acc); break;
+    case 2: burst_dot<NPL, 2>(w, sc, xs, K, P, l, acc); break;
+    case 3: burst_dot<NPL, 3>(w, sc, xs, K, P, l, acc); break;
+    default: burst_dot<NPL, 4>(w, sc, xs, K, P, l, acc); break;
+  }
+}
+
+// Stage activation rows [tb, tb + nt) of the segment (row i of src_row(i))
+// into xs, 16 bytes per thread per step.
+template <typename RowOf>
+__device__ __forceinline__ void stage_rows(uint16_t* xs, int nt, int K, RowOf src_row) {
+  const int pieces = K / 8;  // 16-byte pieces per row
+  for (int j = 0; j < nt; ++j) {
+    const uint4* src = reinterpret_cast<const uint4*>(src_row(j));
+    uint4* dst = reinterpret_cast<uint4*>(xs + (size_t)j * K);
+    for (int q = threadIdx.x; q < pieces; q += kBThreads) dst[q] = src[q];
+  }
+}
+
+// Gate/up of the routed segments (interleaved gate_up rows 2f, 2f + 1, bias
+// and clamped activation).  Grid: (groups of kBPairs features, routed
+// segment slot).
+template <int NPL>
+__global__ __launch_bounds__(kBThreads) void k_gateup_mx_burst(GateUpArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
+  const int e = routed_segment(a.offsets, a.E);
+  if (e < 0) return;
+  const int l = threadIdx.x & (kBLanes - 1);
+  const int f = blockIdx.x * kBPairs + threadIdx.x / kBLanes;
+  if (blockIdx.x * kBPairs >= a.F) return;
+  const bool active = f < a.F;
+  const int fr = active ? f : a.F - 1;
+  const int P = a.H / 32;
+  const uint32_t rb = (uint32_t)a.H / 2;
+  // the wavefront's rows: fused rows 2 fw .. 2 F - 1 of the expert
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int fw = min((int)(blockIdx.x * kBPairs) + wv * (kWave / kBLanes), a.F - 1);
+  const size_t wrow = (size_t)e * 2 * a.F + 2 * (size_t)fw;
+  const uint32_t nrows = (uint32_t)(2 * (a.F - fw));
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc((const uint8_t*)a.gate_w + wrow * rb, nrows * rb);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + wrow * P, nrows * (uint32_t)P);
+  const uint32_t lr = (uint32_t)(2 * (fr - fw));  // this lane's first row in the wavefront's span
+  const uint32_t co[2] = {lr * rb, (lr + 1) * rb}, so[2] = {lr * (uint32_t)P, (lr + 1) * (uint32_t)P};
+  uint4 w[2][NPL];
+  uint32_t sc[2][NPL];
+  burst_load<NPL>(rc, rs, co, so, P, l, w, sc);
+  const size_t row0 = (size_t)e * 2 * a.F + 2 * (size_t)fr;
+  float bg = 0.f, bu = 0.f;
+  if (a.gate_up_b) {
+    bg = xscalar<uint16_t>((const uint16_t*)a.gate_up_b, row0);
+    bu = xscalar<uint16_t>((const uint16_t*)a.gate_up_b, row0 + 1);
+  }
+  const int p0 = a.offsets[e];
+  const int n = a.offsets[e + 1] - p0;
+  const int nas = a.T * a.k;
+  for (int tb = 0; tb < n; tb += kBStage) {
+    const int nt = min(kBStage, n - tb);
+    if (tb) __syncthreads();
+    stage_rows(xs, nt, a.H, [&](int j) {
+      const int sa = a.sorted_assign[p0 + tb + j];
+      return (const uint16_t*)a.x + (size_t)(sa / a.k) * a.H;
+    });
+    __syncthreads();
+    float acc[2][kBStage];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int i = 0; i < kBStage; ++i) acc[r][i] = 0.f;
+    burst_dot_n<NPL>(nt, w, sc, xs, a.H, P, l, acc);
+    float gs = 0.f, us = 0.f;
+#pragma unroll
+    for (int i = 0; i < kBStage; ++i) {
+      if (i < nt) {
+        const float gi = row16_sum(acc[0][i]), ui = row16_sum(acc[1][i]);
+        gs = l == i ? gi : gs;
+        us = l == i ? ui : us;
+      }
+    }
+    if (active && l < nt) {
+      const float g = fminf(gs + bg, a.limit);
+      const float u = fminf(fmaxf(us + bu, -a.limit), a.limit);
+      const float hv = (u + 1.f) * (g / (1.f + expf(-a.alpha * g)));
+      xstore<uint16_t>((uint16_t*)a.h, (size_t)(p0 + tb + l) * a.F + f, hv);
+    }
+  }
+}
+
+// Down of the routed segments: a pair is output rows 2o', 2o' + 1.  Grid:
+// (groups of kBPairs row pairs, routed segment slot).
+template <int NPL>
+__global__ __launch_bounds__(kBThreads) void k_down_mx_burst(DownArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  uint16_t* hs = reinterpret_cast<uint16_t*>(smem);
+  const int e = routed_segment(a.offsets, a.E);
+  if (e < 0) return;
+  const int l = threadIdx.x & (kBLanes - 1);
+  const int npairs = (a.H + 1) / 2;
+  const int pr = blockIdx.x * kBPairs + threadIdx.x / kBLanes;
+  if (blockIdx.x * kBPairs >= npairs) return;
+  const int o0 = 2 * min(pr, npairs - 1);
+  const bool two = o0 + 1 < a.H;  // H odd: the last pair has one row
+  const int P = a.F / 32;
+  const uint32_t rb = (uint32_t)a.F / 2;
+  // the wavefront's rows: output rows ow .. H - 1 of the expert
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int ow = 2 * min((int)(blockIdx.x * kBPairs) + wv * (kWave / kBLanes), npairs - 1);
+  const size_t wrow = (size_t)e * a.H + ow;
+  const uint32_t nrows = (uint32_t)(a.H - ow);
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc((const uint8_t*)a.down_w + wrow * rb, nrows * rb);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + wrow * P, nrows * (uint32_t)P);
+  const uint32_t lr = (uint32_t)(o0 - ow);
+  const uint32_t co[2] = {lr * rb, two ? (lr + 1) * rb : kOutOfRange};
+  const uint32_t so[2] = {lr * (uint32_t)P, two ? (lr + 1) * (uint32_t)P : kOutOfRange};
+  uint4 w[2][NPL];
+  uint32_t sc[2][NPL];
+  burst_load<NPL>(rc, rs, co, so, P, l, w, sc);
+  const size_t row0 = (size_t)e * a.H + o0;
+  float b0 = 0.f, b1 = 0.f;
+  if (a.down_b) {
+    b0 = xscalar<uint16_t>((const uint16_t*)a.down_b, row0);
+    if (two) b1 = xscalar<uint16_t>((const uint16_t*)a.down_b, row0 + 1);
+  }
+  const int p0 = a.offsets[e];
+  const int n = a.offsets[e + 1] - p0;
+  const uint16_t* hseg = (const uint16_t*)a.h + (size_t)p0 * a.F;
+  for (int tb = 0; tb < n; tb += kBStage) {
+    const int nt = min(kBStage, n - tb);
+    if (tb) __syncthreads();
+    stage_rows(hs, nt, a.F, [&](int j) { return hseg + (size_t)(tb + j) * a.F; });
+    __syncthreads();
+    float acc[2][kBStage];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int i = 0; i < kBStage; ++i) acc[r][i] = 0.f;
+    burst_dot_n<NPL>(nt, w, sc, hs, a.F, P, l, acc);
+    float y0 = 0.f, y1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < kBStage; ++i) {
+      if (i < nt) {
+        const float v0 = row16_sum(acc[0][i]), v1 = row16_sum(acc[1][i]);
+        y0 = l == i ? v0 : y0;
+        y1 = l == i ? v1 : y1;
+      }
+    }
+    if (pr < npairs && l < nt) {
+      const int asg = a.sorted_assign[p0 + tb + l];
+      a.y[(size_t)asg * a.H + o0] = y0 + b0;
+      if (two) a.y[(size_t)asg * a.H + o0 + 1] = y1 + b1;
+    }
+  }
+}
+
 }  // namespace
 
-static int max_segments_mx(const moe_config* c, int32_t T) {
+static int max_routed_mx(const moe_config* c, int32_t T) {
   const int64_t nk = (int64_t)T * c->top_k;
-  return (int)(nk < c->n_expert ? nk : c->n_expert) + (c->shared_ff > 0 ? 1 : 0);
+  return (int)(nk < c->n_expert ? nk : c->n_expert);
 }
 
 static size_t stage_rows_mx(int32_t T) { return (size_t)(T < kStage ? T : kStage); }
+static size_t stage_rows_burst(int32_t T) { return (size_t)(T < kBStage ? T : kBStage); }
 
+// Pieces per lane per row for rows of K inputs (K / 32 pieces over 16 lanes;
+// K <= 4096 gives at most 8).
+static int burst_npl(int K) {
+  const int np = (K / 32 + kBLanes - 1) / kBLanes;
+  return np <= 1 ? 1 : np <= 2 ? 2 : np <= 4 ? 4 : np <= 6 ? 6 : 8;
+}
+
+#define MOE_NPL_SWITCH(KERNEL, npl, grid, lds, s, args)                   \
+  switch (npl) {                                                          \
+    case 1: KERNEL<1><<<grid, kBThreads, lds, s>>>(args); break;          \
+    case 2: KERNEL<2><<<grid, kBThreads, lds, s>>>(args); break;          \
+    case 4: KERNEL<4><<<grid, kBThreads, lds, s>>>(args); break;          \
+    case 6: KERNEL<6><<<grid, kBThreads, lds, s>>>(args); break;          \
+    default: KERNEL<8><<<grid, kBThreads, lds, s>>>(args); break;         \
+  }
+
+// Routed segments through the burst kernel; the shared expert (bf16 rows),
+// if any, through the streaming kernel with a single segment slot (slot 0
+// is the shared expert there).
 hipError_t launch_expert_ffn_mx(const moe_config* c, const moe_weights* w, const void* x, const int32_t* offsets,
                                 const int32_t* sorted_assign, int32_t T, void* h, hipStream_t s) {
   GateUpArgs a;
@@ -441,10 +705,16 @@ hipError_t launch_expert_ffn_mx(const moe_config* c, const moe_weights* w, const
   a.h = h;
   a.T = T; a.k = c->top_k; a.H = c->hidden; a.E = c->n_expert; a.F = c->expert_ff; a.Fs = c->shared_ff;
   a.shared = c->shared_ff > 0; a.oai = 1; a.alpha = c->act_alpha; a.limit = c->act_limit;
-  const int fmax = c->expert_ff > c->shared_ff ? c->expert_ff : c->shared_ff;
-  dim3 grid((fmax + kPairsPerBlock - 1) / kPairsPerBlock, max_segments_mx(c, T));
-  const size_t lds = stage_rows_mx(T) * c->hidden * 2;
-  k_gateup_gemv_mx<uint16_t, W_MXFP4><<<grid, kThreads, lds, s>>>(a);
+  {
+    const dim3 grid((c->expert_ff + kBPairs - 1) / kBPairs, max_routed_mx(c, T));
+    const size_t lds = stage_rows_burst(T) * c->hidden * 2;
+    MOE_NPL_SWITCH(k_gateup_mx_burst, burst_npl(c->hidden), grid, lds, s, a)
+  }
+  if (a.shared) {
+    const dim3 grid((c->shared_ff + kPairsPerBlock - 1) / kPairsPerBlock, 1);
+    const size_t lds = stage_rows_mx(T) * c->hidden * 2;
+    k_gateup_gemv_mx<uint16_t, W_MXFP4><<<grid, kThreads, lds, s>>>(a);
+  }
   return hipGetLastError();
 }
 
@@ -461,11 +731,18 @@ hipError_t launch_down_mx(const moe_config* c, const moe_weights* w, const void*
   a.y = y;
   a.T = T; a.k = c->top_k; a.H = c->hidden; a.E = c->n_expert; a.F = c->expert_ff; a.Fs = c->shared_ff;
   a.shared = c->shared_ff > 0;
-  dim3 grid((c->hidden + 2 * kPairsPerBlock - 1) / (2 * kPairsPerBlock), max_segments_mx(c, T));
-  const int fmax = c->expert_ff > c->shared_ff ? c->expert_ff : c->shared_ff;
-  const size_t lds = stage_rows_mx(T) * fmax * 2;
-  k_down_gemv_mx<uint16_t, W_MXFP4><<<grid, kThreads, lds, s>>>(a);
+  {
+    const dim3 grid(((c->hidden + 1) / 2 + kBPairs - 1) / kBPairs, max_routed_mx(c, T));
+    const size_t lds = stage_rows_burst(T) * c->expert_ff * 2;
+    MOE_NPL_SWITCH(k_down_mx_burst, burst_npl(c->expert_ff), grid, lds, s, a)
+  }
+  if (a.shared) {
+    const dim3 grid((c->hidden + 2 * kPairsPerBlock - 1) / (2 * kPairsPerBlock), 1);
+    const size_t lds = stage_rows_mx(T) * c->shared_ff * 2;
+    k_down_gemv_mx<uint16_t, W_MXFP4><<<grid, kThreads, lds, s>>>(a);
+  }
   return hipGetLastError();
 }
+#undef MOE_NPL_SWITCH
 
 }  // namespace moe
