@@ -506,6 +506,7 @@ __device__ __forceinline__ void burst_dot(const uint4 (&w)[2][NPL], const uint32
 template <int NPL>
 __device__ __forceinline__ void burst_dot_n(int nt, const uint4 (&w)[2][NPL], const uint32_t (&sc)[2][NPL],
                                             const uint16_t* xs, int K, int P, int l, float (&acc)[2][kBStage]) {
+  static_assert(kBStage == 4, "one case per staged token count");
   switch (nt) {
     case 1: burst_dot<NPL, 1>(w, sc, xs, K, P, l, acc); break;
     case 2: burst_dot<NPL, 2>(w, sc, xs, K, P, l, acc); break;
