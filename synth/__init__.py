@@ -222,9 +222,11 @@ def _qwen_case(T: int, drawn: bool, seed: int = BASE_SEED, E: int = 256, H: int 
 
 
 def _gptoss_case(T: int, mxfp4: bool, seed: int = BASE_SEED, E: int = 32, H: int = 2880,
-                 F: int = 2880, k: int = 4, only=None) -> Case:
+                 F: int = 2880, k: int = 4, Fs: int = 0, only=None) -> Case:
+    """gpt-oss-shaped layer; Fs > 0 adds a (bf16, plain SwiGLU) shared expert,
+    which the pages do not give gpt-oss but the boundary allows for any layer."""
     name = "gptoss20b_mxfp4" if mxfp4 else "gptoss20b_bf16"
-    c = Case(name, T, H, E, k, F, 0, "topk_softmax", False, 1.0, "swiglu_oai", 1.702, 7.0,
+    c = Case(name, T, H, E, k, F, Fs, "topk_softmax", False, 1.0, "swiglu_oai", 1.702, 7.0,
              "bf16", "mxfp4" if mxfp4 else "bf16", "bf16")
     want = (lambda n: True) if only is None else (lambda n: n in only)
     if want("x"):
@@ -244,6 +246,11 @@ def _gptoss_case(T: int, mxfp4: bool, seed: int = BASE_SEED, E: int = 32, H: int
     else:
         c.t["gate_up_w"] = normal("gate_up_w", (E, 2 * F, H), 1.0 / np.sqrt(H), "bf16", seed)
         c.t["down_w"] = normal("down_w", (E, H, F), 1.0 / np.sqrt(F), "bf16", seed)
+    if Fs > 0:
+        c.t["sh_gate_w"] = normal("sh_gate_w", (Fs, H), 1.0 / np.sqrt(H), "bf16", seed)
+        c.t["sh_up_w"] = normal("sh_up_w", (Fs, H), 1.0 / np.sqrt(H), "bf16", seed)
+        c.t["sh_down_w"] = normal("sh_down_w", (H, Fs), 1.0 / np.sqrt(Fs), "bf16", seed)
+        c.t["sh_gate_inp"] = normal("sh_gate_inp", (1, H), 1.0 / np.sqrt(H), "bf16", seed)[0]
     return c
 
 

@@ -36,6 +36,9 @@ LAYERS = [
     ("gptoss20b_mxfp4", 2, None, {}),                         # fused down + combine, 2 pieces per lane
     ("qwen35moe_decode", 16, None, dict(E=512, k=32, H=64, F=64, Fs=64)),  # largest fused gating + permutation
     ("qwen35moe_decode", 3, None, dict(E=40, k=5, H=64, F=64, Fs=64)),     # E, k not powers of two
+    ("gptoss20b_mxfp4", 16, None, dict(E=8, H=320, F=192, k=2, Fs=128)),   # MXFP4 experts + bf16 shared expert
+    ("gptoss20b_mxfp4", 150, None, dict(E=8, H=320, F=192, k=2, Fs=128)),  # same on the MFMA tiles
+    ("gptoss20b_bf16", 16, None, dict(E=8, H=320, F=192, k=2, Fs=128)),
 ]
 
 
@@ -149,7 +152,7 @@ def _h_row(case, h_flat, p):
     return h_flat[q:q + case.Fs]
 
 
-STEP = [LAYERS[i] for i in (0, 1, 4, 5, 6, 8, 9, 11, 12, 13, 14, 15)]
+STEP = [LAYERS[i] for i in (0, 1, 4, 5, 6, 8, 9, 11, 12, 13, 14, 15, 18, 19, 20)]
 
 
 @pytest.mark.parametrize("p", STEP, ids=_ids)
