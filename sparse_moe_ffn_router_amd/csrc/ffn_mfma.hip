@@ -150,11 +150,23 @@ __device__ __forceinline__ void pipe_issue_pq(const Pipe& p, const Pipe& q, int 
   pipe_issue(x, uq ? s2 - p.nk : s2, wid, la, lb, cr);
 }
 
+// MXFP4 staging: thread t decodes 32-element block mx_blk(t) of tile row
+// mx_row(t).  Each 16-lane quarter of a wave takes 16 rows, the even ones
+// first: two rows r, r + 1 share a swizzle pattern, so taking them in
+// different halves of the quarter makes the rows written by 8 consecutive
+// lanes fall in 8 different swizzle classes and their 16-byte stores hit
+// distinct banks (two lanes per row made every store a 2-way bank conflict).
+__device__ __forceinline__ int mx_row(int t) {
+  const int lane = t & (kWave - 1), l = lane & 15;
+  return (t / kWave) * 32 + ((lane >> 5) << 4) + (l < 8 ? 2 * l : 2 * (l - 8) + 1);
+}
+__device__ __forceinline__ int mx_blk(int t) { return (t >> 4) & 1; }
+
 // MXFP4: decode a step's block to bf16 and write it (swizzled) to lb.
 __device__ __forceinline__ void pipe_put_codes(const CodeRegs& cr, uint8_t* __restrict__ lb) {
   uint4 d[4];
   mxfp4_block_to_bf16(cr.codes, cr.sc, d);
-  const int r = threadIdx.x / 2, blk = threadIdx.x % 2;
+  const int r = mx_row(threadIdx.x), blk = mx_blk(threadIdx.x);
 #pragma unroll
   for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(lb + swz(r, blk * 4 + q)) = d[q];
 }
@@ -421,15 +433,15 @@ __device__ void make_pipe(const GemmArgs& a, const Tile& t, int32_t* ids, Pipe& 
       p.b_off[i] = (uint32_t)((size_t)wrow(r) * t.K * 2) + (swz_slot(r, q % 8) << 4);
     }
   } else {
-    // one 32-element block per thread per step: tile row tid/2, block tid%2
-    const size_t row = wrow(tid / 2);
-    p.b_off[0] = (uint32_t)(row * (t.K / 2)) + (tid % 2) * 16;
+    // one 32-element block per thread per step: tile row mx_row(tid), block mx_blk(tid)
+    const size_t row = wrow(mx_row(tid));
+    p.b_off[0] = (uint32_t)(row * (t.K / 2)) + mx_blk(tid) * 16;
 #pragma unroll
     for (int i = 1; i < kBChunks; ++i) p.b_off[i] = 0;
     const size_t srow0 = MODE == MODE_GATEUP ? (size_t)t.seg * 2 * a.F : (size_t)t.seg * a.H;
     const size_t nrows = MODE == MODE_GATEUP ? (size_t)2 * a.F : (size_t)a.H;
     p.rsc = make_rsrc(a.scales + srow0 * (t.K / 32), (uint32_t)(nrows * (t.K / 32)));
-    p.sc_off = (uint32_t)(row * (t.K / 32)) + (tid % 2);
+    p.sc_off = (uint32_t)(row * (t.K / 32)) + mx_blk(tid);
   }
   // SwiGLU with separate gate and up matrices: B rows >= BN/2 read the up matrix
   p.two_mats = MODE == MODE_GATEUP && (t.sh || !a.oai);
