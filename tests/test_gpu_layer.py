@@ -39,6 +39,8 @@ LAYERS = [
     ("gptoss20b_mxfp4", 16, None, dict(E=8, H=320, F=192, k=2, Fs=128)),   # MXFP4 experts + bf16 shared expert
     ("gptoss20b_mxfp4", 150, None, dict(E=8, H=320, F=192, k=2, Fs=128)),  # same on the MFMA tiles
     ("gptoss20b_bf16", 16, None, dict(E=8, H=320, F=192, k=2, Fs=128)),
+    ("gptoss20b_bf16", 400, None, dict(E=4, H=320, F=192, k=2)),             # ~200-row segments, odd K steps
+    ("qwen35moe_decode", 700, None, dict(E=4, H=256, F=128, Fs=128, k=2)),   # long segments, shared expert
 ]
 
 
@@ -152,7 +154,7 @@ def _h_row(case, h_flat, p):
     return h_flat[q:q + case.Fs]
 
 
-STEP = [LAYERS[i] for i in (0, 1, 4, 5, 6, 8, 9, 11, 12, 13, 14, 15, 18, 19, 20)]
+STEP = [LAYERS[i] for i in (0, 1, 4, 5, 6, 8, 9, 11, 12, 13, 14, 15, 18, 19, 20, 21, 22)]
 
 
 @pytest.mark.parametrize("p", STEP, ids=_ids)
