@@ -5,7 +5,7 @@ Argument marshalling only: every step of the layer runs in the HIP kernels of
 memory and streams); the functions mirror the C entry points one to one and
 raise ``MoeError`` on a non-zero status.  There is no CPU fallback: importing
 this package fails if ``libmoe.so`` has not been built
-(``python -m sparse_moe_ffn_router_amd.build``).
+(``python sparse_moe_ffn_router_amd/build.py``).
 """
 from __future__ import annotations
 
@@ -71,7 +71,7 @@ class MoeConfig:
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError("libmoe.so is not built (%s); run python -m sparse_moe_ffn_router_amd.build" % LIB_PATH)
+        raise ImportError("libmoe.so is not built (%s); run python sparse_moe_ffn_router_amd/build.py" % LIB_PATH)
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     C, W = ctypes.POINTER(_Config), ctypes.POINTER(_Weights)
