@@ -23,6 +23,7 @@ _LIB_PATH = os.path.join(_HERE, "libmoe_ref.so")
 REF_F32, REF_BF16, REF_MXFP4 = 0, 1, 2
 REF_SOFTMAX_TOPK, REF_TOPK_SOFTMAX = 0, 1
 REF_SWIGLU, REF_SWIGLU_OAI = 0, 1
+REF_AQ_NONE, REF_AQ_MXFP8 = 0, 1
 
 
 def build(force: bool = False) -> str:
@@ -45,7 +46,8 @@ class RefCfg(ctypes.Structure):
     _fields_ = [("H", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("F", ctypes.c_int32), ("Fs", ctypes.c_int32), ("gating", ctypes.c_int32),
                 ("norm_topk_prob", ctypes.c_int32), ("weights_scale", ctypes.c_float),
-                ("act", ctypes.c_int32), ("alpha", ctypes.c_float), ("limit", ctypes.c_float)]
+                ("act", ctypes.c_int32), ("alpha", ctypes.c_float), ("limit", ctypes.c_float),
+                ("act_quant", ctypes.c_int32)]
 
 
 class RefWeights(ctypes.Structure):
@@ -67,6 +69,10 @@ def lib():
         P = ctypes.POINTER
         L.ref_mxfp4_value.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
         L.ref_mxfp4_value.restype = ctypes.c_double
+        L.ref_e4m3_value.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
+        L.ref_e4m3_value.restype = ctypes.c_double
+        L.ref_mxfp8_quantize.argtypes = [vp, ctypes.c_int64, vp, vp]
+        L.ref_mxfp8_round.argtypes = [vp, ctypes.c_int64, vp]
         L.ref_elem.argtypes = [P(RefMat), ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
         L.ref_elem.restype = ctypes.c_double
         L.ref_router_logits.argtypes = [P(RefCfg), P(RefWeights), P(RefMat), i32, vp]
@@ -95,6 +101,27 @@ def _p(a):
 _DT = {"f32": REF_F32, "bf16": REF_BF16, "mxfp4": REF_MXFP4}
 
 
+def e4m3_value(code: int, e8m0: int = 127) -> float:
+    return lib().ref_e4m3_value(code, e8m0)
+
+
+def mxfp8_quantize(v):
+    """float array (last dim a multiple of 32) -> (E4M3 codes uint8, E8M0 scales uint8)."""
+    v = np.ascontiguousarray(v, np.float64)
+    codes = np.empty(v.shape, np.uint8)
+    scales = np.empty(v.shape[:-1] + (v.shape[-1] // 32,), np.uint8)
+    lib().ref_mxfp8_quantize(_p(v), v.size, _p(codes), _p(scales))
+    return codes, scales
+
+
+def mxfp8_round(v):
+    """float array -> the values its MXFP8 quantisation represents (float64)."""
+    v = np.ascontiguousarray(v, np.float64)
+    out = np.empty_like(v)
+    lib().ref_mxfp8_round(_p(v), v.size, _p(out))
+    return out
+
+
 def _mat(arr, dtype, scales=None):
     if arr is None:
         return RefMat(0, None, None)
@@ -109,7 +136,8 @@ class Layer:
         self.cfg = RefCfg(c.H, c.E, c.k, c.F, c.Fs,
                           REF_SOFTMAX_TOPK if c.gating == "softmax_topk" else REF_TOPK_SOFTMAX,
                           int(c.norm_topk_prob), c.weights_scale,
-                          REF_SWIGLU if c.act == "swiglu" else REF_SWIGLU_OAI, c.alpha, c.limit)
+                          REF_SWIGLU if c.act == "swiglu" else REF_SWIGLU_OAI, c.alpha, c.limit,
+                          REF_AQ_MXFP8 if getattr(c, "act_quant", "none") == "mxfp8" else REF_AQ_NONE)
         t = c.t
         wd, rd = c.w_dtype, c.router_dtype
         bias_dt = "f32" if wd == "f32" else "bf16"

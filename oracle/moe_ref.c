@@ -20,6 +20,68 @@ double ref_mxfp4_value(uint32_t code, uint32_t e8m0) {
   return mag * ldexp(1.0, (int)e8m0 - 127);
 }
 
+/* E4M3 (OCP Microscaling Formats spec v1.0, section 5.3.3, and the OCP 8-bit
+ * floating point spec): sign bit 7, exponent bits 6..3 with bias 7, mantissa
+ * bits 2..0; exponent 0 is subnormal (m/8 * 2^-6); exponent 15 with
+ * mantissa 7 is NaN, so the largest magnitude is 1.75 * 2^8 = 448. */
+double ref_e4m3_value(uint32_t code, uint32_t e8m0) {
+  uint32_t ex = (code >> 3) & 15u, m = code & 7u;
+  if (ex == 15u && m == 7u) return NAN;
+  double mag = ex == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, (int)ex - 7);
+  if (code & 0x80u) mag = -mag;
+  return mag * ldexp(1.0, (int)e8m0 - 127);
+}
+
+/* E4M3 code of a value already divided by its block scale: nearest
+ * representable value, ties to the even mantissa, magnitudes beyond 448
+ * saturated to 448 (OCP MX v1.0, section 6.3, conversion with saturation). */
+static uint8_t e4m3_encode(double v) {
+  uint8_t sign = v < 0.0 ? 0x80 : 0x00;
+  double a = fabs(v);
+  if (a >= 448.0) return sign | 0x7E;
+  if (a < ldexp(1.0, -6)) {                 /* subnormal grid, step 2^-9 */
+    double m = rint(ldexp(a, 9));            /* 0..8; 8 is the smallest normal */
+    return sign | (uint8_t)m;                /* m = 8 encodes exponent 1, mantissa 0 */
+  }
+  int e;
+  double f = frexp(a, &e);                   /* a = f * 2^e, f in [0.5, 1) */
+  double m = rint((2.0 * f - 1.0) * 8.0);    /* mantissa of 1.m * 2^(e-1), 0..8 */
+  int ex = e - 1 + 7;
+  if (m == 8.0) { m = 0.0; ++ex; }
+  if (ex > 15 || (ex == 15 && m == 7.0)) return sign | 0x7E;
+  return sign | (uint8_t)((ex << 3) | (int)m);
+}
+
+/* OCP MX v1.0, section 6.3: per block of 32, the shared exponent is
+ * floor(log2(max |v|)) minus the largest E4M3 exponent (8), kept in the E8M0
+ * range [-127, 127]; every element is v / 2^shared rounded by e4m3_encode.
+ * An all-zero block gets scale byte 0 and zero codes. */
+void ref_mxfp8_quantize(const double* v, int64_t n, uint8_t* codes, uint8_t* scales) {
+  for (int64_t b = 0; b < n / 32; ++b) {
+    double amax = 0.0;
+    for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(v[b * 32 + i]));
+    int sh = -127;
+    if (amax > 0.0) {
+      int e;
+      frexp(amax, &e);                       /* amax in [2^(e-1), 2^e) */
+      sh = e - 1 - 8;
+      if (sh < -127) sh = -127;
+      if (sh > 127) sh = 127;
+    }
+    scales[b] = (uint8_t)(sh + 127);
+    for (int i = 0; i < 32; ++i) codes[b * 32 + i] = e4m3_encode(ldexp(v[b * 32 + i], -sh));
+  }
+}
+
+void ref_mxfp8_round(const double* v, int64_t n, double* out) {
+  uint8_t* c = malloc((size_t)n);
+  uint8_t* s = malloc((size_t)(n / 32 + 1));
+  ref_mxfp8_quantize(v, n, c, s);
+  for (int64_t i = 0; i < n; ++i) out[i] = ref_e4m3_value(c[i], s[i / 32]);
+  free(c);
+  free(s);
+}
+
 static double bf16_value(uint16_t b) {
   uint32_t u = (uint32_t)b << 16;
   float f;
@@ -203,15 +265,28 @@ void ref_permute(int32_t E, int32_t k, int32_t T, int32_t shared, const int32_t*
 
 static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
 
+/* Input row of a routed expert product (e < E) at the layer's activation
+ * precision: copied, or rounded to MXFP8 when act_quant is set.  The shared
+ * expert (e == E) always takes its input as given. */
+static void expert_input(const ref_cfg* c, int32_t e, const double* v, int64_t n, double* out) {
+  if (c->act_quant == REF_AQ_MXFP8 && e < c->E)
+    ref_mxfp8_round(v, n, out);
+  else
+    memcpy(out, v, sizeof(double) * (size_t)n);
+}
+
 /* SwiGLU expert [Q]: h = silu(W_gate x) * (W_up x), silu(g) = g sigmoid(g)
  * (Shazeer 2020, "GLU Variants Improve Transformer").
  * gpt-oss expert [X] Experts: gu = W_gate_up x + b (2F outputs); gate = the
  * even entries, up = the odd ones; gate clamped above at limit, up clamped
  * to [-limit, limit]; h = (up + 1) * gate * sigmoid(alpha * gate).
- * e == E selects the shared expert, which is a plain SwiGLU [Q]. */
-void ref_expert_act(const ref_cfg* c, const ref_weights* w, int32_t e, const double* xrow, double* h) {
+ * e == E selects the shared expert, which is a plain SwiGLU [Q].
+ * With act_quant the routed experts see x rounded to MXFP8 (expert_input). */
+void ref_expert_act(const ref_cfg* c, const ref_weights* w, int32_t e, const double* xin, double* h) {
   const int64_t H = c->H;
   double* wr = malloc(sizeof(double) * H);
+  double* xrow = malloc(sizeof(double) * H);
+  expert_input(c, e, xin, H, xrow);
   if (e == c->E) {
     for (int64_t f = 0; f < c->Fs; ++f) {
       load_row(&w->sh_gate_w, f, H, wr);
@@ -247,14 +322,18 @@ void ref_expert_act(const ref_cfg* c, const ref_weights* w, int32_t e, const dou
     free(gu);
   }
   free(wr);
+  free(xrow);
 }
 
-/* Down projection [Q][X]: y = W_down h (+ b_down for gpt-oss). */
-void ref_expert_down(const ref_cfg* c, const ref_weights* w, int32_t e, const double* h, double* y) {
+/* Down projection [Q][X]: y = W_down h (+ b_down for gpt-oss); with
+ * act_quant the routed experts see h rounded to MXFP8 (expert_input). */
+void ref_expert_down(const ref_cfg* c, const ref_weights* w, int32_t e, const double* hin, double* y) {
   const int64_t H = c->H;
   const int shared = e == c->E;
   const int64_t F = shared ? c->Fs : c->F;
   double* wr = malloc(sizeof(double) * F);
+  double* h = malloc(sizeof(double) * F);
+  expert_input(c, e, hin, F, h);
   for (int64_t o = 0; o < H; ++o) {
     if (shared)
       load_row(&w->sh_down_w, o, F, wr);
@@ -264,6 +343,7 @@ void ref_expert_down(const ref_cfg* c, const ref_weights* w, int32_t e, const do
     if (!shared && w->down_b.data) y[o] += ref_elem(&w->down_b, e, o, H);
   }
   free(wr);
+  free(h);
 }
 
 static int32_t token_of(const ref_cfg* c, int32_t T, int32_t a) {

@@ -41,6 +41,10 @@ extern "C" {
 enum { REF_F32 = 0, REF_BF16 = 1, REF_MXFP4 = 2 };
 enum { REF_SOFTMAX_TOPK = 0, REF_TOPK_SOFTMAX = 1 };
 enum { REF_SWIGLU = 0, REF_SWIGLU_OAI = 1 };
+/* Precision of the routed experts' GEMM inputs: as given, or rounded to
+ * MXFP8 (E4M3 elements, one E8M0 scale per 32 along the input dimension)
+ * before each routed gate/up and down product. */
+enum { REF_AQ_NONE = 0, REF_AQ_MXFP8 = 1 };
 
 /* A matrix operand: f32 / bf16 elements, or MXFP4 codes [rows][cols/32][16]
  * with E8M0 scales [rows][cols/32]. */
@@ -57,6 +61,7 @@ typedef struct {
   float weights_scale;
   int32_t act;                   /* REF_SWIGLU | REF_SWIGLU_OAI */
   float alpha, limit;
+  int32_t act_quant;             /* REF_AQ_NONE | REF_AQ_MXFP8 (routed experts only) */
 } ref_cfg;
 
 typedef struct {
@@ -76,6 +81,13 @@ typedef struct {
 double ref_elem(const ref_mat* m, int64_t row, int64_t col, int64_t cols);
 /* One E2M1 code (0..15) and one E8M0 exponent byte, exactly. */
 double ref_mxfp4_value(uint32_t code, uint32_t e8m0);
+/* One E4M3 code (0..255; 0x7F and 0xFF are NaN) and one E8M0 byte, exactly. */
+double ref_e4m3_value(uint32_t code, uint32_t e8m0);
+/* MXFP8 (E4M3) quantisation of n values (n a multiple of 32): codes[n] and
+ * one scale byte per 32 consecutive values. */
+void ref_mxfp8_quantize(const double* v, int64_t n, uint8_t* codes, uint8_t* scales);
+/* v -> the MXFP8 value it quantises to, in place-safe form (out may be v). */
+void ref_mxfp8_round(const double* v, int64_t n, double* out);
 
 /* logits[t][e] = fp32(sum_h x[t][h] Wr[e][h] (+ br[e])) */
 void ref_router_logits(const ref_cfg* c, const ref_weights* w, const ref_mat* x, int32_t T, float* logits);

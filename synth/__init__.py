@@ -153,6 +153,7 @@ class Case:
     w_dtype: str                 # "f32" | "bf16" | "mxfp4"
     router_dtype: str            # "f32" | "bf16"
     drawn_logits: bool = False   # logits are an input; no router product
+    act_quant: str = "none"      # "none" | "mxfp8": routed experts' GEMM inputs rounded to MXFP8
     t: dict = field(default_factory=dict)
 
     @property
