@@ -34,6 +34,9 @@
  *     (F32 or BF16); routed expert matrices use `w_dtype`: F32 with F32 x,
  *     BF16 or MXFP4 with BF16 x.  Logits, routing weights, the shared gate
  *     and `out` are fp32.
+ *   - act_quant = MOE_ACT_QUANT_MXFP8 (MXFP4 experts only): the routed
+ *     experts' GEMM inputs (x for gate/up, h for down) are rounded to MXFP8
+ *     before each product, which then runs on the scaled MX MFMA.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -64,6 +67,16 @@ extern "C" {
  * the tensor-layout listing).  E8M0 = 255 (NaN) is outside the contract. */
 #define MOE_DTYPE_MXFP4 2
 
+/* Precision of the routed experts' GEMM inputs.  MXFP8 (OCP MX v1.0):
+ * E4M3 elements with one E8M0 scale per 32 along the input dimension, the
+ * scale 2^(floor(log2(max|v|)) - 8), elements rounded to nearest (ties to
+ * even) and saturated at 448.  Requires w_dtype MXFP4, x_dtype BF16, no
+ * shared expert, and hidden, expert_ff multiples of 64 (MOE_EUNSUPPORTED
+ * otherwise).  MXFP4 is the weight format the gpt-oss page ("Phase 19: MoE -
+ * gpt-oss-20b", section 3) ships; this mode runs those weights natively. */
+#define MOE_ACT_QUANT_NONE 0
+#define MOE_ACT_QUANT_MXFP8 1
+
 /* Gating ("qwen35moe - Forward-Pass Design", Shared-expert MoE FFN;
  * "Phase 19: MoE - gpt-oss-20b", section 2 Router). */
 #define MOE_GATING_SOFTMAX_TOPK 0 /* softmax over E, top-k, optional renorm, * scale */
@@ -91,6 +104,7 @@ typedef struct {
   float act_limit;        /* 7.0 for gpt-oss */
   int32_t x_dtype;        /* MOE_DTYPE_F32 | MOE_DTYPE_BF16 */
   int32_t w_dtype;        /* MOE_DTYPE_F32 | MOE_DTYPE_BF16 | MOE_DTYPE_MXFP4 */
+  int32_t act_quant;      /* MOE_ACT_QUANT_*: 0 for every layer the pages define */
 } moe_config;
 
 /* Weight tensors (device pointers; names follow the pages' GGUF and
@@ -149,14 +163,17 @@ int moe_permute(const moe_config* cfg, const int32_t* topk_idx, int32_t T, int32
 
 /* Expert gate/up products with the activation applied, one row per sorted
  * position: h rows [0, T*k) have F columns, the shared rows [T*k, T*k+T)
- * follow with Fs columns.  h is bf16 when x_dtype is BF16, fp32 otherwise. */
+ * follow with Fs columns.  h is bf16 when x_dtype is BF16, fp32 otherwise.
+ * ws is used only with act_quant (the rounded x); then it must be 256-byte
+ * aligned and at least moe_workspace_bytes(cfg, T) bytes (MOE_EWORKSPACE). */
 int moe_expert_ffn(const moe_config* cfg, const moe_weights* w, const void* x,
                    const int32_t* offsets, const int32_t* sorted_assign, int32_t T, void* h,
                    void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Down projection (+ bias), weighted combine over each token's k picks in
  * pick order, plus sgate * the shared expert's down projection.
- *   h as written by moe_expert_ffn; topk_w [T][k]; sgate [T] (shared only);
+ *   h as written by moe_expert_ffn (with act_quant, rounded to MXFP8 here,
+ *   into ws); topk_w [T][k]; sgate [T] (shared only);
  *   out [T][H] fp32 (fully overwritten). */
 int moe_combine(const moe_config* cfg, const moe_weights* w, const void* h,
                 const int32_t* offsets, const int32_t* sorted_assign, const float* topk_w,
@@ -170,6 +187,16 @@ int moe_combine(const moe_config* cfg, const moe_weights* w, const void* h,
 int moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T, float* out,
                 float* logits, int32_t* topk_idx, float* topk_w, float* sgate, void* ws,
                 size_t ws_bytes, hipStream_t stream);
+
+/* MXFP8 rounding as act_quant applies it (OCP MX v1.0, section 6.3):
+ *   x      [rows][K] bf16, K a multiple of 32
+ *   codes  [rows][K] uint8 E4M3 codes
+ *   scales [rows][scale_stride] uint8 E8M0 bytes, scale_stride =
+ *          4 * ceil(K / 128) (block b of a row at byte b; the bytes past
+ *          K / 32 are left as they are)
+ * Bit-exact and deterministic: every step is exact in fp32. */
+int moe_quantize_mxfp8(const void* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                       hipStream_t stream);
 
 /* Text for a status code (static storage). */
 const char* moe_status_string(int status);

@@ -20,9 +20,10 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, 
 DTYPE_F32, DTYPE_BF16, DTYPE_MXFP4 = 0, 1, 2
 GATING_SOFTMAX_TOPK, GATING_TOPK_SOFTMAX = 0, 1
 ACT_SWIGLU, ACT_SWIGLU_OAI = 0, 1
+ACT_QUANT_NONE, ACT_QUANT_MXFP8 = 0, 1
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
-           "moe_forward", "moe_status_string")
+           "moe_forward", "moe_quantize_mxfp8", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -36,7 +37,7 @@ class _Config(ctypes.Structure):
                 ("expert_ff", ctypes.c_int32), ("shared_ff", ctypes.c_int32), ("gating", ctypes.c_int32),
                 ("norm_topk_prob", ctypes.c_int32), ("weights_scale", ctypes.c_float),
                 ("act", ctypes.c_int32), ("act_alpha", ctypes.c_float), ("act_limit", ctypes.c_float),
-                ("x_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32)]
+                ("x_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32), ("act_quant", ctypes.c_int32)]
 
 
 _WEIGHT_FIELDS = ("router_w", "router_b", "gate_w", "up_w", "gate_up_w", "gate_up_scales", "gate_up_b",
@@ -62,11 +63,12 @@ class MoeConfig:
     act_limit: float = 7.0
     x_dtype: int = DTYPE_BF16
     w_dtype: int = DTYPE_BF16
+    act_quant: int = ACT_QUANT_NONE
 
     def _c(self) -> _Config:
         return _Config(self.hidden, self.n_expert, self.top_k, self.expert_ff, self.shared_ff, self.gating,
                        int(self.norm_topk_prob), self.weights_scale, self.act, self.act_alpha, self.act_limit,
-                       self.x_dtype, self.w_dtype)
+                       self.x_dtype, self.w_dtype, self.act_quant)
 
 
 def _load():
@@ -84,6 +86,7 @@ def _load():
     L.moe_expert_ffn.argtypes = [C, W, vp, vp, vp, i32, vp, vp, sz, vp]
     L.moe_combine.argtypes = [C, W, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
     L.moe_forward.argtypes = [C, W, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_quantize_mxfp8.argtypes = [vp, ctypes.c_int64, i32, vp, vp, vp]
     return L
 
 
@@ -166,3 +169,12 @@ def moe_forward(cfg, w, x, T, out, ws, logits=None, topk_idx=None, topk_w=None, 
     nb = _nbytes(ws) if ws_bytes is None else ws_bytes
     _check(lib.moe_forward(ctypes.byref(c), ctypes.byref(ww), _ptr(x), T, _ptr(out), _ptr(logits), _ptr(topk_idx),
                            _ptr(topk_w), _ptr(sgate), _ptr(ws), nb, _stream(stream)), "moe_forward")
+
+
+def mxfp8_scale_stride(K: int) -> int:
+    return 4 * ((K + 127) // 128)
+
+
+def moe_quantize_mxfp8(x, rows, K, codes, scales, stream=None):
+    _check(lib.moe_quantize_mxfp8(_ptr(x), rows, K, _ptr(codes), _ptr(scales), _stream(stream)),
+           "moe_quantize_mxfp8")

@@ -29,6 +29,11 @@ int check_config(const moe_config* c) {
   if (c->x_dtype == MOE_DTYPE_BF16 && c->w_dtype == MOE_DTYPE_F32) return MOE_EUNSUPPORTED;
   // MXFP4 experts come in the fused interleaved gate_up layout only
   if (c->w_dtype == MOE_DTYPE_MXFP4 && c->act != MOE_ACT_SWIGLU_OAI) return MOE_EUNSUPPORTED;
+  if (c->act_quant != MOE_ACT_QUANT_NONE && c->act_quant != MOE_ACT_QUANT_MXFP8) return MOE_EINVAL;
+  if (c->act_quant == MOE_ACT_QUANT_MXFP8 &&
+      (c->w_dtype != MOE_DTYPE_MXFP4 || c->x_dtype != MOE_DTYPE_BF16 || c->shared_ff != 0 || c->hidden % 64 ||
+       c->expert_ff % 64))
+    return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 
@@ -64,6 +69,16 @@ int make_plan(const moe_config* c, int32_t T, Plan* p) {
     router_split(c, T, &p->nsplit, &steps);
   }
   p->off_part = o; o += p->nsplit > 1 ? up256((size_t)p->nsplit * T * c->n_expert * 4) : 0;
+  if (c->act_quant == MOE_ACT_QUANT_MXFP8) {
+    // bf16 values (2 bytes per element) cover the E4M3 codes (1 byte) too
+    p->mx8 = T > kGemvMaxT && mfma_shapes_ok(c);
+    p->aqx_scales = up256((size_t)T * c->hidden * 2);
+    p->aqx_bytes = p->aqx_scales + up256((size_t)T * mx8_scale_stride(c->hidden));
+    p->aqh_scales = up256((size_t)p->n_assign * c->expert_ff * 2);
+    p->aqh_bytes = p->aqh_scales + up256((size_t)p->n_assign * mx8_scale_stride(c->expert_ff));
+  }
+  p->off_aqx = o; o += p->aqx_bytes;
+  p->off_aqh = o; o += p->aqh_bytes;
   p->total = o;
   // the few-token kernels address activations and h with 32-bit buffer offsets
   const size_t act_bytes = (size_t)(p->n_assign * c->expert_ff + (p->shared ? (int64_t)T * c->shared_ff : 0)) * p->elem_x;
@@ -92,6 +107,37 @@ static int weights_ok(const moe_config* c, const moe_weights* w, bool need_route
 
 static int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
+// Gate/up with the routed experts' input x rounded to MXFP8 in aq (aqx_bytes).
+static hipError_t expert_ffn_aq(const moe_config* c, const moe_weights* w, const Plan& p, const void* x,
+                                const int32_t* offsets, const int32_t* sorted, int32_t T, void* h, char* aq,
+                                hipStream_t s) {
+  hipError_t e;
+  if (p.mx8) {
+    uint8_t* codes = (uint8_t*)aq;
+    uint8_t* scales = (uint8_t*)(aq + p.aqx_scales);
+    if ((e = launch_mxfp8_codes((const uint16_t*)x, T, c->hidden, codes, scales, s)) != hipSuccess) return e;
+    return launch_gateup_mx8(c, w, codes, scales, offsets, sorted, T, h, s);
+  }
+  if ((e = launch_mxfp8_values((const uint16_t*)x, T, c->hidden, (uint16_t*)aq, s)) != hipSuccess) return e;
+  return launch_expert_ffn(c, w, aq, offsets, sorted, T, h, s);
+}
+
+// Down with h rounded to MXFP8 in aq (aqh_bytes); y as launch_down writes it.
+static hipError_t down_aq(const moe_config* c, const moe_weights* w, const Plan& p, const void* h,
+                          const int32_t* offsets, const int32_t* sorted, int32_t T, void* y, char* aq, hipStream_t s) {
+  hipError_t e;
+  if (p.mx8) {
+    uint8_t* codes = (uint8_t*)aq;
+    uint8_t* scales = (uint8_t*)(aq + p.aqh_scales);
+    if ((e = launch_mxfp8_codes((const uint16_t*)h, p.n_assign, c->expert_ff, codes, scales, s)) != hipSuccess)
+      return e;
+    return launch_down_mx8(c, w, codes, scales, offsets, sorted, T, (uint16_t*)y, s);
+  }
+  if ((e = launch_mxfp8_values((const uint16_t*)h, p.n_assign, c->expert_ff, (uint16_t*)aq, s)) != hipSuccess)
+    return e;
+  return launch_down(c, w, aq, offsets, sorted, T, y, s);
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -102,6 +148,14 @@ size_t moe_workspace_bytes(const moe_config* cfg, int32_t T) {
   Plan p;
   if (make_plan(cfg, T, &p)) return 0;
   return p.total;
+}
+
+int moe_quantize_mxfp8(const void* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                       hipStream_t stream) {
+  if (rows < 0 || K <= 0 || K % 32) return MOE_EINVAL;
+  if (rows == 0) return MOE_OK;
+  if (!x || !codes || !scales || !aligned16(x) || !aligned16(codes)) return MOE_EINVAL;
+  return hip_status(launch_mxfp8_codes((const uint16_t*)x, rows, K, codes, scales, stream));
 }
 
 const char* moe_status_string(int status) {
@@ -154,14 +208,16 @@ int moe_permute(const moe_config* cfg, const int32_t* topk_idx, int32_t T, int32
 
 int moe_expert_ffn(const moe_config* cfg, const moe_weights* w, const void* x, const int32_t* offsets,
                    const int32_t* sorted_assign, int32_t T, void* h, void* ws, size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   Plan p;
   int st = make_plan(cfg, T, &p);
   if (st) return st;
   if ((st = weights_ok(cfg, w, false, true))) return st;
   if (T == 0) return MOE_OK;
   if (!x || !offsets || !sorted_assign || !h || !aligned16(x) || !aligned16(h)) return MOE_EINVAL;
+  if (cfg->act_quant == MOE_ACT_QUANT_MXFP8) {
+    if (!ws || ws_bytes < p.aqx_bytes || ((uintptr_t)ws & 255u)) return MOE_EWORKSPACE;
+    return hip_status(expert_ffn_aq(cfg, w, p, x, offsets, sorted_assign, T, h, (char*)ws, stream));
+  }
   return hip_status(launch_expert_ffn(cfg, w, x, offsets, sorted_assign, T, h, stream));
 }
 
@@ -175,9 +231,11 @@ int moe_combine(const moe_config* cfg, const moe_weights* w, const void* h, cons
   if (T == 0) return MOE_OK;
   if (!h || !offsets || !sorted_assign || !topk_w || !out || !aligned16(h) || !aligned16(out)) return MOE_EINVAL;
   if (p.shared && !sgate) return MOE_EINVAL;
-  if (!ws || ws_bytes < p.y_bytes || ((uintptr_t)ws & 255u)) return MOE_EWORKSPACE;
+  if (!ws || ws_bytes < p.y_bytes + p.aqh_bytes || ((uintptr_t)ws & 255u)) return MOE_EWORKSPACE;
   void* y = ws;
-  hipError_t e = launch_down(cfg, w, h, offsets, sorted_assign, T, y, stream);
+  hipError_t e = cfg->act_quant == MOE_ACT_QUANT_MXFP8
+                     ? down_aq(cfg, w, p, h, offsets, sorted_assign, T, y, (char*)ws + p.y_bytes, stream)
+                     : launch_down(cfg, w, h, offsets, sorted_assign, T, y, stream);
   if (e != hipSuccess) return MOE_EHIP;
   return hip_status(launch_combine_gather(cfg, y, topk_w, sgate, T, out, stream));
 }
@@ -216,8 +274,13 @@ int moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, int3
       return MOE_EHIP;
     if ((e = launch_permute(cfg, idx, T, offsets, sorted, pos, perm, stream)) != hipSuccess) return MOE_EHIP;
   }
-  if ((e = launch_expert_ffn(cfg, w, x, offsets, sorted, T, h, stream)) != hipSuccess) return MOE_EHIP;
-  if ((e = launch_down(cfg, w, h, offsets, sorted, T, y, stream)) != hipSuccess) return MOE_EHIP;
+  if (cfg->act_quant == MOE_ACT_QUANT_MXFP8) {
+    if ((e = expert_ffn_aq(cfg, w, p, x, offsets, sorted, T, h, b + p.off_aqx, stream)) != hipSuccess) return MOE_EHIP;
+    if ((e = down_aq(cfg, w, p, h, offsets, sorted, T, y, b + p.off_aqh, stream)) != hipSuccess) return MOE_EHIP;
+  } else {
+    if ((e = launch_expert_ffn(cfg, w, x, offsets, sorted, T, h, stream)) != hipSuccess) return MOE_EHIP;
+    if ((e = launch_down(cfg, w, h, offsets, sorted, T, y, stream)) != hipSuccess) return MOE_EHIP;
+  }
   return hip_status(launch_combine_gather(cfg, y, wt, sg, T, out, stream));
 }
 

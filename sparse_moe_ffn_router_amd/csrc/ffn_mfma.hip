@@ -57,6 +57,9 @@ struct GemmArgs {
   float* part;               // router with ksplit > 1: partial logits [ksplit][T][E]
   int32_t m_tiles_max;       // grid bound on row tiles
   float alpha, limit;
+  const uint8_t* a8;         // MXFP8 path: E4M3 activation codes [rows][K]
+  const uint8_t* a8s;        // and their E8M0 scales [rows][a8s_stride]
+  int32_t a8s_stride;
 };
 
 
@@ -713,6 +716,248 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
   wait_vm<0>();  // the zero-reading loads of the steps past the last tile
 }
 
+
+// ---------------------------------------------------------------------------
+// MXFP8 activations x MXFP4 weights on the scaled MFMA
+// (v_mfma_scale_f32_32x32x64_f8f6f4: E4M3 A, E2M1 B, one E8M0 scale per
+// 32-deep block of each operand row), with fp32 accumulation.  Same tiles,
+// wave layout, segment walk and epilogues as the bf16 kernel above; a K
+// step is 128 deep (two MFMA slices of 64; a last step of 64 when K is an
+// odd multiple of 64).  Per step the LDS ring stage holds 128 activation
+// rows of 128 code bytes (XOR-swizzled like the bf16 rows), 256 weight rows
+// of 64 code bytes (slot p ^ ((n >> 2) & 3) of a row n: 16 consecutive rows
+// read at one logical piece fall in 16 distinct 16-byte bank groups) and the
+// activation rows' scale words; the tile's weight scales, contiguous in the
+// caller's [rows][K/32] layout, are loaded into LDS once per tile.
+//
+// Lane layout of the scaled MFMA (measured on gfx950): lane l holds operand
+// row l % 32; for the E4M3 operand, K elements 16h..16h+15 of the slice's
+// first 32-block and 32+16h..32+16h+15 of its second (h = l / 32); for the
+// E2M1 operand, the 32 elements of block h, as stored (low nibble = even
+// index); the scale of lane l applies to block l / 32 of its row.  The
+// result layout is the 32x32 one of the bf16 MFMA.
+
+constexpr int BK8 = 128;
+constexpr int kMaxScaleRow = 4096 / 32;  // E8M0 bytes per weight row at most (K <= 4096)
+constexpr int kLoads8 = 5;               // loads per thread per step: 2 A, 2 B, 1 scale word
+
+__device__ __forceinline__ int swz_slot4(int n, int p) { return p ^ ((n >> 2) & 3); }
+
+typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint32_t ds_read_u8a(const uint8_t* p) {
+  uint32_t r;
+  asm volatile("ds_read_u8 %0, %1" : "=v"(r) : "v"((uint32_t)(uintptr_t)p) : "memory");
+  return r;
+}
+__device__ __forceinline__ uint32_t ds_read_b32a(const void* p) {
+  uint32_t r;
+  asm volatile("ds_read_b32 %0, %1" : "=v"(r) : "v"((uint32_t)(uintptr_t)p) : "memory");
+  return r;
+}
+
+// Fragments and scales of one K step (two slices).
+struct Mx8Frag {
+  bf16x8_t a[2][2][2];  // [slice][row block][piece]
+  bf16x8_t b[2][2];     // [slice][column block]
+  uint32_t sa[2];       // scale word of each row block
+  uint32_t sb[2][2];    // [slice][column block] scale byte
+};
+__device__ __forceinline__ void mx8_wait(Mx8Frag& f) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(f.a[0][0][0]), "+v"(f.a[0][0][1]), "+v"(f.a[0][1][0]), "+v"(f.a[0][1][1]),
+                 "+v"(f.a[1][0][0]), "+v"(f.a[1][0][1]), "+v"(f.a[1][1][0]), "+v"(f.a[1][1][1]),
+                 "+v"(f.b[0][0]), "+v"(f.b[0][1]), "+v"(f.b[1][0]), "+v"(f.b[1][1]), "+v"(f.sa[0]),
+                 "+v"(f.sa[1]), "+v"(f.sb[0][0]), "+v"(f.sb[0][1]), "+v"(f.sb[1][0]), "+v"(f.sb[1][1]));
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads, 1) void k_mx8_gemm(GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t la[3][BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t lb[3][BN * 64];
+  __shared__ __attribute__((aligned(16))) uint32_t lsa[3][(kThreads / kWave) * kWave];
+  __shared__ __attribute__((aligned(16))) uint8_t lsb[BN * kMaxScaleRow + 256];
+  __shared__ SegTables st;
+  __shared__ int32_t ids_s[BM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wid >> 2, wn = wid & 3;
+  const int hh = lane >> 5;
+
+  // one tile per workgroup; each XCD takes a contiguous range of tiles
+  const int total_m = __builtin_amdgcn_readfirstlane(build_tables(a.offsets, a.E, st));
+  const int total = total_m * a.n_tiles;
+  const int per_xcd = (total + 7) / 8;
+  const int slot = blockIdx.x / 8;
+  const int lin = (blockIdx.x % 8) * per_xcd + slot;
+  if (slot >= per_xcd || lin >= total) return;
+  Tile t;
+  if (!tile_at<MODE>(a, st, lin, total_m, t)) return;
+  const int K = t.K;
+  const int nk = (K + BK8 - 1) / BK8;
+  const int kb = K / 32;  // scale bytes per row
+
+  // assignment ids of the tile's rows (gate/up: token rows to gather; down:
+  // y rows to write); rows past the segment read as -1
+  if (tid < BM) ids_s[tid] = tid < t.rows ? a.sorted_assign[t.p0 + tid] : -1;
+
+  // the tile's weight scales: rows [rb0, rb0 + BN) of the segment's matrix,
+  // contiguous bytes, copied as aligned dwords
+  const int rows_e = MODE == MODE_GATEUP ? 2 * a.F : a.H;
+  const int rb0 = MODE == MODE_GATEUP ? 2 * t.c0 : t.c0;
+  const uint32_t sc_start = (uint32_t)(((size_t)t.seg * rows_e + rb0) * kb);
+  const int sc_shift = (int)(sc_start & 3u);
+  {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales, (uint32_t)((size_t)a.E * rows_e * kb));
+    const int ndw = (BN * kb + sc_shift + 3) / 4;
+    const int nchunk = (ndw + kWave - 1) / kWave;
+    for (int c = wid; c < nchunk; c += kThreads / kWave)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(lsb + c * 256), 4,
+                                               (int)((sc_start & ~3u) + (uint32_t)(c * 256 + lane * 4)), 0, 0, 0);
+  }
+  __syncthreads();  // ids_s visible
+
+  // per-thread load offsets (step 0); a step adds kt * 128 (A), kt * 64 (B), kt * 4 (scales)
+  const int64_t nas = (int64_t)a.T * a.k;
+  const size_t arows = MODE == MODE_GATEUP ? (size_t)a.T : (size_t)nas;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.a8, (uint32_t)(arows * K));
+  const __amdgpu_buffer_rsrc_t ras = make_rsrc(a.a8s, (uint32_t)(arows * a.a8s_stride));
+  const size_t wbytes = (size_t)rows_e * (K / 2);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc((const uint8_t*)a.w0 + (size_t)t.seg * wbytes, (uint32_t)wbytes);
+  uint32_t aoff[2], boff[2], soff;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = tid + i * kThreads;
+    const int r = q / 8;
+    const int id = ids_s[r];
+    uint32_t o = kOutOfRange;
+    if (id >= 0) {
+      const size_t row = MODE == MODE_GATEUP ? (size_t)(id / a.k) : (size_t)(t.p0 + r);
+      o = (uint32_t)(row * K) + (swz_slot(r, q % 8) << 4);
+    }
+    aoff[i] = o;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = tid + i * kThreads;
+    const int n = q / 4;
+    int wr;
+    if (MODE == MODE_GATEUP) {
+      const int f = min(t.c0 + (n & (BN / 2 - 1)), a.F - 1);
+      wr = 2 * f + (n >= BN / 2);
+    } else {
+      wr = min(t.c0 + n, a.H - 1);
+    }
+    boff[i] = (uint32_t)((size_t)wr * (K / 2)) + (swz_slot4(n, q % 4) << 4);
+  }
+  {
+    const int r = wid * 16 + lane;  // lanes 0..15 of each wave: one activation row's scale word
+    const int id = lane < 16 ? ids_s[r] : -1;
+    soff = kOutOfRange;
+    if (id >= 0) {
+      const size_t row = MODE == MODE_GATEUP ? (size_t)(id / a.k) : (size_t)(t.p0 + r);
+      soff = (uint32_t)(row * a.a8s_stride);
+    }
+  }
+  auto issue = [&](int s) {
+    const int sg = s % 3;
+    const bool ok = s < nk;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      dma16(ra, la[sg] + (i * kThreads + wid * kWave) * 16, ok && aoff[i] != kOutOfRange ? aoff[i] + s * BK8 : kOutOfRange);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(rw, lb[sg] + (i * kThreads + wid * kWave) * 16, ok ? boff[i] + s * (BK8 / 2) : kOutOfRange);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, (lds_ptr_t)(lsa[sg] + wid * kWave), 4,
+                                             (int)(ok && soff != kOutOfRange ? soff + s * 4 : kOutOfRange), 0, 0, 0);
+  };
+
+  // fragment rows of this lane
+  const int ar0 = wm * 64 + (lane & 31);
+  int bn[2];
+  if (MODE == MODE_GATEUP) {
+    bn[0] = wn * 32 + (lane & 31);
+    bn[1] = BN / 2 + wn * 32 + (lane & 31);
+  } else {
+    bn[0] = wn * 64 + (lane & 31);
+    bn[1] = wn * 64 + 32 + (lane & 31);
+  }
+  int bsc[2];  // byte offset of each column row's scales in lsb
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int li = MODE == MODE_GATEUP ? (bn[j] < BN / 2 ? 2 * bn[j] : 2 * (bn[j] - BN / 2) + 1) : bn[j];
+    bsc[j] = sc_shift + li * kb;
+  }
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  issue(0);
+  issue(1);
+  wait_vm<kLoads8>();  // the tile's weight scales and step 0
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt) {
+      wait_vm<kLoads8>();
+      lds_barrier();
+    }
+    issue(kt + 2);
+    const int sg = kt % 3;
+    const uint8_t* A = la[sg];
+    const uint8_t* B = lb[sg];
+    Mx8Frag f;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        f.a[s][i][0] = ds_read16(A + swz(ar0 + 32 * i, 4 * s + hh));
+        f.a[s][i][1] = ds_read16(A + swz(ar0 + 32 * i, 4 * s + 2 + hh));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int p = 2 * s + hh;
+        f.b[s][j] = ds_read16(B + bn[j] * 64 + (swz_slot4(bn[j], p) << 4));
+        f.sb[s][j] = ds_read_u8a(lsb + bsc[j] + 4 * kt + p);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = ar0 + 32 * i;
+      f.sa[i] = ds_read_b32a(lsa[sg] + (r / 16) * kWave + (r % 16));
+    }
+    mx8_wait(f);
+    const int nsl = K - kt * BK8 >= BK8 ? 2 : 1;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (s < nsl) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint32_t* p0 = reinterpret_cast<const uint32_t*>(&f.a[s][i][0]);
+          const uint32_t* p1 = reinterpret_cast<const uint32_t*>(&f.a[s][i][1]);
+          const i32x8_t av = {(int)p0[0], (int)p0[1], (int)p0[2], (int)p0[3],
+                              (int)p1[0], (int)p1[1], (int)p1[2], (int)p1[3]};
+          const int sa = (int)((f.sa[i] >> (8 * (2 * s + hh))) & 0xFFu);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const uint32_t* pb = reinterpret_cast<const uint32_t*>(&f.b[s][j]);
+            const i32x8_t bv = {(int)pb[0], (int)pb[1], (int)pb[2], (int)pb[3], 0, 0, 0, 0};
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 0, 4, 0, sa, 0,
+                                                                         (int)f.sb[s][j]);
+          }
+        }
+      }
+    }
+  }
+  wait_vm<0>();  // the zero-reading loads of the steps past the end
+  epilogue<MODE>(a, t, acc, wm, wn, ids_s);
+}
+
 int row_tiles_bound(const moe_config* c, int32_t T) {
   const int64_t nk = (int64_t)T * c->top_k;
   const int64_t nonempty = nk < c->n_expert ? nk : c->n_expert;
@@ -836,6 +1081,54 @@ hipError_t launch_down_mfma(const moe_config* c, const moe_weights* w, const voi
   a.split_steps = (c->expert_ff > c->shared_ff ? c->expert_ff : c->shared_ff) / BK;
   const int min_k = c->shared_ff > 0 && c->shared_ff < c->expert_ff ? c->shared_ff : c->expert_ff;
   return launch<MODE_DOWN>(a, c->w_dtype == MOE_DTYPE_MXFP4, min_k, s);
+}
+
+
+// MXFP8 x MXFP4 expert products (routed experts only, no shared expert).
+hipError_t launch_gateup_mx8(const moe_config* c, const moe_weights* w, const uint8_t* xq, const uint8_t* xs,
+                             const int32_t* offsets, const int32_t* sorted_assign, int32_t T, void* h, hipStream_t s) {
+  GemmArgs a = {};
+  a.a8 = xq;
+  a.a8s = xs;
+  a.a8s_stride = ((c->hidden + BK8 - 1) / BK8) * 4;
+  a.w0 = w->gate_up_w;
+  a.scales = w->gate_up_scales;
+  a.bias = (const uint16_t*)w->gate_up_b;
+  a.offsets = offsets;
+  a.sorted_assign = sorted_assign;
+  a.out = h;
+  a.T = T; a.k = c->top_k; a.H = c->hidden; a.E = c->n_expert; a.F = c->expert_ff; a.Fs = 0;
+  a.shared = 0; a.oai = 1; a.alpha = c->act_alpha; a.limit = c->act_limit;
+  a.n_tiles = (c->expert_ff + BN / 2 - 1) / (BN / 2);
+  a.m_tiles_max = row_tiles_bound(c, T);
+  a.ksplit = 1;
+  a.split_steps = c->hidden / BK;
+  const int64_t tiles = (int64_t)a.n_tiles * a.m_tiles_max;
+  k_mx8_gemm<MODE_GATEUP><<<(unsigned)((tiles + 7) / 8 * 8), kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_mx8(const moe_config* c, const moe_weights* w, const uint8_t* hq, const uint8_t* hs,
+                           const int32_t* offsets, const int32_t* sorted_assign, int32_t T, uint16_t* y, hipStream_t s) {
+  GemmArgs a = {};
+  a.a8 = hq;
+  a.a8s = hs;
+  a.a8s_stride = ((c->expert_ff + BK8 - 1) / BK8) * 4;
+  a.w0 = w->down_w;
+  a.scales = w->down_scales;
+  a.bias = (const uint16_t*)w->down_b;
+  a.offsets = offsets;
+  a.sorted_assign = sorted_assign;
+  a.out = y;
+  a.T = T; a.k = c->top_k; a.H = c->hidden; a.E = c->n_expert; a.F = c->expert_ff; a.Fs = 0;
+  a.shared = 0; a.oai = 1;
+  a.n_tiles = (c->hidden + BN - 1) / BN;
+  a.m_tiles_max = row_tiles_bound(c, T);
+  a.ksplit = 1;
+  a.split_steps = c->expert_ff / BK;
+  const int64_t tiles = (int64_t)a.n_tiles * a.m_tiles_max;
+  k_mx8_gemm<MODE_DOWN><<<(unsigned)((tiles + 7) / 8 * 8), kThreads, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -139,9 +139,14 @@ struct Plan {
   int nseg;           // E (+1)
   size_t elem_x;      // bytes per activation / h element
   size_t off_logits, off_idx, off_w, off_sgate, off_offsets, off_sorted, off_pos;
-  size_t off_perm, off_h, off_y, off_part, total;
+  size_t off_perm, off_h, off_y, off_part, off_aqx, off_aqh, total;
   int32_t nsplit;     // router split-K ranges (1: none)
   size_t perm_bytes, y_bytes;  // scratch needed by moe_permute / moe_combine alone
+  // act_quant: rounded x (moe_expert_ffn's scratch) and rounded h (after y in
+  // moe_combine's scratch); each is the bf16 values or the E4M3 codes, then
+  // the E8M0 scales at aqx_scales / aqh_scales bytes in
+  size_t aqx_bytes, aqh_bytes, aqx_scales, aqh_scales;
+  bool mx8;           // act_quant and the MFMA path: codes + scales, else bf16 values
 };
 
 int make_plan(const moe_config* c, int32_t T, Plan* p);
@@ -177,5 +182,16 @@ hipError_t launch_down(const moe_config* c, const moe_weights* w, const void* h,
                        const int32_t* sorted_assign, int32_t T, void* y, hipStream_t s);
 hipError_t launch_combine_gather(const moe_config* c, const void* y, const float* topk_w, const float* sgate,
                                  int32_t T, float* out, hipStream_t s);
+// MXFP8 rounding of bf16 rows [rows][K] (mxfp8.hip): E4M3 codes + E8M0
+// scales (row stride mx8_scale_stride(K) bytes), or the rounded bf16 values.
+int mx8_scale_stride(int K);
+hipError_t launch_mxfp8_codes(const uint16_t* src, int64_t rows, int K, uint8_t* codes, uint8_t* scales,
+                              hipStream_t s);
+hipError_t launch_mxfp8_values(const uint16_t* src, int64_t rows, int K, uint16_t* dst, hipStream_t s);
+// MXFP8 x MXFP4 grouped expert products on the scaled MFMA (ffn_mfma.hip).
+hipError_t launch_gateup_mx8(const moe_config* c, const moe_weights* w, const uint8_t* xq, const uint8_t* xs,
+                             const int32_t* offsets, const int32_t* sorted_assign, int32_t T, void* h, hipStream_t s);
+hipError_t launch_down_mx8(const moe_config* c, const moe_weights* w, const uint8_t* hq, const uint8_t* hs,
+                           const int32_t* offsets, const int32_t* sorted_assign, int32_t T, uint16_t* y, hipStream_t s);
 
 }  // namespace moe

@@ -14,7 +14,8 @@ def config_of(case) -> "moe.MoeConfig":
         gating=moe.GATING_SOFTMAX_TOPK if case.gating == "softmax_topk" else moe.GATING_TOPK_SOFTMAX,
         norm_topk_prob=case.norm_topk_prob, weights_scale=case.weights_scale,
         act=moe.ACT_SWIGLU if case.act == "swiglu" else moe.ACT_SWIGLU_OAI,
-        act_alpha=case.alpha, act_limit=case.limit, x_dtype=_DT[case.x_dtype], w_dtype=_DT[case.w_dtype])
+        act_alpha=case.alpha, act_limit=case.limit, x_dtype=_DT[case.x_dtype], w_dtype=_DT[case.w_dtype],
+        act_quant=moe.ACT_QUANT_MXFP8 if case.act_quant == "mxfp8" else moe.ACT_QUANT_NONE)
 
 
 def to_torch(a: np.ndarray, device="cuda") -> torch.Tensor:

@@ -15,18 +15,18 @@ HEADER = os.path.join(ROOT, "include", "moe.h")
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn",
-                                  "moe_combine", "moe_forward", "moe_status_string"])
+                                  "moe_combine", "moe_forward", "moe_quantize_mxfp8", "moe_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
     import sparse_moe_ffn_router_amd as moe
     out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True, text=True).stdout
-    exported = set(re.findall(r" T (moe_[a-z_]+)$", out, flags=re.M))
+    exported = set(re.findall(r" T (moe_[a-z0-9_]+)$", out, flags=re.M))
     for name in _declared():
         assert name in exported, name
         assert getattr(moe.lib, name) is not None
@@ -52,6 +52,35 @@ def test_workspace_bytes_and_config_validation():
     for unsup in (dict(hidden=2050), dict(expert_ff=500), dict(x_dtype=moe.DTYPE_F32),
                   dict(w_dtype=moe.DTYPE_MXFP4)):  # mxfp4 needs the interleaved gate_up layout
         assert moe.moe_workspace_bytes(_cfg(**unsup), 8) == 0, unsup
+
+
+def test_act_quant_validation():
+    import sparse_moe_ffn_router_amd as moe
+    mx = dict(hidden=2880, n_expert=32, top_k=4, expert_ff=2880, shared_ff=0, gating=moe.GATING_TOPK_SOFTMAX,
+              norm_topk_prob=False, act=moe.ACT_SWIGLU_OAI, w_dtype=moe.DTYPE_MXFP4)
+    plain = moe.moe_workspace_bytes(_cfg(**mx), 2048)
+    quant = moe.moe_workspace_bytes(_cfg(act_quant=moe.ACT_QUANT_MXFP8, **mx), 2048)
+    assert plain > 0 and quant > plain
+    # rounded x and h (2 bytes per element) plus their scale words
+    assert quant - plain >= 2048 * 2880 * 2 + 2048 * 4 * 2880 * 2
+    assert moe.moe_workspace_bytes(_cfg(act_quant=7, **mx), 8) == 0
+    for unsup in (dict(w_dtype=moe.DTYPE_BF16), dict(shared_ff=512), dict(hidden=2880 + 32),
+                  dict(expert_ff=2880 - 32)):
+        c = dict(mx)
+        c.update(unsup)
+        assert moe.moe_workspace_bytes(_cfg(act_quant=moe.ACT_QUANT_MXFP8, **c), 64) == 0, unsup
+
+
+def test_quantize_argument_checks():
+    import sparse_moe_ffn_router_amd as moe
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    q = moe.lib.moe_quantize_mxfp8
+    fake = vp(1 << 20)
+    assert q(fake, i64(4), i32(48), fake, fake, None) == moe.MOE_EINVAL     # K not a multiple of 32
+    assert q(None, i64(4), i32(64), fake, fake, None) == moe.MOE_EINVAL     # null input
+    assert q(vp((1 << 20) + 2), i64(4), i32(64), fake, fake, None) == moe.MOE_EINVAL  # misaligned
+    assert q(fake, i64(-1), i32(64), fake, fake, None) == moe.MOE_EINVAL
+    assert q(None, i64(0), i32(64), None, None, None) == moe.MOE_OK          # no rows: nothing to do
 
 
 def _raw(fn, *args):
