@@ -356,15 +356,18 @@ def main():
     if a.gptoss:
         del dec
         result["gptoss"] = {}
-        for name, T in (("gptoss20b_bf16", 2048), ("gptoss20b_mxfp4", 16), ("gptoss20b_mxfp4", 2048)):
+        for name, T, aq in (("gptoss20b_bf16", 2048, "none"), ("gptoss20b_mxfp4", 16, "none"),
+                            ("gptoss20b_mxfp4", 2048, "none"), ("gptoss20b_mxfp4", 16, "mxfp8"),
+                            ("gptoss20b_mxfp4", 2048, "mxfp8")):
             c = synth.make_case(name, T=T)
+            c.act_quant = aq
             gl = Layer(c, 2)
             g_ms, _ = time_loop(gl.forward, a.prefill_steps if T > 64 else a.steps, 3)
             n_act = active_experts(gl.idx.cpu().numpy(), c.E)
             per_expert = (2 * c.F * c.H + c.H * c.F) * (2 if c.w_dtype == "bf16" else 0.5 + 1 / 16.0)
             byt = n_act * per_expert + c.E * c.H * 2 + T * c.H * 6
             fl = layer_flops(c, T)
-            key = "%s_T%d" % (name, T)
+            key = "%s_T%d%s" % (name, T, "_mxfp8_act" if aq == "mxfp8" else "")
             result["gptoss"][key] = {"ms": round(g_ms, 4), "tokens_per_s": round(T / (g_ms * 1e-3), 1),
                                      "TFLOPs": round(fl / (g_ms * 1e-3) / 1e12, 2),
                                      "frac_hbm": round(byt / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -763,12 +763,14 @@ struct Mx8Frag {
   uint32_t sa[2];       // scale word of each row block
   uint32_t sb[2][2];    // [slice][column block] scale byte
 };
-__device__ __forceinline__ void mx8_wait(Mx8Frag& f) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(f.a[0][0][0]), "+v"(f.a[0][0][1]), "+v"(f.a[0][1][0]), "+v"(f.a[0][1][1]),
-                 "+v"(f.a[1][0][0]), "+v"(f.a[1][0][1]), "+v"(f.a[1][1][0]), "+v"(f.a[1][1][1]),
-                 "+v"(f.b[0][0]), "+v"(f.b[0][1]), "+v"(f.b[1][0]), "+v"(f.b[1][1]), "+v"(f.sa[0]),
-                 "+v"(f.sa[1]), "+v"(f.sb[0][0]), "+v"(f.sb[0][1]), "+v"(f.sb[1][0]), "+v"(f.sb[1][1]));
+// Wait until at most N LDS reads are outstanding; ties the fragments of
+// slice S (and the activation scale words) to that wait.
+template <int N, int S> __device__ __forceinline__ void mx8_wait(Mx8Frag& f) {
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(f.a[S][0][0]), "+v"(f.a[S][0][1]), "+v"(f.a[S][1][0]), "+v"(f.a[S][1][1]), "+v"(f.b[S][0]),
+                 "+v"(f.b[S][1]), "+v"(f.sb[S][0]), "+v"(f.sb[S][1])
+               : "n"(N), "v"(f.sa[0]), "v"(f.sa[1]));
+  asm volatile("" : "+v"(f.sa[0]), "+v"(f.sa[1]));
 }
 
 template <int MODE>
@@ -913,6 +915,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_mx8_gemm(GemmArgs a) {
     const uint8_t* B = lb[sg];
     Mx8Frag f;
 #pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = ar0 + 32 * i;
+      f.sa[i] = ds_read_b32a(lsa[sg] + (r / 16) * kWave + (r % 16));
+    }
+    // slice 1's reads are in flight during slice 0's MFMAs
+#pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -926,33 +934,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_mx8_gemm(GemmArgs a) {
         f.sb[s][j] = ds_read_u8a(lsb + bsc[j] + 4 * kt + p);
       }
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = ar0 + 32 * i;
-      f.sa[i] = ds_read_b32a(lsa[sg] + (r / 16) * kWave + (r % 16));
-    }
-    mx8_wait(f);
     const int nsl = K - kt * BK8 >= BK8 ? 2 : 1;
+    auto slice = [&](int s) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      if (s < nsl) {
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t* p0 = reinterpret_cast<const uint32_t*>(&f.a[s][i][0]);
+        const uint32_t* p1 = reinterpret_cast<const uint32_t*>(&f.a[s][i][1]);
+        const i32x8_t av = {(int)p0[0], (int)p0[1], (int)p0[2], (int)p0[3],
+                            (int)p1[0], (int)p1[1], (int)p1[2], (int)p1[3]};
+        const int sa = (int)((f.sa[i] >> (8 * (2 * s + hh))) & 0xFFu);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const uint32_t* p0 = reinterpret_cast<const uint32_t*>(&f.a[s][i][0]);
-          const uint32_t* p1 = reinterpret_cast<const uint32_t*>(&f.a[s][i][1]);
-          const i32x8_t av = {(int)p0[0], (int)p0[1], (int)p0[2], (int)p0[3],
-                              (int)p1[0], (int)p1[1], (int)p1[2], (int)p1[3]};
-          const int sa = (int)((f.sa[i] >> (8 * (2 * s + hh))) & 0xFFu);
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const uint32_t* pb = reinterpret_cast<const uint32_t*>(&f.b[s][j]);
-            const i32x8_t bv = {(int)pb[0], (int)pb[1], (int)pb[2], (int)pb[3], 0, 0, 0, 0};
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 0, 4, 0, sa, 0,
-                                                                         (int)f.sb[s][j]);
-          }
+        for (int j = 0; j < 2; ++j) {
+          const uint32_t* pb = reinterpret_cast<const uint32_t*>(&f.b[s][j]);
+          const i32x8_t bv = {(int)pb[0], (int)pb[1], (int)pb[2], (int)pb[3], 0, 0, 0, 0};
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 0, 4, 0, sa, 0,
+                                                                       (int)f.sb[s][j]);
         }
       }
-    }
+    };
+    mx8_wait<8, 0>(f);
+    slice(0);
+    mx8_wait<0, 1>(f);
+    if (nsl == 2) slice(1);
   }
   wait_vm<0>();  // the zero-reading loads of the steps past the end
   epilogue<MODE>(a, t, acc, wm, wn, ids_s);
