@@ -75,6 +75,7 @@ def lib():
         L.ref_mxfp8_round.argtypes = [vp, ctypes.c_int64, vp]
         L.ref_elem.argtypes = [P(RefMat), ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
         L.ref_elem.restype = ctypes.c_double
+        L.ref_rmsnorm.argtypes = [P(RefMat), i32, i32, P(RefMat), ctypes.c_double, i32, vp]
         L.ref_router_logits.argtypes = [P(RefCfg), P(RefWeights), P(RefMat), i32, vp]
         L.ref_shared_gate_logit.argtypes = [P(RefCfg), P(RefWeights), P(RefMat), i32, vp]
         L.ref_topk.argtypes = [i32, i32, vp, vp]
@@ -119,6 +120,19 @@ def mxfp8_round(v):
     v = np.ascontiguousarray(v, np.float64)
     out = np.empty_like(v)
     lib().ref_mxfp8_round(_p(v), v.size, _p(out))
+    return out
+
+
+def rmsnorm(x, g, eps, dtype):
+    """RMSNorm of the rows of x ([T][H]) with weight g ([H]) -> the normalised
+    rows in `dtype` ('f32': float32, 'bf16': uint16 bf16 bits); x and g are
+    given in that same representation."""
+    x = np.ascontiguousarray(x)
+    g = np.ascontiguousarray(g).reshape(1, -1)
+    T, H = x.shape
+    out = np.empty((T, H), np.uint16 if dtype == "bf16" else np.float32)
+    lib().ref_rmsnorm(ctypes.byref(_mat(x, dtype)), T, H, ctypes.byref(_mat(g, dtype)), float(eps),
+                      _DT[dtype], _p(out))
     return out
 
 
@@ -243,6 +257,25 @@ class Layer:
                           _p(out), _p(ti), _p(tw), _p(sg))
         return out, ti, tw, sg
 
+    def block_forward(self, tokens=None, logits=None):
+        """The layer inside its decoder block: out = r + layer(RMSNorm(r) * g)
+        with r = the case's "resid" rows, g its "norm_w", eps its norm_eps.
+        Returns (out, xn, topk_idx, topk_w, sgate); the residual sum is taken
+        in double from the layer's fp32 output and rounded to fp32."""
+        c = self.case
+        xn = rmsnorm(c.t["resid"], c.t["norm_w"], c.norm_eps, c.x_dtype)
+        keep = self.x
+        self._xn = xn
+        self.x = _mat(xn, c.x_dtype)
+        try:
+            out, ti, tw, sg = self.forward(logits=logits, tokens=tokens)
+        finally:
+            self.x = keep
+        r = c.t["resid"]
+        r = (bf16_to_f64(r) if c.x_dtype == "bf16" else np.asarray(r, np.float64))
+        out = (r + out.astype(np.float64)).astype(np.float32)
+        return out, xn, ti, tw, sg
+
     def forward_dense(self, logits=None):
         c = self.case
         out = np.empty((c.T, c.H), np.float64)
@@ -250,6 +283,10 @@ class Layer:
         lib().ref_forward_dense(ctypes.byref(self.cfg), ctypes.byref(self.w), ctypes.byref(self.x), c.T,
                                 _p(lg), _p(out))
         return out
+
+
+def bf16_to_f64(b):
+    return (np.ascontiguousarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
 def topk(keys, k):

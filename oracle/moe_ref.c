@@ -115,6 +115,38 @@ static double dot(const double* a, const double* b, int64_t n) {
   return s;
 }
 
+/* ---------------------------------------------------------------- block */
+
+/* fp32 -> bf16 bits, round to nearest even (finite values). */
+static uint16_t bf16_round(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+/* [B] RMSNorm: the mean of squares over the row, plus eps, its inverse
+ * square root, times the element and its weight, all in double; the result
+ * is rounded to the nearest float and, for bf16 output, that float to the
+ * nearest bf16 (the storage type the layer then reads). */
+void ref_rmsnorm(const ref_mat* x, int32_t T, int32_t H, const ref_mat* g, double eps, int32_t out_dtype,
+                 void* out) {
+  double* v = malloc(sizeof(double) * (size_t)H);
+  for (int64_t t = 0; t < T; ++t) {
+    load_row(x, t, H, v);
+    double ms = dot(v, v, H) / (double)H;
+    double r = 1.0 / sqrt(ms + eps);
+    for (int64_t h = 0; h < H; ++h) {
+      double y = v[h] * r * ref_elem(g, 0, h, H);
+      if (out_dtype == REF_BF16)
+        ((uint16_t*)out)[t * H + h] = bf16_round((float)y);
+      else
+        ((float*)out)[t * H + h] = (float)y;
+    }
+  }
+  free(v);
+}
+
 /* ---------------------------------------------------------------- router */
 
 /* [Q] router logits = ffn_gate_inp . x (no bias); [X] Router: x W^T + b. */

@@ -21,6 +21,14 @@
  *        bias; weighted sum) and section 3 plus the tensor-layout listing
  *        (MXFP4: 32-element blocks along the input dim, low nibble = even
  *        index, value = lut[code] * 2^(e8m0-127)).
+ *   [B]  The decoder block around the layer: "qwen35moe - Forward-Pass
+ *        Design (Pantheon port)", section "Block scaffold" (pre-norm
+ *        sandwich, every norm an RMS norm, the residual adds the
+ *        un-normalised input) and its config table (rms_norm_eps 1e-6);
+ *        "Phase 19: MoE - gpt-oss-20b", section 2 (standard RMSNorm with
+ *        the variance in fp32, eps 1e-5; decoder layer out = h +
+ *        moe(post_norm(h))); "qwen35moe CPU-reference golden vectors",
+ *        section "Kernel 3" (y = x * w / sqrt(mean(x^2) + eps)).
  *
  * Every dot product accumulates in double.  Values the pages fix as fp32
  * (router logits, routing weights, the shared gate scalar) are rounded to
@@ -88,6 +96,13 @@ double ref_e4m3_value(uint32_t code, uint32_t e8m0);
 void ref_mxfp8_quantize(const double* v, int64_t n, uint8_t* codes, uint8_t* scales);
 /* v -> the MXFP8 value it quantises to, in place-safe form (out may be v). */
 void ref_mxfp8_round(const double* v, int64_t n, double* out);
+
+/* [B] RMSNorm of T rows of H values:
+ *   y[t][h] = x[t][h] * g[h] / sqrt(mean_h x[t][h]^2 + eps)
+ * in double, rounded once to out_dtype (REF_F32: float; REF_BF16: bf16 bits,
+ * nearest even).  x and g are F32 or BF16 matrices ([T][H] and [1][H]). */
+void ref_rmsnorm(const ref_mat* x, int32_t T, int32_t H, const ref_mat* g, double eps, int32_t out_dtype,
+                 void* out);
 
 /* logits[t][e] = fp32(sum_h x[t][h] Wr[e][h] (+ br[e])) */
 void ref_router_logits(const ref_cfg* c, const ref_weights* w, const ref_mat* x, int32_t T, float* logits);

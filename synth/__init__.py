@@ -36,7 +36,8 @@ TID = {
     "x": 1, "router_w": 2, "router_b": 3, "gate_w": 4, "up_w": 5, "gate_up_w": 6,
     "gate_up_b": 7, "down_w": 8, "down_b": 9, "sh_gate_w": 10, "sh_up_w": 11,
     "sh_down_w": 12, "sh_gate_inp": 13, "gate_up_codes": 14, "gate_up_scales": 15,
-    "down_codes": 16, "down_scales": 17, "logits": 18,
+    "down_codes": 16, "down_scales": 17, "logits": 18, "resid": 19, "norm_w": 20,
+    "resid_scale": 21,
 }
 
 
@@ -154,6 +155,7 @@ class Case:
     router_dtype: str            # "f32" | "bf16"
     drawn_logits: bool = False   # logits are an input; no router product
     act_quant: str = "none"      # "none" | "mxfp8": routed experts' GEMM inputs rounded to MXFP8
+    norm_eps: float = 1e-6       # RMSNorm epsilon of the block around the layer
     t: dict = field(default_factory=dict)
 
     @property
@@ -263,6 +265,25 @@ CASES = {
     "gptoss20b_bf16": (lambda T, **kw: _gptoss_case(T, False, **kw), 2048),
     "gptoss20b_mxfp4": (lambda T, **kw: _gptoss_case(T, True, **kw), 2048),
 }
+
+
+def add_block_inputs(c: Case, seed: int = BASE_SEED) -> Case:
+    """Inputs of the decoder block around the layer: the residual stream
+    "resid" [T][H] (N(0,1) rows times a per-token power of two in
+    2^-3..2^4, so every token has its own RMS) and the norm weight "norm_w"
+    [H], 1 + N(0, 0.1^2) (norm weights centred near 1), both in the case's
+    activation dtype; norm_eps is the model's (gpt-oss 1e-5, qwen35moe
+    1e-6).  The layer's own "x" is left as it is."""
+    T, H = c.T, c.H
+    scale = 2.0 ** (range_bytes("resid_scale", (1, max(T, 1)), 0, 8, seed)[0, :T].astype(np.float32) - 3.0)
+    r = normal("resid", (T, H), 1.0, "f32", seed) * scale[:, None]
+    g = normal("norm_w", (1, H), 0.1, "f32", seed)[0] + np.float32(1.0)
+    if c.x_dtype == "bf16":
+        r, g = bf16_bits(r), bf16_bits(g)
+    c.t["resid"] = np.ascontiguousarray(r)
+    c.t["norm_w"] = np.ascontiguousarray(g)
+    c.norm_eps = 1e-5 if c.gating == "topk_softmax" else 1e-6
+    return c
 
 
 def make_case(name: str, T: int | None = None, **kw) -> Case:
