@@ -188,6 +188,25 @@ int moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, int3
                 float* logits, int32_t* topk_idx, float* topk_w, float* sgate, void* ws,
                 size_t ws_bytes, hipStream_t stream);
 
+/* The layer inside its pre-norm decoder block, with the norm in front and
+ * the residual add behind it ("qwen35moe - Forward-Pass Design (Pantheon
+ * port)", section "Block scaffold": every norm is an RMS norm and the
+ * residual adds the un-normalised input; "Phase 19: MoE - gpt-oss-20b",
+ * section 2: RMSNorm with the variance in fp32, out = h + moe(post_norm(h))):
+ *   xn[t]  = resid[t] * norm_w / sqrt(mean(resid[t]^2) + norm_eps)
+ *            (fp32 statistics, rounded once to x_dtype)
+ *   out[t] = resid[t] + layer(xn)[t]          (fp32; the layer as moe_forward)
+ *   norm_w   [H] x_dtype (post_attention_norm / ffn_norm weight)
+ *   norm_eps 1e-6 (qwen35moe), 1e-5 (gpt-oss); 0 <= norm_eps <= 1
+ *   resid    [T][H] x_dtype, the un-normalised residual stream
+ *   xn       NULL, or [T][H] x_dtype output: the normalised rows the layer
+ *            read; must not overlap resid (else they live in ws)
+ *   out      [T][H] fp32, fully overwritten; must not overlap resid or xn
+ *   logits, topk_idx, topk_w, sgate, ws: as in moe_forward. */
+int moe_forward_prenorm(const moe_config* cfg, const moe_weights* w, const void* norm_w, float norm_eps,
+                        const void* resid, int32_t T, float* out, void* xn, float* logits, int32_t* topk_idx,
+                        float* topk_w, float* sgate, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* MXFP8 rounding as act_quant applies it (OCP MX v1.0, section 6.3):
  *   x      [rows][K] bf16, K a multiple of 32
  *   codes  [rows][K] uint8 E4M3 codes

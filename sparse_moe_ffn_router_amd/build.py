@@ -17,7 +17,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "route.hip", "permute.hip", "ffn_gemv.hip", "ffn_gemv_mx.hip", "ffn_mfma.hip", "mxfp8.hip"]
+SOURCES = ["api.hip", "route.hip", "permute.hip", "ffn_gemv.hip", "ffn_gemv_mx.hip", "ffn_mfma.hip", "mxfp8.hip", "norm.hip"]
 CFLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,

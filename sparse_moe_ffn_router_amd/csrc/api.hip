@@ -79,6 +79,8 @@ int make_plan(const moe_config* c, int32_t T, Plan* p) {
   }
   p->off_aqx = o; o += p->aqx_bytes;
   p->off_aqh = o; o += p->aqh_bytes;
+  // moe_forward_prenorm: the normalised rows when the caller does not take them
+  p->off_xn = o; o += up256((size_t)T * c->hidden * p->elem_x);
   p->total = o;
   // the few-token kernels address activations and h with 32-bit buffer offsets
   const size_t act_bytes = (size_t)(p->n_assign * c->expert_ff + (p->shared ? (int64_t)T * c->shared_ff : 0)) * p->elem_x;
@@ -136,6 +138,43 @@ static hipError_t down_aq(const moe_config* c, const moe_weights* w, const Plan&
   if ((e = launch_mxfp8_values((const uint16_t*)h, p.n_assign, c->expert_ff, (uint16_t*)aq, s)) != hipSuccess)
     return e;
   return launch_down(c, w, aq, offsets, sorted, T, y, s);
+}
+
+// The layer's launch sequence on checked arguments: route, permute, expert
+// FFN, down, combine (+ resid rows when given).
+static int forward_steps(const moe_config* cfg, const moe_weights* w, const Plan& p, const void* x,
+                         const void* resid, int32_t T, float* out, float* logits, int32_t* topk_idx, float* topk_w,
+                         float* sgate, char* b, hipStream_t stream) {
+  float* lg = logits ? logits : (float*)(b + p.off_logits);
+  int32_t* idx = topk_idx ? topk_idx : (int32_t*)(b + p.off_idx);
+  float* wt = topk_w ? topk_w : (float*)(b + p.off_w);
+  float* sg = p.shared ? (sgate ? sgate : (float*)(b + p.off_sgate)) : nullptr;
+  int32_t* offsets = (int32_t*)(b + p.off_offsets);
+  int32_t* sorted = (int32_t*)(b + p.off_sorted);
+  int32_t* pos = (int32_t*)(b + p.off_pos);
+  int32_t* perm = (int32_t*)(b + p.off_perm);
+  void* h = b + p.off_h;
+  void* y = b + p.off_y;
+  // MFMA router product split over K ranges, summed by the gating kernel
+  float* part = (p.nsplit > 1 && w->router_w) ? (float*)(b + p.off_part) : nullptr;
+  hipError_t e;
+  if ((e = launch_router_logits(cfg, w, x, T, lg, sg, stream, part)) != hipSuccess) return MOE_EHIP;
+  if (can_fuse_gate_permute(T)) {
+    if ((e = launch_gate_permute(cfg, lg, sg, T, idx, wt, sg, offsets, sorted, pos, stream)) != hipSuccess)
+      return MOE_EHIP;
+  } else {
+    if ((e = launch_gating(cfg, w, x, lg, sg, T, idx, wt, sg, stream, part, part ? p.nsplit : 1)) != hipSuccess)
+      return MOE_EHIP;
+    if ((e = launch_permute(cfg, idx, T, offsets, sorted, pos, perm, stream)) != hipSuccess) return MOE_EHIP;
+  }
+  if (cfg->act_quant == MOE_ACT_QUANT_MXFP8) {
+    if ((e = expert_ffn_aq(cfg, w, p, x, offsets, sorted, T, h, b + p.off_aqx, stream)) != hipSuccess) return MOE_EHIP;
+    if ((e = down_aq(cfg, w, p, h, offsets, sorted, T, y, b + p.off_aqh, stream)) != hipSuccess) return MOE_EHIP;
+  } else {
+    if ((e = launch_expert_ffn(cfg, w, x, offsets, sorted, T, h, stream)) != hipSuccess) return MOE_EHIP;
+    if ((e = launch_down(cfg, w, h, offsets, sorted, T, y, stream)) != hipSuccess) return MOE_EHIP;
+  }
+  return hip_status(launch_combine_gather(cfg, y, wt, sg, T, out, stream, resid));
 }
 
 }  // namespace moe
@@ -251,37 +290,27 @@ int moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, int3
   if (!w->router_w && !logits) return MOE_EINVAL;
   if (logits && !aligned16(logits)) return MOE_EINVAL;
   if (!ws || ws_bytes < p.total || ((uintptr_t)ws & 255u)) return MOE_EWORKSPACE;
+  return forward_steps(cfg, w, p, x, nullptr, T, out, logits, topk_idx, topk_w, sgate, (char*)ws, stream);
+}
+
+int moe_forward_prenorm(const moe_config* cfg, const moe_weights* w, const void* norm_w, float norm_eps,
+                        const void* resid, int32_t T, float* out, void* xn, float* logits, int32_t* topk_idx,
+                        float* topk_w, float* sgate, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Plan p;
+  int st = make_plan(cfg, T, &p);
+  if (st) return st;
+  if ((st = weights_ok(cfg, w, true, true))) return st;
+  if (!(norm_eps >= 0.f) || norm_eps > 1.f) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!norm_w || !resid || !out || !aligned16(norm_w) || !aligned16(resid) || !aligned16(out)) return MOE_EINVAL;
+  if (xn && !aligned16(xn)) return MOE_EINVAL;
+  if (!w->router_w && !logits) return MOE_EINVAL;
+  if (logits && !aligned16(logits)) return MOE_EINVAL;
+  if (!ws || ws_bytes < p.total || ((uintptr_t)ws & 255u)) return MOE_EWORKSPACE;
   char* b = (char*)ws;
-  float* lg = logits ? logits : (float*)(b + p.off_logits);
-  int32_t* idx = topk_idx ? topk_idx : (int32_t*)(b + p.off_idx);
-  float* wt = topk_w ? topk_w : (float*)(b + p.off_w);
-  float* sg = p.shared ? (sgate ? sgate : (float*)(b + p.off_sgate)) : nullptr;
-  int32_t* offsets = (int32_t*)(b + p.off_offsets);
-  int32_t* sorted = (int32_t*)(b + p.off_sorted);
-  int32_t* pos = (int32_t*)(b + p.off_pos);
-  int32_t* perm = (int32_t*)(b + p.off_perm);
-  void* h = b + p.off_h;
-  void* y = b + p.off_y;
-  // MFMA router product split over K ranges, summed by the gating kernel
-  float* part = (p.nsplit > 1 && w->router_w) ? (float*)(b + p.off_part) : nullptr;
-  hipError_t e;
-  if ((e = launch_router_logits(cfg, w, x, T, lg, sg, stream, part)) != hipSuccess) return MOE_EHIP;
-  if (can_fuse_gate_permute(T)) {
-    if ((e = launch_gate_permute(cfg, lg, sg, T, idx, wt, sg, offsets, sorted, pos, stream)) != hipSuccess)
-      return MOE_EHIP;
-  } else {
-    if ((e = launch_gating(cfg, w, x, lg, sg, T, idx, wt, sg, stream, part, part ? p.nsplit : 1)) != hipSuccess)
-      return MOE_EHIP;
-    if ((e = launch_permute(cfg, idx, T, offsets, sorted, pos, perm, stream)) != hipSuccess) return MOE_EHIP;
-  }
-  if (cfg->act_quant == MOE_ACT_QUANT_MXFP8) {
-    if ((e = expert_ffn_aq(cfg, w, p, x, offsets, sorted, T, h, b + p.off_aqx, stream)) != hipSuccess) return MOE_EHIP;
-    if ((e = down_aq(cfg, w, p, h, offsets, sorted, T, y, b + p.off_aqh, stream)) != hipSuccess) return MOE_EHIP;
-  } else {
-    if ((e = launch_expert_ffn(cfg, w, x, offsets, sorted, T, h, stream)) != hipSuccess) return MOE_EHIP;
-    if ((e = launch_down(cfg, w, h, offsets, sorted, T, y, stream)) != hipSuccess) return MOE_EHIP;
-  }
-  return hip_status(launch_combine_gather(cfg, y, wt, sg, T, out, stream));
+  void* x = xn ? xn : b + p.off_xn;
+  if (launch_rmsnorm(cfg, resid, norm_w, norm_eps, T, x, stream) != hipSuccess) return MOE_EHIP;
+  return forward_steps(cfg, w, p, x, resid, T, out, logits, topk_idx, topk_w, sgate, b, stream);
 }
 
 }  // extern "C"

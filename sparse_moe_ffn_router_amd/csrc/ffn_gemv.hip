@@ -401,10 +401,13 @@ template <> __device__ __forceinline__ float4 load_y4<uint16_t>(const uint16_t* 
   return make_float4(bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y));
 }
 
+// rdt: residual rows added last (the decoder block's residual): 0 none,
+// 1 bf16, 2 fp32.
 template <typename YT>
 __global__ __launch_bounds__(256) void k_combine_gather(const YT* __restrict__ y, const float* __restrict__ topk_w,
                                                         const float* __restrict__ sgate, int32_t T, int32_t k,
-                                                        int32_t H, float* __restrict__ out) {
+                                                        int32_t H, float* __restrict__ out,
+                                                        const void* __restrict__ resid, int32_t rdt) {
   constexpr int kBatch = 8;
   const int t = blockIdx.y;
   const int o4 = blockIdx.x * blockDim.x + threadIdx.x;  // index of 4 outputs
@@ -416,6 +419,13 @@ __global__ __launch_bounds__(256) void k_combine_gather(const YT* __restrict__ y
   if (sgate) {
     g = sgate[t];
     vs = load_y4<YT>(y, (size_t)T * k + t, o4, H);
+  }
+  float4 res = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (rdt == 1) {
+    const uint2 v = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(resid) + (size_t)t * H)[o4];
+    res = make_float4(bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y));
+  } else if (rdt == 2) {
+    res = reinterpret_cast<const float4*>(static_cast<const float*>(resid) + (size_t)t * H)[o4];
   }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j0 = 0; j0 < k; j0 += kBatch) {
@@ -442,6 +452,12 @@ __global__ __launch_bounds__(256) void k_combine_gather(const YT* __restrict__ y
     acc.y = fmaf(g, vs.y, acc.y);
     acc.z = fmaf(g, vs.z, acc.z);
     acc.w = fmaf(g, vs.w, acc.w);
+  }
+  if (rdt) {
+    acc.x = res.x + acc.x;
+    acc.y = res.y + acc.y;
+    acc.z = res.z + acc.z;
+    acc.w = res.w + acc.w;
   }
   reinterpret_cast<float4*>(out + (size_t)t * H)[o4] = acc;
 }
@@ -562,16 +578,19 @@ hipError_t launch_down(const moe_config* c, const moe_weights* w, const void* h,
 }
 
 hipError_t launch_combine_gather(const moe_config* c, const void* y, const float* topk_w, const float* sgate,
-                                 int32_t T, float* out, hipStream_t s) {
+                                 int32_t T, float* out, hipStream_t s, const void* resid) {
   if (T == 0) return hipSuccess;
   // few tokens: 64-thread workgroups, so the loads spread over more CUs
   const int threads = T <= kGemvMaxT ? 64 : 256;
   dim3 grid((c->hidden / 4 + threads - 1) / threads, T);
   const float* sg = c->shared_ff > 0 ? sgate : nullptr;
+  const int rdt = !resid ? 0 : c->x_dtype == MOE_DTYPE_BF16 ? 1 : 2;
   if (y_is_bf16(c, T))
-    k_combine_gather<uint16_t><<<grid, threads, 0, s>>>((const uint16_t*)y, topk_w, sg, T, c->top_k, c->hidden, out);
+    k_combine_gather<uint16_t><<<grid, threads, 0, s>>>((const uint16_t*)y, topk_w, sg, T, c->top_k, c->hidden, out,
+                                                        resid, rdt);
   else
-    k_combine_gather<float><<<grid, threads, 0, s>>>((const float*)y, topk_w, sg, T, c->top_k, c->hidden, out);
+    k_combine_gather<float><<<grid, threads, 0, s>>>((const float*)y, topk_w, sg, T, c->top_k, c->hidden, out,
+                                                     resid, rdt);
   return hipGetLastError();
 }
 

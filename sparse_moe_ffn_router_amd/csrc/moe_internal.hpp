@@ -139,7 +139,7 @@ struct Plan {
   int nseg;           // E (+1)
   size_t elem_x;      // bytes per activation / h element
   size_t off_logits, off_idx, off_w, off_sgate, off_offsets, off_sorted, off_pos;
-  size_t off_perm, off_h, off_y, off_part, off_aqx, off_aqh, total;
+  size_t off_perm, off_h, off_y, off_part, off_aqx, off_aqh, off_xn, total;
   int32_t nsplit;     // router split-K ranges (1: none)
   size_t perm_bytes, y_bytes;  // scratch needed by moe_permute / moe_combine alone
   // act_quant: rounded x (moe_expert_ffn's scratch) and rounded h (after y in
@@ -180,8 +180,12 @@ hipError_t launch_expert_ffn(const moe_config* c, const moe_weights* w, const vo
 bool y_is_bf16(const moe_config* c, int32_t T);
 hipError_t launch_down(const moe_config* c, const moe_weights* w, const void* h, const int32_t* offsets,
                        const int32_t* sorted_assign, int32_t T, void* y, hipStream_t s);
+// resid: NULL, or [T][H] x_dtype rows added to out (the block's residual).
 hipError_t launch_combine_gather(const moe_config* c, const void* y, const float* topk_w, const float* sgate,
-                                 int32_t T, float* out, hipStream_t s);
+                                 int32_t T, float* out, hipStream_t s, const void* resid = nullptr);
+// RMSNorm of T rows of x ([T][H] x_dtype) with weight g [H] into y (norm.hip).
+hipError_t launch_rmsnorm(const moe_config* c, const void* x, const void* g, float eps, int32_t T, void* y,
+                          hipStream_t s);
 // MXFP8 rounding of bf16 rows [rows][K] (mxfp8.hip): E4M3 codes + E8M0
 // scales (row stride mx8_scale_stride(K) bytes), or the rounded bf16 values.
 int mx8_scale_stride(int K);

@@ -20,7 +20,8 @@ def _declared():
 
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn",
-                                  "moe_combine", "moe_forward", "moe_quantize_mxfp8", "moe_status_string"])
+                                  "moe_combine", "moe_forward", "moe_forward_prenorm", "moe_quantize_mxfp8",
+                                  "moe_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -125,6 +126,17 @@ def test_entry_points_reject_bad_arguments_before_launch():
     nr = moe._Weights(*([fake] * len(moe._WEIGHT_FIELDS)))
     nr.router_w = None
     assert _raw("moe_forward", cb, ctypes.byref(nr), fake, 8, fake, None, None, None, None, fake, need, None) == moe.MOE_EINVAL
+    # the pre-norm block: norm weight, residual and a sane eps are required
+    pre = lambda nw, eps, r, T, out, xn, ws, nb: _raw("moe_forward_prenorm", cb, fb, nw, ctypes.c_float(eps), r, T,
+                                                      out, xn, None, None, None, None, ws, nb, None)
+    assert pre(None, 1e-6, None, 0, None, None, None, 0) == moe.MOE_OK                   # T = 0
+    assert pre(None, 1e-6, fake, 8, fake, None, fake, need) == moe.MOE_EINVAL          # no norm weight
+    assert pre(fake, 1e-6, None, 8, fake, None, fake, need) == moe.MOE_EINVAL          # no residual
+    assert pre(fake, -1.0, fake, 8, fake, None, fake, need) == moe.MOE_EINVAL          # negative eps
+    assert pre(fake, float("nan"), fake, 8, fake, None, fake, need) == moe.MOE_EINVAL  # NaN eps
+    assert pre(fake, 1e-6, fake + 8, 8, fake, None, fake, need) == moe.MOE_EINVAL      # misaligned residual
+    assert pre(fake, 1e-6, fake, 8, fake, fake + 2, fake, need) == moe.MOE_EINVAL      # misaligned xn
+    assert pre(fake, 1e-6, fake, 4096, fake, None, fake, need - 1) == moe.MOE_EWORKSPACE
     # unsupported combination
     c2 = _cfg(w_dtype=moe.DTYPE_MXFP4)._c()
     assert _raw("moe_route", ctypes.byref(c2), fb, fake, fake, fake, fake, fake, 8, None, 0, None) == moe.MOE_EUNSUPPORTED
