@@ -104,6 +104,26 @@ class Layer:
         self.moe.moe_forward(self.cfg, self.weights[step % len(self.weights)], self.x, self.T, self.out, self.ws,
                              logits=self.logits, topk_idx=self.idx, topk_w=self.wt, sgate=self.sg)
 
+    def block(self, step):
+        """The layer inside its pre-norm block (RMSNorm in front, residual add
+        behind) on residual rows of the same batch size."""
+        if not hasattr(self, "resid"):
+            import synth
+            from tests._gpu import to_torch
+            synth.add_block_inputs(self.case)
+            self.resid = to_torch(self.case.t["resid"])
+            self.norm_w = to_torch(self.case.t["norm_w"])
+            self.xn = torch_empty_like(self.x)
+        self.moe.moe_forward_prenorm(self.cfg, self.weights[step % len(self.weights)], self.norm_w,
+                                     self.case.norm_eps, self.resid, self.T, self.out, self.ws, xn=self.xn,
+                                     logits=self.logits, topk_idx=self.idx, topk_w=self.wt, sgate=self.sg)
+
+    def forward_on_xn(self, step):
+        """The plain layer on the normalised rows the block produced (the
+        same routing, so the block's own cost shows)."""
+        self.moe.moe_forward(self.cfg, self.weights[step % len(self.weights)], self.xn, self.T, self.out, self.ws,
+                             logits=self.logits, topk_idx=self.idx, topk_w=self.wt, sgate=self.sg)
+
     def ops(self, step, ev_ffn=None):
         """The same kernels through the four step entry points; optional
         events bracket the expert gate/up launch."""
@@ -116,6 +136,11 @@ class Layer:
         if ev_ffn:
             ev_ffn[1].record()
         m.moe_combine(self.cfg, w, self.h, self.offsets, self.sorted, self.wt, self.sg, self.T, self.out, self.ws)
+
+
+def torch_empty_like(t):
+    import torch
+    return torch.empty_like(t)
 
 
 def time_loop(fn, steps, warmup):
@@ -287,6 +312,11 @@ def main():
     log("decode: %.4f ms/step, %.0f tokens/s, %d active experts" % (ms, tok_s, n_active))
     g_ms = graph_replay_ms(layer, a.steps, a.warmup)
     log("decode, HIP graph replay: %.4f ms/step" % g_ms)
+    b_ms, _ = time_loop(layer.block, a.steps, a.warmup)
+    b_active = active_experts(layer.idx.cpu().numpy(), dec.E)
+    bx_ms, _ = time_loop(layer.forward_on_xn, a.steps, a.warmup)
+    log("decode, pre-norm block (RMSNorm + layer + residual): %.4f ms/step; the layer alone on the same "
+        "normalised rows %.4f ms (%d active experts)" % (b_ms, bx_ms, b_active))
 
     # dominant kernel (expert gate/up), timed with events on the launch stream
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
@@ -324,6 +354,11 @@ def main():
                    "layer_frac_hbm": round(layer_gbs / HBM_PEAK_GBS, 4), "wall_s": round(wall, 3)},
         "graph_replay": {"ms_per_step": round(g_ms, 5), "tokens_per_s": round(dec.T / (g_ms * 1e-3), 1),
                          "note": "the same moe_forward pass captured once per weight copy in a HIP graph"},
+        "prenorm_block": {"ms_per_step": round(b_ms, 5), "tokens_per_s": round(dec.T / (b_ms * 1e-3), 1),
+                          "layer_on_same_rows_ms": round(bx_ms, 5), "over_layer_ms": round(b_ms - bx_ms, 5),
+                          "active_experts": b_active,
+                          "note": "moe_forward_prenorm on residual rows (RMSNorm in the router-product kernel, "
+                                  "residual add in the combine) against moe_forward on the rows it normalised"},
         "roofline": roofline,
     }
     del layer

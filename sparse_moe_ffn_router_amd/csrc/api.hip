@@ -140,10 +140,20 @@ static hipError_t down_aq(const moe_config* c, const moe_weights* w, const Plan&
   return launch_down(c, w, aq, offsets, sorted, T, y, s);
 }
 
+// The pre-norm block's prologue and epilogue: norm weight, eps and the
+// residual rows (which the layer's input x is normalised from).
+struct PreNorm {
+  const void* g;
+  float eps;
+  const void* resid;
+};
+
 // The layer's launch sequence on checked arguments: route, permute, expert
-// FFN, down, combine (+ resid rows when given).
+// FFN, down, combine.  With pn, x is where the normalised rows go: few
+// tokens normalise inside the router-product kernel, larger batches in an
+// RMSNorm launch of their own; the combine adds pn->resid.
 static int forward_steps(const moe_config* cfg, const moe_weights* w, const Plan& p, const void* x,
-                         const void* resid, int32_t T, float* out, float* logits, int32_t* topk_idx, float* topk_w,
+                         const PreNorm* pn, int32_t T, float* out, float* logits, int32_t* topk_idx, float* topk_w,
                          float* sgate, char* b, hipStream_t stream) {
   float* lg = logits ? logits : (float*)(b + p.off_logits);
   int32_t* idx = topk_idx ? topk_idx : (int32_t*)(b + p.off_idx);
@@ -158,7 +168,14 @@ static int forward_steps(const moe_config* cfg, const moe_weights* w, const Plan
   // MFMA router product split over K ranges, summed by the gating kernel
   float* part = (p.nsplit > 1 && w->router_w) ? (float*)(b + p.off_part) : nullptr;
   hipError_t e;
-  if ((e = launch_router_logits(cfg, w, x, T, lg, sg, stream, part)) != hipSuccess) return MOE_EHIP;
+  if (pn && router_norm_fusable(cfg, w, T)) {
+    e = launch_router_logits_norm(cfg, w, pn->resid, pn->g, pn->eps, T, const_cast<void*>(x), lg, sg, stream);
+  } else {
+    if (pn && (e = launch_rmsnorm(cfg, pn->resid, pn->g, pn->eps, T, const_cast<void*>(x), stream)) != hipSuccess)
+      return MOE_EHIP;
+    e = launch_router_logits(cfg, w, x, T, lg, sg, stream, part);
+  }
+  if (e != hipSuccess) return MOE_EHIP;
   if (can_fuse_gate_permute(T)) {
     if ((e = launch_gate_permute(cfg, lg, sg, T, idx, wt, sg, offsets, sorted, pos, stream)) != hipSuccess)
       return MOE_EHIP;
@@ -174,7 +191,7 @@ static int forward_steps(const moe_config* cfg, const moe_weights* w, const Plan
     if ((e = launch_expert_ffn(cfg, w, x, offsets, sorted, T, h, stream)) != hipSuccess) return MOE_EHIP;
     if ((e = launch_down(cfg, w, h, offsets, sorted, T, y, stream)) != hipSuccess) return MOE_EHIP;
   }
-  return hip_status(launch_combine_gather(cfg, y, wt, sg, T, out, stream, resid));
+  return hip_status(launch_combine_gather(cfg, y, wt, sg, T, out, stream, pn ? pn->resid : nullptr));
 }
 
 }  // namespace moe
@@ -308,9 +325,8 @@ int moe_forward_prenorm(const moe_config* cfg, const moe_weights* w, const void*
   if (logits && !aligned16(logits)) return MOE_EINVAL;
   if (!ws || ws_bytes < p.total || ((uintptr_t)ws & 255u)) return MOE_EWORKSPACE;
   char* b = (char*)ws;
-  void* x = xn ? xn : b + p.off_xn;
-  if (launch_rmsnorm(cfg, resid, norm_w, norm_eps, T, x, stream) != hipSuccess) return MOE_EHIP;
-  return forward_steps(cfg, w, p, x, resid, T, out, logits, topk_idx, topk_w, sgate, b, stream);
+  const PreNorm pn = {norm_w, norm_eps, resid};
+  return forward_steps(cfg, w, p, xn ? xn : b + p.off_xn, &pn, T, out, logits, topk_idx, topk_w, sgate, b, stream);
 }
 
 }  // extern "C"

@@ -401,13 +401,15 @@ template <> __device__ __forceinline__ float4 load_y4<uint16_t>(const uint16_t* 
   return make_float4(bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y));
 }
 
-// rdt: residual rows added last (the decoder block's residual): 0 none,
-// 1 bf16, 2 fp32.
-template <typename YT>
+// RD: residual rows added last (the decoder block's residual): 0 none,
+// 1 bf16, 2 fp32 (a template parameter: a runtime choice between two
+// loads made the wave wait for one before issuing the y loads).
+// SH: a shared expert (its row and gate), likewise a template parameter.
+template <typename YT, int RD, bool SH>
 __global__ __launch_bounds__(256) void k_combine_gather(const YT* __restrict__ y, const float* __restrict__ topk_w,
                                                         const float* __restrict__ sgate, int32_t T, int32_t k,
                                                         int32_t H, float* __restrict__ out,
-                                                        const void* __restrict__ resid, int32_t rdt) {
+                                                        const void* __restrict__ resid) {
   constexpr int kBatch = 8;
   const int t = blockIdx.y;
   const int o4 = blockIdx.x * blockDim.x + threadIdx.x;  // index of 4 outputs
@@ -416,16 +418,18 @@ __global__ __launch_bounds__(256) void k_combine_gather(const YT* __restrict__ y
   // round trip for k <= 8) and added last
   float g = 0.f;
   float4 vs = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (sgate) {
+  if constexpr (SH) {
     g = sgate[t];
     vs = load_y4<YT>(y, (size_t)T * k + t, o4, H);
   }
-  float4 res = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (rdt == 1) {
+  // raw residual bits, converted only where they are added: a conversion
+  // right after the load would make the wave wait for it before the y loads
+  uint4 rraw = make_uint4(0, 0, 0, 0);
+  if constexpr (RD == 1) {
     const uint2 v = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(resid) + (size_t)t * H)[o4];
-    res = make_float4(bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y));
-  } else if (rdt == 2) {
-    res = reinterpret_cast<const float4*>(static_cast<const float*>(resid) + (size_t)t * H)[o4];
+    rraw = make_uint4(v.x, v.y, 0, 0);
+  } else if constexpr (RD == 2) {
+    rraw = reinterpret_cast<const uint4*>(static_cast<const float*>(resid) + (size_t)t * H)[o4];
   }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j0 = 0; j0 < k; j0 += kBatch) {
@@ -447,13 +451,16 @@ __global__ __launch_bounds__(256) void k_combine_gather(const YT* __restrict__ y
       }
     }
   }
-  if (sgate) {
+  if constexpr (SH) {
     acc.x = fmaf(g, vs.x, acc.x);
     acc.y = fmaf(g, vs.y, acc.y);
     acc.z = fmaf(g, vs.z, acc.z);
     acc.w = fmaf(g, vs.w, acc.w);
   }
-  if (rdt) {
+  if constexpr (RD != 0) {
+    const float4 res = RD == 1 ? make_float4(bf16lo(rraw.x), bf16hi(rraw.x), bf16lo(rraw.y), bf16hi(rraw.y))
+                               : make_float4(__uint_as_float(rraw.x), __uint_as_float(rraw.y),
+                                             __uint_as_float(rraw.z), __uint_as_float(rraw.w));
     acc.x = res.x + acc.x;
     acc.y = res.y + acc.y;
     acc.z = res.z + acc.z;
@@ -577,6 +584,26 @@ hipError_t launch_down(const moe_config* c, const moe_weights* w, const void* h,
   return hipGetLastError();
 }
 
+template <typename YT, bool SH>
+static void combine_launch_sh(int rd, dim3 grid, int threads, hipStream_t s, const YT* y, const float* topk_w,
+                              const float* sg, int32_t T, int32_t k, int32_t H, float* out, const void* resid) {
+  if (rd == 1)
+    k_combine_gather<YT, 1, SH><<<grid, threads, 0, s>>>(y, topk_w, sg, T, k, H, out, resid);
+  else if (rd == 2)
+    k_combine_gather<YT, 2, SH><<<grid, threads, 0, s>>>(y, topk_w, sg, T, k, H, out, resid);
+  else
+    k_combine_gather<YT, 0, SH><<<grid, threads, 0, s>>>(y, topk_w, sg, T, k, H, out, resid);
+}
+
+template <typename YT>
+static void combine_launch(int rd, dim3 grid, int threads, hipStream_t s, const void* y, const float* topk_w,
+                           const float* sg, int32_t T, int32_t k, int32_t H, float* out, const void* resid) {
+  if (sg)
+    combine_launch_sh<YT, true>(rd, grid, threads, s, (const YT*)y, topk_w, sg, T, k, H, out, resid);
+  else
+    combine_launch_sh<YT, false>(rd, grid, threads, s, (const YT*)y, topk_w, sg, T, k, H, out, resid);
+}
+
 hipError_t launch_combine_gather(const moe_config* c, const void* y, const float* topk_w, const float* sgate,
                                  int32_t T, float* out, hipStream_t s, const void* resid) {
   if (T == 0) return hipSuccess;
@@ -584,13 +611,11 @@ hipError_t launch_combine_gather(const moe_config* c, const void* y, const float
   const int threads = T <= kGemvMaxT ? 64 : 256;
   dim3 grid((c->hidden / 4 + threads - 1) / threads, T);
   const float* sg = c->shared_ff > 0 ? sgate : nullptr;
-  const int rdt = !resid ? 0 : c->x_dtype == MOE_DTYPE_BF16 ? 1 : 2;
+  const int rd = !resid ? 0 : c->x_dtype == MOE_DTYPE_BF16 ? 1 : 2;
   if (y_is_bf16(c, T))
-    k_combine_gather<uint16_t><<<grid, threads, 0, s>>>((const uint16_t*)y, topk_w, sg, T, c->top_k, c->hidden, out,
-                                                        resid, rdt);
+    combine_launch<uint16_t>(rd, grid, threads, s, y, topk_w, sg, T, c->top_k, c->hidden, out, resid);
   else
-    k_combine_gather<float><<<grid, threads, 0, s>>>((const float*)y, topk_w, sg, T, c->top_k, c->hidden, out,
-                                                     resid, rdt);
+    combine_launch<float>(rd, grid, threads, s, y, topk_w, sg, T, c->top_k, c->hidden, out, resid);
   return hipGetLastError();
 }
 

@@ -117,6 +117,46 @@ __device__ __forceinline__ int gate_token(const float* __restrict__ l, int E, in
 
 constexpr int kRouterTokens = 8;  // tokens per pass of a wave
 
+// RMSNorm element helpers (the pre-norm block's prologue): sum of squares
+// of one 16-byte piece, and a piece scaled by the row factor r and the norm
+// weight, rounded to the activation type (x * r first, then * weight).
+__device__ __forceinline__ float sumsq4(uint4 v, uint16_t) {
+  float s = 0.f;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s = fmaf(bf16lo(w[i]), bf16lo(w[i]), s);
+    s = fmaf(bf16hi(w[i]), bf16hi(w[i]), s);
+  }
+  return s;
+}
+__device__ __forceinline__ float sumsq4(uint4 v, float) {
+  float s = 0.f;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s = fmaf(__uint_as_float(w[i]), __uint_as_float(w[i]), s);
+  return s;
+}
+
+__device__ __forceinline__ uint4 scale4(uint4 v, uint4 g, float r, uint16_t) {
+  const uint32_t a[4] = {v.x, v.y, v.z, v.w}, b[4] = {g.x, g.y, g.z, g.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // gfx950 converts a pair to bf16 in one instruction, nearest-even
+    const bf16x2_t p = {(__bf16)(bf16lo(a[i]) * r * bf16lo(b[i])), (__bf16)(bf16hi(a[i]) * r * bf16hi(b[i]))};
+    o[i] = __builtin_bit_cast(uint32_t, p);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+__device__ __forceinline__ uint4 scale4(uint4 v, uint4 g, float r, float) {
+  return make_uint4(__float_as_uint(__uint_as_float(v.x) * r * __uint_as_float(g.x)),
+                    __float_as_uint(__uint_as_float(v.y) * r * __uint_as_float(g.y)),
+                    __float_as_uint(__uint_as_float(v.z) * r * __uint_as_float(g.z)),
+                    __float_as_uint(__uint_as_float(v.w) * r * __uint_as_float(g.w)));
+}
+
+
 template <typename XT> struct RouterVec;
 template <> struct RouterVec<uint16_t> {
   static constexpr int N = 8;
@@ -190,6 +230,97 @@ __device__ __forceinline__ void router_row(const XT* __restrict__ x, const XT* _
       float v = acc[0];
 #pragma unroll
       for (int j = 1; j < kRouterTokens; ++j) v = lane == j ? acc[j] : v;
+      if (r < E)
+        logits[(size_t)(t0 + lane) * E + r] = v + bias;
+      else
+        sgate_pre[t0 + lane] = v;
+    }
+  }
+}
+
+// router_row with the pre-norm block's RMSNorm folded in: x holds the
+// un-normalised rows, g the norm weight.  A whole row (P 16-byte pieces per
+// lane, P * 64 >= H / (16 / sizeof(XT))) is held in registers, so each
+// token's factor 1 / sqrt(mean(x^2) + eps) comes from the pieces already
+// loaded for the product, and each piece is normalised and rounded to the
+// activation type before it is multiplied -- the same values, sums and
+// order as the RMSNorm kernel followed by router_row, so the logits are
+// bit-equal to those.  The weight row and g stay in registers over all
+// tokens; tokens go in groups of TG (PF: the next group's rows load while
+// the current group's sums are reduced, for widths where the registers
+// allow it).  Wave `wave` of `nwaves` also
+// stores the normalised rows t with t % nwaves == wave to xn for the expert
+// kernels.
+template <typename XT, int P, int TG, bool PF>
+__device__ __forceinline__ void router_row_norm(const XT* __restrict__ x, const XT* __restrict__ wr,
+                                                const XT* __restrict__ br, const XT* __restrict__ wsg,
+                                                const XT* __restrict__ g, float eps, int T, int H, int E, int r,
+                                                float* __restrict__ logits, float* __restrict__ sgate_pre,
+                                                XT* __restrict__ xn, int wave, int nwaves) {
+  constexpr int N = RouterVec<XT>::N;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int np = H / N;
+  const uint4* wrow = reinterpret_cast<const uint4*>(r < E ? wr + (size_t)r * H : wsg);
+  const uint4* grow = reinterpret_cast<const uint4*>(g);
+  uint4 w[P], gv[P], xv[TG][P];
+  auto load_group = [&](int t0) {
+#pragma unroll
+    for (int j = 0; j < TG; ++j) {
+      const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)min(t0 + j, T - 1) * H);
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        const int pc = lane + i * kWave;
+        xv[j][i] = pc < np ? xr[pc] : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int pc = lane + i * kWave;
+    w[i] = pc < np ? wrow[pc] : make_uint4(0, 0, 0, 0);
+    gv[i] = pc < np ? grow[pc] : make_uint4(0, 0, 0, 0);
+  }
+  load_group(0);
+  // after the row loads, so that its wait (layers with a router bias) comes
+  // with theirs at the loop entry
+  const float bias = (r < E && br) ? RouterVec<XT>::scalar(br, r) : 0.f;
+  for (int t0 = 0; t0 < T; t0 += TG) {
+    if constexpr (!PF) {
+      if (t0 > 0) load_group(t0);
+    }
+    float acc[TG];
+#pragma unroll
+    for (int j = 0; j < TG; ++j) {
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < P; ++i) ss += sumsq4(xv[j][i], XT());
+      ss = wave_sum(ss);
+      const float rj = 1.f / sqrtf(ss / (float)H + eps);
+      acc[j] = 0.f;
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        xv[j][i] = scale4(xv[j][i], gv[i], rj, XT());
+        acc[j] = RouterVec<XT>::dot(w[i], xv[j][i], acc[j]);
+      }
+      const int t = t0 + j;
+      if (t < T && t % nwaves == wave) {
+        uint4* yr = reinterpret_cast<uint4*>(xn + (size_t)t * H);
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+          const int pc = lane + i * kWave;
+          if (pc < np) yr[pc] = xv[j][i];
+        }
+      }
+    }
+    if constexpr (PF) {
+      if (t0 + TG < T) load_group(t0 + TG);
+    }
+#pragma unroll
+    for (int j = 0; j < TG; ++j) acc[j] = wave_sum(acc[j]);
+    if (lane < TG && t0 + lane < T) {
+      float v = acc[0];
+#pragma unroll
+      for (int j = 1; j < TG; ++j) v = lane == j ? acc[j] : v;
       if (r < E)
         logits[(size_t)(t0 + lane) * E + r] = v + bias;
       else

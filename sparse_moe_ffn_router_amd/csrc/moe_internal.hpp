@@ -183,6 +183,12 @@ hipError_t launch_down(const moe_config* c, const moe_weights* w, const void* h,
 // resid: NULL, or [T][H] x_dtype rows added to out (the block's residual).
 hipError_t launch_combine_gather(const moe_config* c, const void* y, const float* topk_w, const float* sgate,
                                  int32_t T, float* out, hipStream_t s, const void* resid = nullptr);
+// The few-token router product with the RMSNorm prologue folded in: resid
+// rows are normalised on the fly (weight g) and also written to xn
+// (route.hip); usable when router_norm_fusable.
+bool router_norm_fusable(const moe_config* c, const moe_weights* w, int32_t T);
+hipError_t launch_router_logits_norm(const moe_config* c, const moe_weights* w, const void* resid, const void* g,
+                                     float eps, int32_t T, void* xn, float* logits, float* sgate_pre, hipStream_t s);
 // RMSNorm of T rows of x ([T][H] x_dtype) with weight g [H] into y (norm.hip).
 hipError_t launch_rmsnorm(const moe_config* c, const void* x, const void* g, float eps, int32_t T, void* y,
                           hipStream_t s);

@@ -14,6 +14,7 @@
 // One wavefront per row: a row of up to 4096 bf16 (2048 fp32) values is at
 // most 8 16-byte pieces per lane, held in registers between the sum of
 // squares and the scaling, so x is read once.
+#include "gating.hpp"
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -21,42 +22,6 @@ namespace {
 
 constexpr int kNormWaves = 4;    // rows per workgroup
 constexpr int kNormPieces = 8;   // 16-byte pieces per lane at most
-
-__device__ __forceinline__ float sumsq4(uint4 v, uint16_t) {
-  float s = 0.f;
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    s = fmaf(bf16lo(w[i]), bf16lo(w[i]), s);
-    s = fmaf(bf16hi(w[i]), bf16hi(w[i]), s);
-  }
-  return s;
-}
-__device__ __forceinline__ float sumsq4(uint4 v, float) {
-  float s = 0.f;
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) s = fmaf(__uint_as_float(w[i]), __uint_as_float(w[i]), s);
-  return s;
-}
-
-__device__ __forceinline__ uint4 scale4(uint4 v, uint4 g, float r, uint16_t) {
-  const uint32_t a[4] = {v.x, v.y, v.z, v.w}, b[4] = {g.x, g.y, g.z, g.w};
-  uint32_t o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = f32_to_bf16(bf16lo(a[i]) * r * bf16lo(b[i]));
-    const uint32_t hi = f32_to_bf16(bf16hi(a[i]) * r * bf16hi(b[i]));
-    o[i] = lo | (hi << 16);
-  }
-  return make_uint4(o[0], o[1], o[2], o[3]);
-}
-__device__ __forceinline__ uint4 scale4(uint4 v, uint4 g, float r, float) {
-  return make_uint4(__float_as_uint(__uint_as_float(v.x) * r * __uint_as_float(g.x)),
-                    __float_as_uint(__uint_as_float(v.y) * r * __uint_as_float(g.y)),
-                    __float_as_uint(__uint_as_float(v.z) * r * __uint_as_float(g.z)),
-                    __float_as_uint(__uint_as_float(v.w) * r * __uint_as_float(g.w)));
-}
 
 template <typename XT>
 __global__ __launch_bounds__(kNormWaves * kWave) void k_rmsnorm(const XT* __restrict__ x, const XT* __restrict__ g,

@@ -25,6 +25,23 @@ __global__ __launch_bounds__(kRouterWaves * kWave) void k_router_gemv(
   router_row<XT, 4>(x, wr, br, wsg, T, H, E, r, logits, sgate_pre);
 }
 
+// The same rows with the pre-norm block's prologue for few tokens: x is the
+// residual stream, normalised on the fly by every wave (router_row_norm with
+// P pieces per lane, sized to the row on the host), and the waves also write
+// the normalised rows to xn for the expert kernels -- no separate
+// normalisation launch.
+template <typename XT, int P, int TG, bool PF>
+__global__ __launch_bounds__(kRouterWaves * kWave) void k_router_gemv_norm(
+    const XT* __restrict__ x, const XT* __restrict__ wr, const XT* __restrict__ br,
+    const XT* __restrict__ wsg, int32_t T, int32_t H, int32_t E, int32_t row0, int32_t row1,
+    float* __restrict__ logits, float* __restrict__ sgate_pre, const XT* __restrict__ g, float eps,
+    XT* __restrict__ xn) {
+  const int wave = blockIdx.x * kRouterWaves + (threadIdx.x / kWave);
+  const int r = row0 + wave;
+  if (r >= row1) return;
+  router_row_norm<XT, P, TG, PF>(x, wr, br, wsg, g, eps, T, H, E, r, logits, sgate_pre, xn, wave, row1 - row0);
+}
+
 constexpr int kGateWaves = 4;  // tokens per workgroup
 
 // sg_mode: 0 no shared expert; 1 sigmoid of the dot staged in sgate_pre;
@@ -68,6 +85,10 @@ bool mfma_shapes_ok(const moe_config* c);
 
 bool sgate_in_router(const moe_config* c, int32_t T) { return !(T > kGemvMaxT && mfma_shapes_ok(c)); }
 
+bool router_norm_fusable(const moe_config* c, const moe_weights* w, int32_t T) {
+  return w->router_w != nullptr && T <= kGemvMaxT && sgate_in_router(c, T);
+}
+
 hipError_t launch_router_logits(const moe_config* c, const moe_weights* w, const void* x, int32_t T,
                                 float* logits, float* sgate_pre, hipStream_t s, float* part) {
   const int E = c->n_expert;
@@ -86,6 +107,45 @@ hipError_t launch_router_logits(const moe_config* c, const moe_weights* w, const
     k_router_gemv<float><<<grid, kRouterWaves * kWave, 0, s>>>(
         (const float*)x, (const float*)w->router_w, (const float*)w->router_b, (const float*)w->sh_gate_inp, T,
         c->hidden, E, row0, row1, logits, sgate_pre);
+  return hipGetLastError();
+}
+
+template <typename XT, int P, int TG, bool PF>
+static void router_norm_launch(const moe_config* c, const moe_weights* w, const void* resid, const void* g,
+                               float eps, int32_t T, void* xn, float* logits, float* sgate_pre, hipStream_t s,
+                               int row0, int row1) {
+  dim3 grid((row1 - row0 + kRouterWaves - 1) / kRouterWaves);
+  k_router_gemv_norm<XT, P, TG, PF><<<grid, kRouterWaves * kWave, 0, s>>>(
+      (const XT*)resid, (const XT*)w->router_w, (const XT*)w->router_b, (const XT*)w->sh_gate_inp, T, c->hidden,
+      c->n_expert, row0, row1, logits, sgate_pre, (const XT*)g, eps, (XT*)xn);
+}
+
+template <typename XT>
+static void router_norm_dispatch(const moe_config* c, const moe_weights* w, const void* resid, const void* g,
+                                 float eps, int32_t T, void* xn, float* logits, float* sgate_pre, hipStream_t s,
+                                 int row0, int row1) {
+  const int np = c->hidden / (16 / (int)sizeof(XT));  // 16-byte pieces per row (<= 512)
+  if (np <= 64)
+    router_norm_launch<XT, 1, 8, true>(c, w, resid, g, eps, T, xn, logits, sgate_pre, s, row0, row1);
+  else if (np <= 128)
+    router_norm_launch<XT, 2, 8, true>(c, w, resid, g, eps, T, xn, logits, sgate_pre, s, row0, row1);
+  else if (np <= 256)
+    router_norm_launch<XT, 4, 8, false>(c, w, resid, g, eps, T, xn, logits, sgate_pre, s, row0, row1);
+  else if (np <= 384)
+    router_norm_launch<XT, 6, 4, false>(c, w, resid, g, eps, T, xn, logits, sgate_pre, s, row0, row1);
+  else
+    router_norm_launch<XT, 8, 2, false>(c, w, resid, g, eps, T, xn, logits, sgate_pre, s, row0, row1);
+}
+
+hipError_t launch_router_logits_norm(const moe_config* c, const moe_weights* w, const void* resid, const void* g,
+                                     float eps, int32_t T, void* xn, float* logits, float* sgate_pre, hipStream_t s) {
+  // router_norm_fusable: router_w given and few tokens, so rows [0, E (+1)) run here
+  const int row1 = c->shared_ff > 0 ? c->n_expert + 1 : c->n_expert;
+  if (T == 0) return hipSuccess;
+  if (c->x_dtype == MOE_DTYPE_BF16)
+    router_norm_dispatch<uint16_t>(c, w, resid, g, eps, T, xn, logits, sgate_pre, s, 0, row1);
+  else
+    router_norm_dispatch<float>(c, w, resid, g, eps, T, xn, logits, sgate_pre, s, 0, row1);
   return hipGetLastError();
 }
 

@@ -9,7 +9,9 @@ oracle's block on the same seeded inputs.
 * the layer part out - resid: the layer tolerance of the weights' dtype
   (max|err| <= tol * max|ref|) on tokens routed alike;
 * the residual add: bit-equal to fp32(resid + moe_forward(xn)) run on the
-  GPU's own normalised rows."""
+  GPU's own normalised rows (for up to 64 tokens the router-product kernel
+  normalises on the fly, so this also checks that its logits equal the
+  plain router's on the rows it wrote)."""
 import numpy as np
 import pytest
 import torch
@@ -31,6 +33,9 @@ BLOCKS = [
     ("gptoss20b_bf16", 2048, 20, {}),
     ("gptoss20b_mxfp4", 16, None, {}),                                    # decode shape
     ("gptoss20b_mxfp4", 150, None, dict(E=8, H=320, F=192, k=2)),
+    ("qwen35moe_decode", 64, 16, {}),                                     # largest batch normalised in the router
+    ("qwen35moe_decode", 65, 16, {}),                                     # smallest with its own norm launch
+    ("gptoss20b_bf16", 64, None, dict(E=8, H=320, F=192, k=2)),           # 8 router waves write 64 rows
 ]
 
 
