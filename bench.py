@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated per step")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-prefill", action="store_true", help="skip the T=4096 measurement")
+    ap.add_argument("--no-block", action="store_true",
+                    help="skip the pre-norm block measurement (its residual rows route to other experts, so "
+                         "counter runs of the decode gate/up kernel leave it out)")
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--gptoss", action="store_true",
@@ -312,11 +315,18 @@ def main():
     log("decode: %.4f ms/step, %.0f tokens/s, %d active experts" % (ms, tok_s, n_active))
     g_ms = graph_replay_ms(layer, a.steps, a.warmup)
     log("decode, HIP graph replay: %.4f ms/step" % g_ms)
-    b_ms, _ = time_loop(layer.block, a.steps, a.warmup)
-    b_active = active_experts(layer.idx.cpu().numpy(), dec.E)
-    bx_ms, _ = time_loop(layer.forward_on_xn, a.steps, a.warmup)
-    log("decode, pre-norm block (RMSNorm + layer + residual): %.4f ms/step; the layer alone on the same "
-        "normalised rows %.4f ms (%d active experts)" % (b_ms, bx_ms, b_active))
+    block = None
+    if not a.no_block:
+        b_ms, _ = time_loop(layer.block, a.steps, a.warmup)
+        b_active = active_experts(layer.idx.cpu().numpy(), dec.E)
+        bx_ms, _ = time_loop(layer.forward_on_xn, a.steps, a.warmup)
+        log("decode, pre-norm block (RMSNorm + layer + residual): %.4f ms/step; the layer alone on the same "
+            "normalised rows %.4f ms (%d active experts)" % (b_ms, bx_ms, b_active))
+        block = {"ms_per_step": round(b_ms, 5), "tokens_per_s": round(dec.T / (b_ms * 1e-3), 1),
+                 "layer_on_same_rows_ms": round(bx_ms, 5), "over_layer_ms": round(b_ms - bx_ms, 5),
+                 "active_experts": b_active,
+                 "note": "moe_forward_prenorm on residual rows (RMSNorm in the router-product kernel, "
+                         "residual add in the combine) against moe_forward on the rows it normalised"}
 
     # dominant kernel (expert gate/up), timed with events on the launch stream
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
@@ -354,11 +364,7 @@ def main():
                    "layer_frac_hbm": round(layer_gbs / HBM_PEAK_GBS, 4), "wall_s": round(wall, 3)},
         "graph_replay": {"ms_per_step": round(g_ms, 5), "tokens_per_s": round(dec.T / (g_ms * 1e-3), 1),
                          "note": "the same moe_forward pass captured once per weight copy in a HIP graph"},
-        "prenorm_block": {"ms_per_step": round(b_ms, 5), "tokens_per_s": round(dec.T / (b_ms * 1e-3), 1),
-                          "layer_on_same_rows_ms": round(bx_ms, 5), "over_layer_ms": round(b_ms - bx_ms, 5),
-                          "active_experts": b_active,
-                          "note": "moe_forward_prenorm on residual rows (RMSNorm in the router-product kernel, "
-                                  "residual add in the combine) against moe_forward on the rows it normalised"},
+        "prenorm_block": block,
         "roofline": roofline,
     }
     del layer
