@@ -36,7 +36,24 @@ BLOCKS = [
     ("qwen35moe_decode", 64, 16, {}),                                     # largest batch normalised in the router
     ("qwen35moe_decode", 65, 16, {}),                                     # smallest with its own norm launch
     ("gptoss20b_bf16", 64, None, dict(E=8, H=320, F=192, k=2)),           # 8 router waves write 64 rows
+    ("qwen35moe_prefill_zipf", 8, None, {}),                              # drawn logits at decode size: RMSNorm launch
+    ("tiny_fp32", 100, None, {}),                                         # fp32 rows past 64 tokens
 ]
+
+
+def test_prenorm_block_mxfp8_inputs():
+    # the MX MFMA path reads the normalised rows rounded to MXFP8
+    case = _case("gptoss20b_mxfp4", 150, dict(E=8, H=320, F=192, k=2))
+    case.act_quant = "mxfp8"
+    cfg, w, out, xn, idx, ws = _run(case)
+    tokens = np.arange(case.T, dtype=np.int32)
+    r_out, _, r_idx, _, _ = oracle.Layer(case).block_forward(tokens=tokens)
+    same = (idx.cpu().numpy() == r_idx).all(1)
+    assert same.mean() >= 0.95
+    r64 = _f64(case.t["resid"], "bf16")[same]
+    rel = assert_normwise(out.cpu().numpy()[same].astype(np.float64) - r64, r_out[same].astype(np.float64) - r64,
+                          3e-2, "mxfp8 block layer part")
+    log("  mxfp8 block: max|err|/max|ref| = %.3e" % rel)
 
 
 def _ids(p):

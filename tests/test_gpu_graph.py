@@ -74,3 +74,45 @@ def test_forward_graph_replay(name, T, over):
             ref, ref_idx, _, _ = oracle.Layer(case).forward()
             assert (idx_g.cpu().numpy() == ref_idx).all(1).mean() >= 0.95
             assert_normwise(out_g.cpu().numpy(), ref, tol_of(case), "graph replay vs oracle")
+
+
+PRENORM = [
+    ("qwen35moe_decode", 8, dict(E=32, H=256, F=128, Fs=128, k=4)),   # norm inside the router product
+    ("qwen35moe_decode", 300, dict(E=16, H=256, F=192, Fs=128, k=4)),  # RMSNorm launch + MFMA path
+]
+
+
+@pytest.mark.parametrize("name,T,over", PRENORM, ids=[_ids(p) for p in PRENORM])
+def test_prenorm_graph_replay(name, T, over):
+    """moe_forward_prenorm captured once, replayed on new residual rows, each
+    replay bit-equal to an eager pass."""
+    log("prenorm graph replay: %s T=%d %s" % (name, T, over))
+    case = synth.add_block_inputs(synth.make_case(name, T=T, **over))
+    cfg = config_of(case)
+    w = device_weights(case)
+    g_w = to_torch(case.t["norm_w"])
+    rs = [case.t["resid"]] + [synth.add_block_inputs(synth.make_case(name, T=T, only={"x"}, **over),
+                                                     seed=synth.BASE_SEED + i).t["resid"] for i in (1, 2, 3)]
+    r_static = to_torch(rs[0])
+    out_g = torch.empty((T, case.H), dtype=torch.float32, device="cuda")
+    ws_g = torch.empty(moe.moe_workspace_bytes(cfg, T), dtype=torch.uint8, device="cuda")
+    out_e, ws_e = torch.empty_like(out_g), torch.empty_like(ws_g)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        moe.moe_forward_prenorm(cfg, w, g_w, case.norm_eps, r_static, T, out_g, ws_g)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.moe_forward_prenorm(cfg, w, g_w, case.norm_eps, r_static, T, out_g, ws_g)
+    torch.cuda.synchronize()
+    for rep, r in enumerate(rs):
+        r_static.copy_(to_torch(r))
+        out_g.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        moe.moe_forward_prenorm(cfg, w, g_w, case.norm_eps, to_torch(r), T, out_e, ws_e)
+        torch.cuda.synchronize()
+        assert torch.equal(out_g.view(torch.int32), out_e.view(torch.int32)), \
+            "replay %d: output differs from the eager pass" % rep
