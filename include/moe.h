@@ -126,9 +126,9 @@ typedef struct {
   const void* sh_gate_inp;       /* ffn_gate_inp_shexp [H] */
 } moe_weights;
 
-/* Bytes of workspace that moe_forward (the largest user) needs for T tokens;
- * it also covers moe_permute, moe_expert_ffn and moe_combine.  Returns 0 for
- * an invalid config. */
+/* Bytes of workspace that moe_forward and moe_forward_prenorm (the largest
+ * users) need for T tokens; it also covers moe_permute, moe_expert_ffn and
+ * moe_combine.  Returns 0 for an invalid config. */
 size_t moe_workspace_bytes(const moe_config* cfg, int32_t T);
 
 /* Routing: router product (when w->router_w != NULL) and gating.
