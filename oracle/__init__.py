@@ -18,7 +18,9 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libmoe_ref.so")
+# MOE_REF_LIB names another build of moe_ref.c to load (the sanitizer test
+# builds one with AddressSanitizer and UBSan and runs the oracle's tests on it)
+_LIB_PATH = os.environ.get("MOE_REF_LIB") or os.path.join(_HERE, "libmoe_ref.so")
 
 REF_F32, REF_BF16, REF_MXFP4 = 0, 1, 2
 REF_SOFTMAX_TOPK, REF_TOPK_SOFTMAX = 0, 1
@@ -223,9 +225,10 @@ class Layer:
         offsets = np.ascontiguousarray(offsets, np.int32)
         sorted_assign = np.ascontiguousarray(sorted_assign, np.int32)
         nseg = c.E + (1 if c.has_shared else 0)
-        rows = int(offsets[nseg])
-        assert c.F == c.Fs or not c.has_shared, "h rows share one width"
-        h = np.empty((rows, c.F), np.float32)
+        n = c.T * c.k
+        assert int(offsets[nseg]) == n + (c.T if c.has_shared else 0)
+        # routed rows (F values each) first, then the shared rows (Fs values)
+        h = np.empty(n * c.F + (c.T * c.Fs if c.has_shared else 0), np.float32)
         lib().ref_expert_ffn(ctypes.byref(self.cfg), ctypes.byref(self.w), ctypes.byref(self.x), c.T,
                              _p(offsets), _p(sorted_assign), _p(h))
         return h

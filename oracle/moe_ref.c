@@ -383,6 +383,14 @@ static int32_t token_of(const ref_cfg* c, int32_t T, int32_t a) {
   return a < n ? a / c->k : (int32_t)(a - n);
 }
 
+/* Offset of the h row at sorted position pos: the T*k routed rows of F
+ * values come first, then the T shared rows of Fs values (the layout the
+ * GPU library's moe_expert_ffn writes). */
+static int64_t h_row_offset(const ref_cfg* c, int32_t T, int64_t pos) {
+  const int64_t n = (int64_t)T * c->k;
+  return pos < n ? pos * c->F : n * c->F + (pos - n) * c->Fs;
+}
+
 static int32_t expert_of_pos(const int32_t* offsets, int32_t nseg, int32_t pos) {
   int32_t e = 0;
   while (e + 1 < nseg && offsets[e + 1] <= pos) ++e;
@@ -405,7 +413,7 @@ void ref_expert_ffn(const ref_cfg* c, const ref_weights* w, const ref_mat* x, in
       int64_t Fe = e == c->E ? c->Fs : c->F;
       load_row(x, t, H, xr);
       ref_expert_act(c, w, e, xr, hv);
-      for (int64_t f = 0; f < Fe; ++f) h[pos * Fe + f] = (float)hv[f];
+      for (int64_t f = 0; f < Fe; ++f) h[h_row_offset(c, T, pos) + f] = (float)hv[f];
     }
     free(xr);
     free(hv);
@@ -432,13 +440,13 @@ void ref_combine(const ref_cfg* c, const ref_weights* w, const float* h, const i
       for (int32_t j = 0; j < c->k; ++j) {
         int32_t p = pos_of[t * c->k + j];
         int32_t e = expert_of_pos(offsets, nseg, p);
-        for (int64_t f = 0; f < c->F; ++f) hv[f] = (double)h[(int64_t)p * c->F + f];
+        for (int64_t f = 0; f < c->F; ++f) hv[f] = (double)h[h_row_offset(c, T, p) + f];
         ref_expert_down(c, w, e, hv, y);
         for (int64_t o = 0; o < H; ++o) acc[o] += (double)topk_w[t * c->k + j] * y[o];
       }
       if (c->Fs > 0) {
         int32_t p = pos_of[n + t];
-        for (int64_t f = 0; f < c->Fs; ++f) hv[f] = (double)h[(int64_t)p * c->Fs + f];
+        for (int64_t f = 0; f < c->Fs; ++f) hv[f] = (double)h[h_row_offset(c, T, p) + f];
         ref_expert_down(c, w, c->E, hv, y);
         for (int64_t o = 0; o < H; ++o) acc[o] += (double)sgate[t] * y[o];
       }

@@ -115,6 +115,23 @@ def test_sparse_equals_dense_brute_force(act, gating, Fs):
     assert np.all(np.abs(out2 - dense) <= 1e-5 * np.abs(dense).max())
 
 
+@pytest.mark.parametrize("F,Fs", [(32, 64), (64, 32)])
+def test_permuted_path_with_shared_width_unlike_routed(F, Fs):
+    """h holds the T*k routed rows of F values, then the T shared rows of Fs
+    values; with F != Fs the permuted path (expert_ffn -> combine) must still
+    equal the dense brute force."""
+    c = small_random_case(T=6, F=F, Fs=Fs)
+    L = oracle.Layer(c)
+    dense = L.forward_dense()
+    idx, w = L.route(L.router_logits())
+    sg = oracle.sigmoid(L.shared_gate_logit())
+    off, sa, _ = oracle.permute(c.E, c.k, c.T, True, idx)
+    h = L.expert_ffn(off, sa)
+    assert h.size == c.T * c.k * F + c.T * Fs
+    out = L.combine(h, off, sa, w, sg)
+    assert np.all(np.abs(out - dense) <= 1e-5 * np.abs(dense).max())
+
+
 def test_identical_experts_reduce_to_one_ffn():
     """All routed experts equal => sum of weights (= 1) times that FFN."""
     c = small_random_case(T=4, Fs=0)

@@ -134,6 +134,29 @@ def test_router_logits_exact_integer_case_and_bias():
     assert np.array_equal(lg, ref.astype(np.float32))
 
 
+def test_shared_gate_exact_integer_case():
+    """Small integers make the shared-gate dot exact: sh_gate_inp . x equals
+    the int64 product, in the step function and inside the whole layer (whose
+    gate is sigmoid of that dot).  The router rows and the shared expert's own
+    matrices hold other integers, so reading the wrong tensor, or the wrong
+    row of x, fails."""
+    rng = np.random.default_rng(29)
+    T, H = 5, 64
+    c = blank_case(T, H, 8, 2, 32, Fs=32)
+    c.t["x"] = rng.integers(-3, 4, (T, H)).astype(np.float32)
+    c.t["sh_gate_inp"] = rng.integers(-3, 4, H).astype(np.float32)
+    c.t["router_w"] = rng.integers(-3, 4, (8, H)).astype(np.float32)
+    c.t["sh_gate_w"] = rng.integers(-3, 4, (32, H)).astype(np.float32)
+    c.t["sh_up_w"] = rng.integers(-3, 4, (32, H)).astype(np.float32)
+    ref = c.t["x"].astype(np.int64) @ c.t["sh_gate_inp"].astype(np.int64)
+    assert len(set(ref.tolist())) > 2          # the tokens' gates differ
+    L = oracle.Layer(c)
+    assert np.array_equal(L.shared_gate_logit(), ref.astype(np.float32))
+    _, _, _, sg = L.forward()
+    want = expit(ref.astype(np.float64)).astype(np.float32)
+    assert np.all(np.abs(sg - want) <= np.spacing(want))
+
+
 def test_shared_gate_closed_forms():
     assert oracle.sigmoid(np.array([0.0], np.float32))[0] == np.float32(0.5)
     assert abs(float(oracle.sigmoid(np.array([math.log(3.0)], np.float32))[0]) - 0.75) < 1e-7
