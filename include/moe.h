@@ -30,6 +30,10 @@
  *   - Shapes: hidden, expert_ff and shared_ff must be multiples of 32;
  *     1 <= top_k <= min(n_expert, 32); n_expert <= 1024; T >= 0 (T = 0 is a
  *     no-op that returns MOE_OK).  Tensor pointers must be 16-byte aligned.
+ *     A batch whose token rows x pass 2 GiB (T * hidden * element size),
+ *     or, with act_quant, whose MXFP8 codes of h pass 2 GiB (T * top_k *
+ *     expert_ff bytes), is refused with MOE_EUNSUPPORTED (the kernels
+ *     address them through 32-bit buffer extents).
  *   - Dtypes: x, router, biases and the shared expert share `x_dtype`
  *     (F32 or BF16); routed expert matrices use `w_dtype`: F32 with F32 x,
  *     BF16 or MXFP4 with BF16 x.  Logits, routing weights, the shared gate
@@ -132,6 +136,12 @@ typedef struct {
 size_t moe_workspace_bytes(const moe_config* cfg, int32_t T);
 
 /* Routing: router product (when w->router_w != NULL) and gating.
+ * Defined by "qwen35moe - Forward-Pass Design (Pantheon port)", section
+ * "Shared-expert MoE FFN (every layer)" (softmax over the router logits,
+ * top-k, norm_topk_prob, expert_weights_scale, sigmoid shared gate),
+ * "qwen35moe CPU-reference golden vectors", section "Kernel 4 - MoE
+ * routing" (selection order, first-seen ties) and "Phase 19: MoE -
+ * gpt-oss-20b", section 2 "Router" (biased logits, top-k, softmax of the k).
  *   x        [T][H] x_dtype; may be NULL only when router_w == NULL and there
  *            is no shared expert
  *   logits   [T][E] fp32: written when router_w != NULL (bias included),
@@ -144,7 +154,9 @@ size_t moe_workspace_bytes(const moe_config* cfg, int32_t T);
  *            bytes: with it, a large batch's router product is split over
  *            ranges of the hidden dimension (more workgroups) whose partial
  *            sums the gating adds up in a fixed order
- * Same logits in => bit-identical topk_idx, on every call. */
+ * Same logits in => bit-identical topk_idx, on every call.  Logits that
+ * are NaN or infinite are outside the contract; the picks are still k
+ * distinct experts in [0, E) for every token. */
 int moe_route(const moe_config* cfg, const moe_weights* w, const void* x, float* logits,
               int32_t* topk_idx, float* topk_w, float* sgate, int32_t T, void* ws, size_t ws_bytes,
               hipStream_t stream);
@@ -152,18 +164,31 @@ int moe_route(const moe_config* cfg, const moe_weights* w, const void* x, float*
 /* Token -> expert permutation: a stable counting sort of the T*k
  * assignments a = t*k + j by expert id (ascending a inside each segment).
  * With a shared expert a last segment E holds a = T*k + t for every token.
+ * The pages only imply this step: expert-grouped launches in "qwen35moe -
+ * Forward-Pass Design (Pantheon port)", sections "K80 GPU decode - status
+ * & performance" and "Batched prefill" (tokens that share an expert stream
+ * its weights once).
  *   offsets       [E + 1 (+1 if shared)] int32, exclusive prefix of the counts
  *   sorted_assign [T*k (+T)] int32, assignment id at each sorted position
  *   assign_pos    [T*k (+T)] int32, its inverse
- * topk_idx entries must lie in [0, E); the result is bit-exact and
- * deterministic. */
+ * Contract: each token's k picks are distinct experts in [0, E) (what
+ * moe_route writes); the result is then bit-exact and deterministic.  Picks
+ * that break it (an id out of range, or one repeating an earlier pick of
+ * the same token) are replaced, in slot order, by the lowest experts the
+ * token's valid picks leave free, so the permutation is always a bijection
+ * and no later step indexes past a buffer; the layer's output for such a
+ * token is then that of the replaced picks. */
 int moe_permute(const moe_config* cfg, const int32_t* topk_idx, int32_t T, int32_t* offsets,
                 int32_t* sorted_assign, int32_t* assign_pos, void* ws, size_t ws_bytes,
                 hipStream_t stream);
 
 /* Expert gate/up products with the activation applied, one row per sorted
  * position: h rows [0, T*k) have F columns, the shared rows [T*k, T*k+T)
- * follow with Fs columns.  h is bf16 when x_dtype is BF16, fp32 otherwise.
+ * follow with Fs columns.  Defined by "qwen35moe - Forward-Pass Design
+ * (Pantheon port)", section "Shared-expert MoE FFN" (SwiGLU experts and
+ * the shared SwiGLU expert) and "Phase 19: MoE - gpt-oss-20b", section 2
+ * "Experts" (interleaved gate_up with bias, clamps, (up+1)*gate*
+ * sigmoid(alpha*gate)) and section 3 (MXFP4 blocks and scales).  h is bf16 when x_dtype is BF16, fp32 otherwise.
  * ws is used only with act_quant (the rounded x); then it must be 256-byte
  * aligned and at least moe_workspace_bytes(cfg, T) bytes (MOE_EWORKSPACE). */
 int moe_expert_ffn(const moe_config* cfg, const moe_weights* w, const void* x,
@@ -171,7 +196,11 @@ int moe_expert_ffn(const moe_config* cfg, const moe_weights* w, const void* x,
                    void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Down projection (+ bias), weighted combine over each token's k picks in
- * pick order, plus sgate * the shared expert's down projection.
+ * pick order, plus sgate * the shared expert's down projection.  Defined by
+ * "qwen35moe - Forward-Pass Design (Pantheon port)", section "Shared-expert
+ * MoE FFN" (weighted sum of the picked experts plus the gated shared
+ * expert) and "Phase 19: MoE - gpt-oss-20b", section 2 "Experts" (the down
+ * bias inside each expert's weighted term).
  *   h as written by moe_expert_ffn (with act_quant, rounded to MXFP8 here,
  *   into ws); topk_w [T][k]; sgate [T] (shared only);
  *   out [T][H] fp32 (fully overwritten). */
@@ -180,7 +209,10 @@ int moe_combine(const moe_config* cfg, const moe_weights* w, const void* h,
                 const float* sgate, int32_t T, float* out, void* ws, size_t ws_bytes,
                 hipStream_t stream);
 
-/* The whole layer: route, permute, expert FFN, combine.
+/* The whole layer: route, permute, expert FFN, combine, as the layer
+ * statement at the top of this header gives it ("qwen35moe - Forward-Pass
+ * Design (Pantheon port)", section "Shared-expert MoE FFN (every layer)";
+ * "Phase 19: MoE - gpt-oss-20b", section 2 "Router" and "Experts").
  *   logits: NULL or [T][E] fp32 -- an output when router_w != NULL, the
  *   required input when router_w == NULL.  topk_idx, topk_w, sgate: NULL or
  *   outputs as in moe_route.  Intermediates live in ws. */

@@ -260,18 +260,19 @@ class Layer:
                           _p(out), _p(ti), _p(tw), _p(sg))
         return out, ti, tw, sg
 
-    def block_forward(self, tokens=None, logits=None):
+    def block_forward(self, tokens=None, logits=None, idx=None):
         """The layer inside its decoder block: out = r + layer(RMSNorm(r) * g)
         with r = the case's "resid" rows, g its "norm_w", eps its norm_eps.
         Returns (out, xn, topk_idx, topk_w, sgate); the residual sum is taken
-        in double from the layer's fp32 output and rounded to fp32."""
+        in double from the layer's fp32 output and rounded to fp32.  With
+        `idx`, the layer takes those picks instead of routing."""
         c = self.case
         xn = rmsnorm(c.t["resid"], c.t["norm_w"], c.norm_eps, c.x_dtype)
         keep = self.x
         self._xn = xn
         self.x = _mat(xn, c.x_dtype)
         try:
-            out, ti, tw, sg = self.forward(logits=logits, tokens=tokens)
+            out, ti, tw, sg = self.forward(logits=logits, idx=idx, tokens=tokens)
         finally:
             self.x = keep
         r = c.t["resid"]

@@ -50,7 +50,7 @@ int make_plan(const moe_config* c, int32_t T, Plan* p) {
   p->n_rows = p->n_assign + (p->shared ? T : 0);
   p->nseg = c->n_expert + p->shared;
   p->elem_x = c->x_dtype == MOE_DTYPE_BF16 ? 2 : 4;
-  p->perm_bytes = up256(permute_scratch_bytes(T, c->n_expert));
+  p->perm_bytes = up256(permute_scratch_bytes(T, c->n_expert, c->top_k));
   p->y_bytes = up256((size_t)p->n_rows * c->hidden * 4);
   size_t o = 0;
   p->off_logits = o; o += up256((size_t)T * c->n_expert * 4);
@@ -82,11 +82,16 @@ int make_plan(const moe_config* c, int32_t T, Plan* p) {
   // moe_forward_prenorm: the normalised rows when the caller does not take them
   p->off_xn = o; o += up256((size_t)T * c->hidden * p->elem_x);
   p->total = o;
-  // the few-token kernels address activations and h with 32-bit buffer offsets
+  // Buffer descriptors hold 32-bit extents: every kernel addresses the
+  // token rows x through one (router product, gate/up); the few-token
+  // kernels address all of h through one; the MX MFMA path addresses the
+  // MXFP8 codes of h ([T*k][F] bytes) through one.  Larger batches are
+  // rejected here rather than wrapped on the device.
+  const size_t lim = (size_t)1 << 31;
   const size_t act_bytes = (size_t)(p->n_assign * c->expert_ff + (p->shared ? (int64_t)T * c->shared_ff : 0)) * p->elem_x;
-  if (!(T > kGemvMaxT && mfma_shapes_ok(c)) &&
-      ((size_t)T * c->hidden * p->elem_x >= ((size_t)1 << 31) || act_bytes >= ((size_t)1 << 31)))
-    return MOE_EUNSUPPORTED;
+  if ((size_t)T * c->hidden * p->elem_x >= lim) return MOE_EUNSUPPORTED;
+  if (!(T > kGemvMaxT && mfma_shapes_ok(c)) && act_bytes >= lim) return MOE_EUNSUPPORTED;
+  if (p->mx8 && (size_t)p->n_assign * c->expert_ff >= lim) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 

@@ -1058,11 +1058,7 @@ hipError_t launch_gateup_mfma(const moe_config* c, const moe_weights* w, const v
   a.m_tiles_max = row_tiles_bound(c, T);
   a.ksplit = 1;
   a.split_steps = c->hidden / BK;
-#ifdef MOE_GATEUP_GRID_ALL
-  return launch<MODE_GATEUP>(a, c->w_dtype == MOE_DTYPE_MXFP4, 0, s);
-#else
   return launch<MODE_GATEUP>(a, c->w_dtype == MOE_DTYPE_MXFP4, c->hidden, s);
-#endif
 }
 
 hipError_t launch_down_mfma(const moe_config* c, const moe_weights* w, const void* h, const int32_t* offsets,

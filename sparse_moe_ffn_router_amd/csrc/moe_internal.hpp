@@ -39,11 +39,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 }
 
 // Order-preserving map of an fp32 value to uint32 with -0 folded into +0:
-// a > b (as floats, NaN excluded) <=> key(a) > key(b); -0 and +0 tie.
+// a > b (as floats, NaN excluded) <=> key(a) > key(b); -0 and +0 tie.  The
+// key is never 0 (the top-k's mark for a picked or absent expert): the one
+// pattern that would map there, the NaN 0xFFFFFFFF, gets key 1, below -Inf
+// like every NaN with the sign bit set.
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t b = __float_as_uint(f);
   if (b == 0x80000000u) b = 0u;
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  const uint32_t k = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return k ? k : 1u;
 }
 
 // DPP lane exchanges (gfx9 encodings): quad permutes, mirrors within a
@@ -167,7 +171,7 @@ hipError_t launch_gating(const moe_config* c, const moe_weights* w, const void* 
 bool sgate_in_router(const moe_config* c, int32_t T);
 hipError_t launch_permute(const moe_config* c, const int32_t* topk_idx, int32_t T, int32_t* offsets,
                           int32_t* sorted_assign, int32_t* assign_pos, int32_t* scratch, hipStream_t s);
-size_t permute_scratch_bytes(int32_t T, int32_t E);
+size_t permute_scratch_bytes(int32_t T, int32_t E, int32_t k);
 // Gating + permutation in one launch for small batches.
 bool can_fuse_gate_permute(int32_t T);
 hipError_t launch_gate_permute(const moe_config* c, const float* logits, const float* sgate_pre, int32_t T,

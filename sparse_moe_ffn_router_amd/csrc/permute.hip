@@ -24,6 +24,41 @@ constexpr int kWords = kBlockTokens / 64;     // 64-bit words per expert mask
 
 __device__ __forceinline__ uint64_t lower_bits(int t) { return t ? (~0ull >> (64 - t)) : 0ull; }
 
+// The k picks of one token, made distinct and in range, in place (one
+// thread per token).  The contract asks each token for k distinct experts
+// in [0, E), which the gating always gives; a caller's picks that break it
+// (an id out of range, or one repeating an earlier pick of the token) are
+// replaced, in slot order, by the lowest experts the token's valid picks
+// leave free (k <= E, so there are enough).  The permutation is then always
+// a bijection with full segments, so no later kernel reads or writes past a
+// buffer, whatever the picks held.
+__device__ void make_picks_distinct(int32_t* p, int k, int E) {
+  int v[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) v[j] = j < k ? p[j] : 0;
+  uint32_t bad = 0;  // slots to replace
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j < k) {
+      bool b = (unsigned)v[j] >= (unsigned)E;
+#pragma unroll
+      for (int i = 0; i < j; ++i) b = b || (((bad >> i) & 1u) == 0 && v[i] == v[j]);
+      bad |= (uint32_t)b << j;
+    }
+  }
+  if (!bad) return;  // the contract holds (always, after the gating)
+  int cand = 0;
+  for (int j = 0; j < k; ++j) {
+    if (!((bad >> j) & 1u)) continue;
+    for (;; ++cand) {
+      bool used = false;
+      for (int i = 0; i < k && !used; ++i) used = ((bad >> i) & 1u) == 0 && p[i] == cand;
+      if (!used) break;
+    }
+    p[j] = cand++;
+  }
+}
+
 // Exclusive scan of v over the first n threads of a 1024-thread block
 // (n <= 1024); returns the exclusive prefix, *total gets the sum.
 __device__ int block_excl_scan(int v, int* wsum, int* total) {
@@ -102,6 +137,8 @@ __global__ __launch_bounds__(kThreadsBig) void k_permute_small(const int32_t* __
   __shared__ int wsum[kThreadsBig / kWave];
   for (int a = threadIdx.x; a < T * k; a += kThreadsBig) idx_s[a] = topk_idx[a];
   __syncthreads();
+  if (threadIdx.x < T) make_picks_distinct(idx_s + threadIdx.x * k, k, E);
+  __syncthreads();
   permute_one_block(idx_s, T, k, E, shared, mask, base, wsum, offsets, sorted_assign, assign_pos);
 }
 
@@ -128,19 +165,26 @@ __global__ __launch_bounds__(kThreadsBig) void k_gate_permute_small(
 }
 
 // Large batches, pass 1: masks and counts of one block of kBlockTokens
-// tokens, stored to scratch (masks [G][E][kWords], counts [G][E]).
+// tokens, stored to scratch (masks [G][E][kWords], counts [G][E]); the
+// block's picks, made distinct per token, go to picks [T][k] for pass 3.
 __global__ __launch_bounds__(kThreadsBig) void k_perm_masks(const int32_t* __restrict__ topk_idx, int32_t T,
                                                             int32_t k, int32_t E, uint64_t* __restrict__ gmask,
-                                                            int32_t* __restrict__ counts) {
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ picks) {
   __shared__ uint64_t mask[kMaxExperts * kWords];
+  __shared__ int32_t idx_s[kBlockTokens * kMaxTopK];
   const int g = blockIdx.x, tid = threadIdx.x;
   for (int i = tid; i < E * kWords; i += kThreadsBig) mask[i] = 0ull;
-  __syncthreads();
   const int t0 = g * kBlockTokens;
   const int nt = min(kBlockTokens, T - t0);
+  for (int i = tid; i < nt * k; i += kThreadsBig) idx_s[i] = topk_idx[(size_t)t0 * k + i];
+  __syncthreads();
+  if (tid < nt) make_picks_distinct(idx_s + tid * k, k, E);
+  __syncthreads();
   for (int i = tid; i < nt * k; i += kThreadsBig) {
     const int tl = i / k;
-    const int e = topk_idx[(size_t)t0 * k + i];
+    const int e = idx_s[i];
+    picks[(size_t)t0 * k + i] = e;
     atomicOr((unsigned long long*)&mask[e * kWords + tl / 64], 1ull << (tl & 63));
   }
   __syncthreads();
@@ -220,9 +264,9 @@ __global__ __launch_bounds__(256) void k_perm_place(const int32_t* __restrict__ 
 
 }  // namespace
 
-size_t permute_scratch_bytes(int32_t T, int32_t E) {
+size_t permute_scratch_bytes(int32_t T, int32_t E, int32_t k) {
   const size_t G = (size_t)(T + kBlockTokens - 1) / kBlockTokens;
-  return G * E * kWords * sizeof(uint64_t) + G * E * sizeof(int32_t);
+  return G * E * kWords * sizeof(uint64_t) + G * E * sizeof(int32_t) + (size_t)T * k * sizeof(int32_t);
 }
 
 hipError_t launch_permute(const moe_config* c, const int32_t* topk_idx, int32_t T, int32_t* offsets,
@@ -236,9 +280,10 @@ hipError_t launch_permute(const moe_config* c, const int32_t* topk_idx, int32_t 
   const int G = (T + kBlockTokens - 1) / kBlockTokens;
   uint64_t* gmask = reinterpret_cast<uint64_t*>(scratch);
   int32_t* counts = reinterpret_cast<int32_t*>(gmask + (size_t)G * E * kWords);
-  k_perm_masks<<<G, kThreadsBig, 0, s>>>(topk_idx, T, k, E, gmask, counts);
+  int32_t* picks = counts + (size_t)G * E;
+  k_perm_masks<<<G, kThreadsBig, 0, s>>>(topk_idx, T, k, E, gmask, counts, picks);
   k_perm_scan<<<1, kThreadsBig, 0, s>>>(counts, G, T, k, E, shared, offsets, sorted_assign, assign_pos);
-  k_perm_place<<<(T * k + 255) / 256, 256, 0, s>>>(topk_idx, T, k, E, gmask, counts, sorted_assign, assign_pos);
+  k_perm_place<<<(T * k + 255) / 256, 256, 0, s>>>(picks, T, k, E, gmask, counts, sorted_assign, assign_pos);
   return hipGetLastError();
 }
 

@@ -60,3 +60,53 @@ def assert_rel(got, ref, rtol, atol=0.0, what=""):
     bad = np.abs(got - ref) > rtol * np.abs(ref) + atol
     assert not bad.any(), "%s: %d elements beyond %.1e relative, worst %s vs %s" % (
         what, int(bad.sum()), rtol, got[bad][:4], ref[bad][:4])
+
+
+def logit_bound(case, tokens, x=None):
+    """fp32 dot-product error bound of the GPU's router logits for the given
+    tokens, per (token, expert): H * 2^-24 * sum |x||w| (Higham), plus one
+    fp32 step.  Zero when the logits are given (drawn) rather than computed."""
+    if case.drawn_logits:
+        return np.zeros((len(tokens), case.E))
+    xs = case.t["x"] if x is None else x
+    f64 = lambda a, dt: synth.bf16_to_f32(a).astype(np.float64) if dt == "bf16" else np.asarray(a, np.float64)
+    xa = np.abs(f64(xs[tokens], case.x_dtype))
+    wa = np.abs(f64(case.t["router_w"], case.router_dtype))
+    return case.H * 2.0 ** -24 * (xa @ wa.T) + 2.0 ** -23
+
+
+def check_layer_output(case, tokens, g_idx, g_out, r_out, r_idx, ref_logits, redo, tol, what="layer output",
+                       exact_routing=False, x=None):
+    """Routing and output of a whole-layer pass against the oracle.
+
+    g_idx, g_out: the GPU's picks [T][k] and output rows (all tokens);
+    r_out, r_idx: the oracle's, on its own routing (rows `tokens` valid);
+    ref_logits: the oracle's logits of the sampled tokens;
+    redo(idx, tokens): the oracle's output rows when it takes the given picks.
+
+    With exact_routing (the same logits on both sides) every sampled token
+    must route identically.  Otherwise a token may route differently only if
+    the oracle's logits leave a gap inside the rounding bound of the GPU's;
+    such a token's output is then compared with the oracle's output on the
+    GPU's own picks, at the same tolerance.  Returns max|err|/max|ref|."""
+    g_i, r_i = g_idx[tokens], r_idx[tokens]
+    same = (g_i == r_i).all(1)
+    ref = np.array(r_out[tokens], np.float64)
+    if exact_routing:
+        assert same.all(), "%d of %d tokens routed differently on identical logits" % ((~same).sum(), len(tokens))
+    elif not same.all():
+        bnd = logit_bound(case, tokens, x)
+        for i in np.nonzero(~same)[0]:
+            kth = np.sort(ref_logits[i])[::-1][case.k - 1]
+            sel = set(g_i[i].tolist())
+            assert len(sel) == case.k and all(0 <= e < case.E for e in sel), "token %d: invalid picks" % i
+            for e in range(case.E):
+                if e in sel:
+                    assert ref_logits[i, e] >= kth - 2 * bnd[i].max(), "token %d: GPU picked a clearly losing expert" % i
+                else:
+                    assert ref_logits[i, e] <= kth + 2 * bnd[i].max(), "token %d: GPU dropped a clear winner" % i
+        diff = np.asarray(tokens)[~same]
+        ref[~same] = np.asarray(redo(g_idx, diff), np.float64)[diff]
+        log("  %d of %d sampled tokens routed differently inside the rounding bound; compared on the GPU's picks"
+            % ((~same).sum(), len(tokens)))
+    return assert_normwise(g_out[tokens], ref, tol, what)

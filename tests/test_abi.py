@@ -147,3 +147,24 @@ def test_status_strings():
     for s in (moe.MOE_OK, moe.MOE_EINVAL, moe.MOE_EUNSUPPORTED, moe.MOE_EWORKSPACE, moe.MOE_EHIP):
         assert moe.status_string(s) and moe.status_string(s) != "unknown status"
     assert moe.status_string(12345) == "unknown status"
+
+
+def test_batches_past_32_bit_buffer_extents_are_rejected():
+    """The kernels address the token rows (and, on the MX MFMA path, the
+    MXFP8 codes of h) through buffer descriptors with 32-bit extents; a batch
+    whose rows would pass 2 GiB is refused on the host (no workspace size,
+    MOE_EUNSUPPORTED from the entry points) instead of wrapping."""
+    import sparse_moe_ffn_router_amd as moe
+    T_max = (2 ** 31 - 1) // (2048 * 2)            # bf16 x rows of H = 2048 just below 2 GiB
+    assert moe.moe_workspace_bytes(_cfg(), T_max) > 0
+    assert moe.moe_workspace_bytes(_cfg(), T_max + 1) == 0
+    fake = 1 << 20
+    wb = moe._Weights(*([fake] * len(moe._WEIGHT_FIELDS)))
+    cb = _cfg()._c()
+    assert _raw("moe_forward", ctypes.byref(cb), ctypes.byref(wb), fake, T_max + 1, fake, None, None, None, None,
+                fake, 1 << 40, None) == moe.MOE_EUNSUPPORTED
+    mx = dict(hidden=2880, n_expert=32, top_k=4, expert_ff=2880, shared_ff=0, gating=moe.GATING_TOPK_SOFTMAX,
+              act=moe.ACT_SWIGLU_OAI, w_dtype=moe.DTYPE_MXFP4, act_quant=moe.ACT_QUANT_MXFP8)
+    T_h = (2 ** 31 - 1) // (4 * 2880)             # E4M3 codes of h: T*k*F bytes
+    assert moe.moe_workspace_bytes(_cfg(**mx), T_h) > 0
+    assert moe.moe_workspace_bytes(_cfg(**mx), T_h + 1) == 0

@@ -7,7 +7,9 @@ oracle's block on the same seeded inputs.
   fp32 in its own order, so a value next to a rounding boundary may round
   the other way); fp32 outputs within 2e-6 relative;
 * the layer part out - resid: the layer tolerance of the weights' dtype
-  (max|err| <= tol * max|ref|) on tokens routed alike;
+  (max|err| <= tol * max|ref|) on every sampled token; one routed
+  differently (only inside the rounding bound of its logits) is compared
+  with the oracle's block on the GPU's picks;
 * the residual add: bit-equal to fp32(resid + moe_forward(xn)) run on the
   GPU's own normalised rows (for up to 64 tokens the router-product kernel
   normalises on the fly, so this also checks that its logits equal the
@@ -20,7 +22,7 @@ import oracle
 import sparse_moe_ffn_router_amd as moe
 import synth
 from tests._gpu import config_of, device_weights, to_torch
-from tests._parity import assert_normwise, cached_case, log, tol_of
+from tests._parity import assert_normwise, cached_case, check_layer_output, log, tol_of
 
 pytestmark = pytest.mark.gpu
 
@@ -47,13 +49,36 @@ def test_prenorm_block_mxfp8_inputs():
     case.act_quant = "mxfp8"
     cfg, w, out, xn, idx, ws = _run(case)
     tokens = np.arange(case.T, dtype=np.int32)
-    r_out, _, r_idx, _, _ = oracle.Layer(case).block_forward(tokens=tokens)
-    same = (idx.cpu().numpy() == r_idx).all(1)
-    assert same.mean() >= 0.95
-    r64 = _f64(case.t["resid"], "bf16")[same]
-    rel = assert_normwise(out.cpu().numpy()[same].astype(np.float64) - r64, r_out[same].astype(np.float64) - r64,
-                          3e-2, "mxfp8 block layer part")
+    rel = _check_block(case, tokens, idx, out, 3e-2, "mxfp8 block layer part")
     log("  mxfp8 block: max|err|/max|ref| = %.3e" % rel)
+
+
+def _check_block(case, tokens, idx, out, tol, what):
+    """The layer part (out - resid) of the sampled tokens against the
+    oracle's block.  The router reads the normalised rows, whose bf16
+    elements may sit one step from the oracle's, so a token may route
+    differently only inside the rounding bound of its logits; it is then
+    compared with the oracle's block on the GPU's picks.  Drawn logits are
+    the same on both sides, so there every token must route alike."""
+    L = oracle.Layer(case)
+    lg = case.t.get("logits") if case.drawn_logits else None
+    r_out, r_xn, r_idx, _, _ = L.block_forward(tokens=tokens, logits=lg)
+    r64 = _f64(case.t["resid"], case.x_dtype)
+    ref_lg = case.t["logits"][tokens] if case.drawn_logits else \
+        oracle.Layer(_with_x(case, r_xn)).router_logits()[tokens]
+    redo = lambda gi, tk: L.block_forward(tokens=tk, logits=lg, idx=gi)[0] - r64
+    return check_layer_output(case, tokens, idx.cpu().numpy(), out.cpu().numpy().astype(np.float64) - r64,
+                              r_out.astype(np.float64) - r64, r_idx, ref_lg, redo, tol, what,
+                              exact_routing=case.drawn_logits, x=r_xn)
+
+
+def _with_x(case, x):
+    c = synth.Case(case.name, case.T, case.H, case.E, case.k, case.F, case.Fs, case.gating, case.norm_topk_prob,
+                   case.weights_scale, case.act, case.alpha, case.limit, case.x_dtype, case.w_dtype,
+                   case.router_dtype)
+    c.t = dict(case.t)
+    c.t["x"] = x
+    return c
 
 
 def _ids(p):
@@ -136,16 +161,8 @@ def test_prenorm_block_matches_oracle(p):
 
     # 3. the layer part against the oracle's block
     tokens = _sample(T, nsample)
-    r_out, r_xn, r_idx, _, _ = oracle.Layer(case).block_forward(tokens=tokens,
-                                                                logits=case.t.get("logits") if case.drawn_logits else None)
-    same = (idx.cpu().numpy()[tokens] == r_idx[tokens]).all(1)
-    assert same.mean() >= 0.95
-    r64 = _f64(case.t["resid"], dt)[tokens][same]
-    got = out.cpu().numpy()[tokens][same].astype(np.float64) - r64
-    ref = r_out[tokens][same].astype(np.float64) - r64
-    rel = assert_normwise(got, ref, tol_of(case), "block layer part")
-    log("  layer part: max|err|/max|ref| = %.3e (tol %.0e), routing equal on %d/%d tokens"
-        % (rel, tol_of(case), int(same.sum()), len(tokens)))
+    rel = _check_block(case, tokens, idx, out, tol_of(case), "block layer part")
+    log("  layer part: max|err|/max|ref| = %.3e (tol %.0e)" % (rel, tol_of(case)))
 
 
 def test_prenorm_without_xn_output_is_identical():

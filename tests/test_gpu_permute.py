@@ -75,3 +75,44 @@ def test_permute_T0_and_repeatable():
     b = _gpu_permute(256, 8, 4096, True, idx)
     for u, v in zip(a, b):
         assert np.array_equal(u, v)
+
+
+def _distinct_rule(idx, E):
+    """The contract asks for k distinct picks in [0, E) per token; picks that
+    break it (out of range, or repeating an earlier valid pick of the token)
+    are replaced, in slot order, by the lowest experts the token's valid
+    picks leave free.  Restated here from the header's description."""
+    out = np.array(idx, np.int64)
+    for t in range(out.shape[0]):
+        valid, bad = [], []
+        for j, e in enumerate(out[t]):
+            if 0 <= e < E and e not in valid:
+                valid.append(int(e))
+            else:
+                bad.append(j)
+        free = (e for e in range(E) if e not in valid)
+        for j in bad:
+            out[t, j] = next(free)
+    return out.astype(np.int32)
+
+
+@pytest.mark.parametrize("E,k,T,shared", [(16, 4, 40, True), (64, 8, 300, False), (8, 8, 600, True)])
+def test_permute_out_of_contract_picks_stay_a_bijection(E, k, T, shared):
+    """Repeated, negative and too-large expert ids: every row is still placed
+    exactly once (the expert kernels then never index past their buffers),
+    by the documented replacement rule, in both kernel paths."""
+    log("permute out-of-contract picks E=%d k=%d T=%d" % (E, k, T))
+    rng = np.random.default_rng(E + k + T)
+    idx = _uniform(E, k, T, T)
+    idx[::3, 1] = idx[::3, 0]                          # a repeat of slot 0
+    idx[1::5, k - 1] = E + rng.integers(0, 1000, idx[1::5].shape[0])
+    idx[2::7, 0] = -1 - rng.integers(0, 5, idx[2::7].shape[0])
+    idx[4] = idx[4, 0]                                 # one expert in every slot
+    off, sa, ap = _gpu_permute(E, k, T, shared, idx)
+    n = T * k + (T if shared else 0)
+    assert np.array_equal(np.sort(sa), np.arange(n))   # a bijection
+    assert np.array_equal(ap[sa], np.arange(n))
+    fixed = _distinct_rule(idx, E)
+    assert all(len(set(r)) == k for r in fixed.tolist())
+    r_off, r_sa, r_ap = oracle.permute(E, k, T, shared, fixed)
+    assert np.array_equal(off, r_off) and np.array_equal(sa, r_sa) and np.array_equal(ap, r_ap)

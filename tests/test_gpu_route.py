@@ -181,3 +181,35 @@ def test_route_deterministic_and_T0():
         assert np.array_equal(u, v)
     cfg = config_of(case)
     moe.moe_route(cfg, device_weights(case), None, None, None, None, None, 0)  # T = 0: no-op
+
+
+@pytest.mark.parametrize("E,k,T", [(256, 8, 8), (256, 8, 100), (32, 4, 64), (1024, 32, 20)])
+def test_route_non_finite_logits_give_distinct_in_range_picks(E, k, T):
+    """NaN and infinite logits are outside the contract, but the picks must
+    still be k distinct experts in [0, E) for every token (the permutation
+    and the expert kernels index by them).  Rows holding infinities but no
+    NaN are ordered, so there the picks equal the oracle's."""
+    log("route non-finite logits E=%d k=%d T=%d" % (E, k, T))
+    rng = np.random.default_rng(E * 3 + T)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    nan_neg = np.array([0xFFFFFFFF], np.uint32).view(np.float32)[0]   # every bit set
+    nan_pos = np.array([0x7FC00000], np.uint32).view(np.float32)[0]
+    lg[0, :] = nan_neg                                  # a whole row of the all-ones NaN
+    lg[1, : E // 2] = nan_neg
+    lg[2, ::3] = nan_pos
+    lg[3, :] = np.inf
+    lg[4, 5] = np.inf
+    lg[4, 9] = -np.inf
+    lg[5, :] = -np.inf
+    lg[6, rng.integers(0, E, 4)] = np.inf
+    lg[7, ::2] = -np.inf
+    for gating in ("softmax_topk", "topk_softmax"):
+        c = synth.Case("nonfinite", T, 64, E, k, 64, 0, gating, True, 1.0, "swiglu", 1.702, 7.0,
+                       "bf16", "bf16", "bf16")
+        c.t["x"] = np.zeros((T, 64), np.uint16)
+        _, idx, _, _ = _route(c, lg, with_router=False, ws=True)
+        assert ((idx >= 0) & (idx < E)).all()
+        assert all(len(set(r)) == k for r in idx.tolist()), "repeated pick"
+        finite_order = ~np.isnan(lg).any(1)
+        ref_idx, _ = route_ref(c, lg)
+        assert np.array_equal(idx[finite_order], ref_idx[finite_order])
