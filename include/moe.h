@@ -220,6 +220,22 @@ int moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, int3
                 float* logits, int32_t* topk_idx, float* topk_w, float* sgate, void* ws,
                 size_t ws_bytes, hipStream_t stream);
 
+/* moe_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same layer and arguments, but the intermediates live in a scratch
+ * array of MOE_NOALLOC_SCRATCH_BYTES built into the library instead of a
+ * caller's workspace.  Each GPU the library runs on holds its own copy of
+ * that array until the process ends.  The call allocates nothing (no
+ * hipMalloc, no library allocation); its first call on a device looks up
+ * that device's copy.  A batch whose moe_workspace_bytes(cfg, T) exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES is refused with MOE_EWORKSPACE (for the
+ * qwen35moe-shaped decode layer, T <= 256 fits).  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (two
+ * streams, or two host threads) race and must be ordered by the caller. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int moe_forward_noalloc(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T, float* out,
+                        float* logits, int32_t* topk_idx, float* topk_w, float* sgate, hipStream_t stream);
+
 /* The layer inside its pre-norm decoder block, with the norm in front and
  * the residual add behind it ("qwen35moe - Forward-Pass Design (Pantheon
  * port)", section "Block scaffold": every norm is an RMS norm and the

@@ -23,7 +23,9 @@ ACT_SWIGLU, ACT_SWIGLU_OAI = 0, 1
 ACT_QUANT_NONE, ACT_QUANT_MXFP8 = 0, 1
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
-           "moe_forward", "moe_forward_prenorm", "moe_quantize_mxfp8", "moe_status_string")
+           "moe_forward", "moe_forward_noalloc", "moe_forward_prenorm", "moe_quantize_mxfp8",
+           "moe_status_string")
+NOALLOC_SCRATCH_BYTES = 32 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 
 
 class MoeError(RuntimeError):
@@ -86,6 +88,7 @@ def _load():
     L.moe_expert_ffn.argtypes = [C, W, vp, vp, vp, i32, vp, vp, sz, vp]
     L.moe_combine.argtypes = [C, W, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
     L.moe_forward.argtypes = [C, W, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_forward_noalloc.argtypes = [C, W, vp, i32, vp, vp, vp, vp, vp, vp]
     L.moe_forward_prenorm.argtypes = [C, W, vp, ctypes.c_float, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_quantize_mxfp8.argtypes = [vp, ctypes.c_int64, i32, vp, vp, vp]
     return L
@@ -170,6 +173,15 @@ def moe_forward(cfg, w, x, T, out, ws, logits=None, topk_idx=None, topk_w=None, 
     nb = _nbytes(ws) if ws_bytes is None else ws_bytes
     _check(lib.moe_forward(ctypes.byref(c), ctypes.byref(ww), _ptr(x), T, _ptr(out), _ptr(logits), _ptr(topk_idx),
                            _ptr(topk_w), _ptr(sgate), _ptr(ws), nb, _stream(stream)), "moe_forward")
+
+
+def moe_forward_noalloc(cfg, w, x, T, out, logits=None, topk_idx=None, topk_w=None, sgate=None, stream=None):
+    """moe_forward with the library's built-in scratch (no workspace argument,
+    nothing allocated)."""
+    c, ww = cfg._c(), _weights(w)
+    _check(lib.moe_forward_noalloc(ctypes.byref(c), ctypes.byref(ww), _ptr(x), T, _ptr(out), _ptr(logits),
+                                   _ptr(topk_idx), _ptr(topk_w), _ptr(sgate), _stream(stream)),
+           "moe_forward_noalloc")
 
 
 def moe_forward_prenorm(cfg, w, norm_w, norm_eps, resid, T, out, ws, xn=None, logits=None, topk_idx=None,

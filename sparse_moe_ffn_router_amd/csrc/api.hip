@@ -3,6 +3,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -199,6 +201,33 @@ static int forward_steps(const moe_config* cfg, const moe_weights* w, const Plan
   return hip_status(launch_combine_gather(cfg, y, wt, sg, T, out, stream, pn ? pn->resid : nullptr));
 }
 
+// Scratch of moe_forward_noalloc: one file-scope device array, which every
+// GPU the library runs on holds (its own copy, at its own address) until
+// the process ends.  In host code the array's name is only a stand-in for
+// that address: each device's address is taken once, with the device
+// current, through hipGetSymbolAddress and kept in scratch_ptr; host code
+// passes only that pointer on.  Nothing in the forward pass needs its
+// scratch to start at zero (every workspace area is written before it is
+// read), so the contents the previous call left do not matter.
+static __device__ __attribute__((aligned(256))) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex scratch_mu;
+static void* scratch_ptr[kMaxDevices];
+
+static int scratch_of_current_device(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_EHIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_EHIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = (char*)scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -332,6 +361,22 @@ int moe_forward_prenorm(const moe_config* cfg, const moe_weights* w, const void*
   char* b = (char*)ws;
   const PreNorm pn = {norm_w, norm_eps, resid};
   return forward_steps(cfg, w, p, xn ? xn : b + p.off_xn, &pn, T, out, logits, topk_idx, topk_w, sgate, b, stream);
+}
+
+int moe_forward_noalloc(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T, float* out,
+                        float* logits, int32_t* topk_idx, float* topk_w, float* sgate, hipStream_t stream) {
+  Plan p;
+  int st = make_plan(cfg, T, &p);
+  if (st) return st;
+  if ((st = weights_ok(cfg, w, true, true))) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !out || !aligned16(x) || !aligned16(out)) return MOE_EINVAL;
+  if (!w->router_w && !logits) return MOE_EINVAL;
+  if (logits && !aligned16(logits)) return MOE_EINVAL;
+  if (p.total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_EWORKSPACE;
+  char* b = nullptr;
+  if ((st = scratch_of_current_device(&b))) return st;
+  return forward_steps(cfg, w, p, x, nullptr, T, out, logits, topk_idx, topk_w, sgate, b, stream);
 }
 
 }  // extern "C"

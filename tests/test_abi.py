@@ -20,7 +20,8 @@ def _declared():
 
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn",
-                                  "moe_combine", "moe_forward", "moe_forward_prenorm", "moe_quantize_mxfp8",
+                                  "moe_combine", "moe_forward", "moe_forward_noalloc", "moe_forward_prenorm",
+                                  "moe_quantize_mxfp8",
                                   "moe_status_string"])
 
 
