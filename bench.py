@@ -5,16 +5,20 @@ Default workload: the qwen35moe-shaped decode layer (T=8 tokens, H=2048,
 activations, fp32 router).  A step is one whole-layer pass (moe_forward:
 router product, gating, permutation, expert gate/up + SwiGLU, down +
 weighted combine + shared expert) over one batch of synthetic tokens, with
-inputs resident in HBM.  Weights rotate over several identical copies at
-different addresses so every step streams its experts cold from HBM (the
+inputs resident in HBM.  Steps rotate over four seeded token batches (each
+routes to its own set of experts) and over four identical weight copies at
+different addresses, so every step streams its experts cold from HBM (the
 256 MB last-level cache never holds the previous step's experts), as
 consecutive layers of a model would.
 
 The same JSON line also reports the prefill-sized layer (same weights,
-T=4096 tokens, router logits drawn so expert load is Zipf(1.0)-skewed),
-the roofline of the dominant kernel and the CPU oracle's throughput.
+T=4096 tokens, router logits drawn so expert load is Zipf(1.0)-skewed), the
+gpt-oss-20b-shaped layers (bf16 T=2048; MXFP4 experts at T=16 and T=2048;
+the MXFP8-input mode of the MXFP4 layer), each against its roofline, the
+roofline of the decode layer's dominant kernel and the CPU oracle's
+throughput (one thread and all threads).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-prefill]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-prefill] [--no-gptoss]
        python bench.py --pmc-summary FETCH_DIR WRITE_DIR   (HBM traffic from two rocprofv3 --pmc runs)
 
 HBM traffic of the dominant kernel comes from two rocprofv3 counter runs of
@@ -41,6 +45,8 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/sec + %HBM-roofline (T=8 decode) and %MFMA-peak (T=4096)"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
+N_BATCHES = 4  # seeded token batches the decode steps rotate over
 GATEUP_KERNEL = "k_gateup_gemv"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 KERNEL_SOURCES = ("sparse_moe_ffn_router_amd/csrc/ffn_gemv.hip", "sparse_moe_ffn_router_amd/csrc/moe_internal.hpp")
@@ -59,9 +65,11 @@ def parse():
                     help="skip the pre-norm block measurement (its residual rows route to other experts, so "
                          "counter runs of the decode gate/up kernel leave it out)")
     ap.add_argument("--prefill-steps", type=int, default=20)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--gptoss", action="store_true",
-                    help="also time the gpt-oss-20b-shaped layers (bf16 T=2048, MXFP4 T=16 and T=2048)")
+    ap.add_argument("--cpu-run-seconds", type=float, default=1.5,
+                    help="length of each of the 5 timed oracle runs per form")
+    ap.add_argument("--no-gptoss", action="store_true",
+                    help="skip the gpt-oss-20b-shaped layers (bf16 T=2048, MXFP4 T=16 and T=2048)")
+    ap.add_argument("--batches", type=int, default=N_BATCHES, help="seeded token batches the decode steps rotate over")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after the decode measurement, copy a buffer of this many MiB 5 times (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -76,7 +84,7 @@ def log(msg):
 class Layer:
     """Device-resident layer: weight copies, one batch of tokens, outputs."""
 
-    def __init__(self, case, copies, T=None, logits=None, x=None):
+    def __init__(self, case, copies, T=None, logits=None, x=None, xs=None):
         import torch
         from tests._gpu import config_of, device_weights, to_torch
         import sparse_moe_ffn_router_amd as moe
@@ -88,7 +96,9 @@ class Layer:
         if logits is not None:
             base = {k: v for k, v in base.items() if k not in ("router_w", "router_b")}
         self.weights = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
-        self.x = to_torch(case.t["x"] if x is None else x)
+        # token batches; step s runs batch s % len(xs) on weight copy s % copies
+        self.xs = [to_torch(b) for b in xs] if xs else [to_torch(case.t["x"] if x is None else x)]
+        self.x = self.xs[0]
         self.logits = to_torch(logits) if logits is not None else \
             torch.empty((self.T, case.E), dtype=torch.float32, device="cuda")
         self.out = torch.empty((self.T, case.H), dtype=torch.float32, device="cuda")
@@ -104,8 +114,14 @@ class Layer:
                              dtype=torch.bfloat16, device="cuda")
 
     def forward(self, step):
-        self.moe.moe_forward(self.cfg, self.weights[step % len(self.weights)], self.x, self.T, self.out, self.ws,
-                             logits=self.logits, topk_idx=self.idx, topk_w=self.wt, sgate=self.sg)
+        self.moe.moe_forward(self.cfg, self.weights[step % len(self.weights)], self.xs[step % len(self.xs)], self.T,
+                             self.out, self.ws, logits=self.logits, topk_idx=self.idx, topk_w=self.wt, sgate=self.sg)
+
+    def forward_batch(self, b):
+        """Steps over batch b alone (weight copies still rotate)."""
+        return lambda step: self.moe.moe_forward(self.cfg, self.weights[step % len(self.weights)], self.xs[b],
+                                                 self.T, self.out, self.ws, logits=self.logits, topk_idx=self.idx,
+                                                 topk_w=self.wt, sgate=self.sg)
 
     def block(self, step):
         """The layer inside its pre-norm block (RMSNorm in front, residual add
@@ -130,12 +146,12 @@ class Layer:
     def ops(self, step, ev_ffn=None):
         """The same kernels through the four step entry points; optional
         events bracket the expert gate/up launch."""
-        m, w = self.moe, self.weights[step % len(self.weights)]
-        m.moe_route(self.cfg, w, self.x, self.logits, self.idx, self.wt, self.sg, self.T, self.ws)
+        m, w, x = self.moe, self.weights[step % len(self.weights)], self.xs[step % len(self.xs)]
+        m.moe_route(self.cfg, w, x, self.logits, self.idx, self.wt, self.sg, self.T, self.ws)
         m.moe_permute(self.cfg, self.idx, self.T, self.offsets, self.sorted, self.pos, self.ws)
         if ev_ffn:
             ev_ffn[0].record()
-        m.moe_expert_ffn(self.cfg, w, self.x, self.offsets, self.sorted, self.T, self.h)
+        m.moe_expert_ffn(self.cfg, w, x, self.offsets, self.sorted, self.T, self.h)
         if ev_ffn:
             ev_ffn[1].record()
         m.moe_combine(self.cfg, w, self.h, self.offsets, self.sorted, self.wt, self.sg, self.T, self.out, self.ws)
@@ -163,18 +179,20 @@ def time_loop(fn, steps, warmup):
 
 
 def graph_replay_ms(layer, steps, warmup):
-    """moe_forward captured in one HIP graph per weight copy, replayed in
-    the same rotation as the eager loop."""
+    """moe_forward captured in one HIP graph per (batch, weight copy) pair of
+    the rotation, replayed in the same rotation as the eager loop."""
+    import math
     import torch
+    n = len(layer.weights) * len(layer.xs) // math.gcd(len(layer.weights), len(layer.xs))
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        for c in range(len(layer.weights)):
+        for c in range(n):
             layer.forward(c)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     graphs = []
-    for c in range(len(layer.weights)):
+    for c in range(n):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             layer.forward(c)
@@ -206,6 +224,19 @@ def layer_bytes(case, n_active, T):
     shared expert, tokens in, fp32 out."""
     per_expert = 3 * case.F * case.H * 2
     b = n_active * per_expert + case.E * case.H * 2 + T * case.H * 2 + T * case.H * 4
+    if case.has_shared:
+        b += 3 * case.Fs * case.H * 2 + case.H * 2
+    return b
+
+
+def gptoss_layer_bytes(case, n_active, T):
+    """Algorithmic bytes of a gpt-oss-shaped layer: every active expert's
+    gate_up and down weights once (bf16: 2 bytes per weight; MXFP4: half a
+    byte of code plus one E8M0 byte per 32 weights) and its bf16 biases, the
+    router and its bias, tokens in (bf16) and out (fp32)."""
+    per_w = 2.0 if case.w_dtype == "bf16" else 0.5 + 1.0 / 32.0
+    per_expert = (2 * case.F * case.H + case.H * case.F) * per_w + (2 * case.F + case.H) * 2
+    b = n_active * per_expert + case.E * case.H * 2 + case.E * 2 + T * case.H * 2 + T * case.H * 4
     if case.has_shared:
         b += 3 * case.Fs * case.H * 2 + case.H * 2
     return b
@@ -274,21 +305,38 @@ def recorded_traffic():
         return None
 
 
-def cpu_baseline(case, seconds):
+def cpu_baseline(case, run_seconds):
     """The oracle (plain C, double accumulation, OpenMP over tokens) on the
-    decode batch, repeated for about `seconds` seconds."""
+    decode batch: 5 timed runs of a fixed number of whole-batch passes (sized
+    to about run_seconds each), median, with one thread and with all the
+    threads the process may use."""
+    import statistics
     import oracle
     L = oracle.Layer(case)
-    n, t0 = 0, time.perf_counter()
-    while True:
+    avail = len(os.sched_getaffinity(0))
+    forms = {}
+    for name, threads in (("single_thread", 1), ("openmp", avail)):
+        oracle.set_threads(threads)
+        t0 = time.perf_counter()
         L.forward()
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    return {"value": round(n * case.T / el, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d repeats of the whole T=%d decode batch (%.1f s)" % (n, case.T, el)}
+        reps = max(1, int(run_seconds / max(time.perf_counter() - t0, 1e-6)))
+        runs = []
+        for _ in range(5):
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                L.forward()
+            runs.append(time.perf_counter() - t0)
+        med = statistics.median(runs)
+        forms[name] = {"value": round(reps * case.T / med, 3), "unit": "tokens/s",
+                       "cores": min(threads, case.T), "threads": threads,
+                       "runs_s": [round(r, 3) for r in runs], "passes_per_run": reps}
+    oracle.set_threads(avail)
+    omp = forms["openmp"]
+    return {"value": omp["value"], "unit": "tokens/s", "cores": omp["cores"], "kind": "oracle",
+            "sample": "median of 5 runs of %d passes over the whole T=%d decode batch, OpenMP over tokens "
+                      "(%d threads available, at most %d busy: one per token)" % (omp["passes_per_run"], case.T,
+                                                                                  avail, case.T),
+            "nproc": avail, "single_thread": forms["single_thread"], "openmp": forms["openmp"]}
 
 
 def main():
@@ -307,12 +355,19 @@ def main():
     torch.cuda.set_device(0)
     t0 = time.perf_counter()
     dec = synth.make_case("qwen35moe_decode", T=8)
+    # seeded token batches of the same layer: batch 0 is the case's own x
+    xs = [dec.t["x"]] + [synth.normal("x", (dec.T, dec.H), 1.0, "bf16", synth.BASE_SEED + b) for b in range(1, a.batches)]
     log("decode case generated in %.1f s" % (time.perf_counter() - t0))
-    layer = Layer(dec, a.copies)
+    layer = Layer(dec, a.copies, xs=xs)
+    per_batch = []
+    for b in range(len(xs)):
+        b_ms, _ = time_loop(layer.forward_batch(b), max(a.steps // 2, 20), a.warmup)
+        per_batch.append({"batch": b, "ms_per_step": round(b_ms, 5), "tokens_per_s": round(dec.T / (b_ms * 1e-3), 1),
+                          "active_experts": active_experts(layer.idx.cpu().numpy(), dec.E)})
     ms, wall = time_loop(layer.forward, a.steps, a.warmup)
-    n_active = active_experts(layer.idx.cpu().numpy(), dec.E)
+    actives = [p_["active_experts"] for p_ in per_batch]
     tok_s = dec.T / (ms * 1e-3)
-    log("decode: %.4f ms/step, %.0f tokens/s, %d active experts" % (ms, tok_s, n_active))
+    log("decode: %.4f ms/step, %.0f tokens/s over %d batches (active experts %s)" % (ms, tok_s, len(xs), actives))
     g_ms = graph_replay_ms(layer, a.steps, a.warmup)
     log("decode, HIP graph replay: %.4f ms/step" % g_ms)
     block = None
@@ -334,15 +389,17 @@ def main():
         layer.ops(s)
     torch.cuda.synchronize()
     for s in range(a.steps):
-        layer.ops(s, evs[s])
+        layer.ops(a.warmup + s, evs[s])
     torch.cuda.synchronize()
-    k_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
-    gb = gateup_bytes(dec, n_active, dec.T)
-    achieved = gb / (k_ms * 1e-3) / 1e9
+    k_times = [e0.elapsed_time(e1) for e0, e1 in evs]
+    k_ms = float(np.mean(k_times))
+    k_bytes = [gateup_bytes(dec, actives[(a.warmup + s) % len(xs)], dec.T) for s in range(a.steps)]
+    gb = float(np.mean(k_bytes))
+    achieved = sum(k_bytes) / (sum(k_times) * 1e-3) / 1e9
     roofline = {"bound": "hbm", "kernel": "k_gateup_gemv (expert gate/up + SwiGLU)", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": recorded_traffic(),
-                "kernel_ms": round(k_ms, 5), "algorithmic_bytes": gb}
+                "kernel_ms": round(k_ms, 5), "algorithmic_bytes": round(gb)}
     if a.copy_calib_mib:
         src = torch.empty(a.copy_calib_mib * 2 ** 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -350,7 +407,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    lb = layer_bytes(dec, n_active, dec.T)
+    lb = float(np.mean([layer_bytes(dec, n, dec.T) for n in actives]))
     layer_gbs = lb / (ms * 1e-3) / 1e9
 
     result = {
@@ -359,11 +416,13 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "qwen35moe-shaped decode MoE layer", "tokens": dec.T, "hidden": dec.H,
                    "n_expert": dec.E, "top_k": dec.k, "expert_ff": dec.F, "shared_ff": dec.Fs,
-                   "active_experts": n_active, "weight_copies_rotated": a.copies,
-                   "layer_algorithmic_bytes": lb, "layer_GBps": round(layer_gbs, 1),
-                   "layer_frac_hbm": round(layer_gbs / HBM_PEAK_GBS, 4), "wall_s": round(wall, 3)},
+                   "token_batches_rotated": len(xs), "active_experts_per_batch": actives,
+                   "weight_copies_rotated": a.copies,
+                   "layer_algorithmic_bytes": round(lb), "layer_GBps": round(layer_gbs, 1),
+                   "layer_frac_hbm": round(layer_gbs / HBM_PEAK_GBS, 4), "wall_s": round(wall, 3),
+                   "per_batch": per_batch},
         "graph_replay": {"ms_per_step": round(g_ms, 5), "tokens_per_s": round(dec.T / (g_ms * 1e-3), 1),
-                         "note": "the same moe_forward pass captured once per weight copy in a HIP graph"},
+                         "note": "the same moe_forward passes captured once per (batch, weight copy) in HIP graphs"},
         "prenorm_block": block,
         "roofline": roofline,
     }
@@ -385,41 +444,58 @@ def main():
         fl = layer_flops(pre, T)
         tf = fl / (tot * 1e-3) / 1e12
         pb = layer_bytes(pre, pre.E, T)
+        attainable = min(BF16_PEAK_TFLOPS, fl / pb * HBM_PEAK_GBS / 1e3)
         result["prefill"] = {
             "workload": "qwen35moe-shaped prefill MoE layer, Zipf(1.0) expert load", "tokens": T,
             "ms_per_step": round(tot, 4), "layer_ms_drawn_logits": round(p_ms, 4), "router_ms": round(r_ms, 4),
             "tokens_per_s": round(T / (tot * 1e-3), 1), "TFLOPs": round(tf, 2),
             "frac_bf16_mfma_peak": round(tf / BF16_PEAK_TFLOPS, 4), "algorithmic_flops": fl,
-            "algorithmic_bytes": pb, "frac_hbm": round(pb / (tot * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            "algorithmic_bytes": pb, "frac_hbm": round(pb / (tot * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "attainable_TFLOPs": round(attainable, 1), "frac_attainable": round(tf / attainable, 4)}
         log("prefill: %.3f ms (+router %.3f ms), %.1f TFLOP/s" % (p_ms, r_ms, tf))
         del pl, rt
+        torch.cuda.empty_cache()
 
-    if a.gptoss:
-        del dec
+    if not a.no_gptoss:
         result["gptoss"] = {}
         for name, T, aq in (("gptoss20b_bf16", 2048, "none"), ("gptoss20b_mxfp4", 16, "none"),
                             ("gptoss20b_mxfp4", 2048, "none"), ("gptoss20b_mxfp4", 16, "mxfp8"),
                             ("gptoss20b_mxfp4", 2048, "mxfp8")):
             c = synth.make_case(name, T=T)
             c.act_quant = aq
-            gl = Layer(c, 2)
-            g_ms, _ = time_loop(gl.forward, a.prefill_steps if T > 64 else a.steps, 3)
-            n_act = active_experts(gl.idx.cpu().numpy(), c.E)
-            per_expert = (2 * c.F * c.H + c.H * c.F) * (2 if c.w_dtype == "bf16" else 0.5 + 1 / 16.0)
-            byt = n_act * per_expert + c.E * c.H * 2 + T * c.H * 6
+            few = T <= 64
+            gxs = [c.t["x"]] + ([synth.normal("x", (T, c.H), 1.0, "bf16", synth.BASE_SEED + b)
+                                 for b in range(1, a.batches)] if few else [])
+            gl = Layer(c, a.copies if few else 2, xs=gxs)
+            n_act = []
+            for b in range(len(gxs)):
+                gl.forward_batch(b)(0)
+                torch.cuda.synchronize()
+                n_act.append(active_experts(gl.idx.cpu().numpy(), c.E))
+            g_ms, _ = time_loop(gl.forward, a.steps if few else a.prefill_steps, 3 if not few else a.warmup)
+            byt = float(np.mean([gptoss_layer_bytes(c, n, T) for n in n_act]))
             fl = layer_flops(c, T)
+            tf = fl / (g_ms * 1e-3) / 1e12
             key = "%s_T%d%s" % (name, T, "_mxfp8_act" if aq == "mxfp8" else "")
-            result["gptoss"][key] = {"ms": round(g_ms, 4), "tokens_per_s": round(T / (g_ms * 1e-3), 1),
-                                     "TFLOPs": round(fl / (g_ms * 1e-3) / 1e12, 2),
-                                     "frac_hbm": round(byt / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                     "active_experts": n_act}
-            log("%s: %s" % (key, result["gptoss"][key]))
+            rec = {"ms": round(g_ms, 4), "tokens_per_s": round(T / (g_ms * 1e-3), 1), "TFLOPs": round(tf, 2),
+                   "algorithmic_bytes": round(byt), "frac_hbm": round(byt / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "active_experts": n_act if few else n_act[0]}
+            if not few:
+                peak = FP8_PEAK_TFLOPS if aq == "mxfp8" else BF16_PEAK_TFLOPS
+                rec["bound"] = "fp8 mfma" if aq == "mxfp8" else "bf16 mfma"
+                rec["frac_mfma_peak"] = round(tf / peak, 4)
+                rec["attainable_TFLOPs"] = round(min(peak, fl / byt * HBM_PEAK_GBS / 1e3), 1)
+                rec["frac_attainable"] = round(tf / rec["attainable_TFLOPs"], 4)
+            else:
+                rec["bound"] = "hbm"
+                rec["token_batches_rotated"] = len(gxs)
+            result["gptoss"][key] = rec
+            log("%s: %s" % (key, rec))
             del gl, c
             torch.cuda.empty_cache()
-        dec = synth.make_case("qwen35moe_decode", T=8)
 
     if not a.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(dec, a.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(dec, a.cpu_run_seconds)
         log("cpu oracle: %s" % result["cpu_baseline"])
     print(json.dumps(result), flush=True)
 

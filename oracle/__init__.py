@@ -93,6 +93,8 @@ def lib():
         L.ref_forward.argtypes = [P(RefCfg), P(RefWeights), P(RefMat), i32, vp, vp, vp, i32,
                                   vp, vp, vp, vp]
         L.ref_forward_dense.argtypes = [P(RefCfg), P(RefWeights), P(RefMat), i32, vp, vp]
+        L.ref_set_threads.argtypes = [i32]
+        L.ref_set_threads.restype = i32
         _lib = L
     return _lib
 
@@ -315,6 +317,11 @@ def permute(E, k, T, shared, topk_idx):
     ap = np.empty(max(n, 1), np.int32)
     lib().ref_permute(E, k, T, int(shared), _p(topk_idx), _p(offsets), _p(sa), _p(ap))
     return offsets, sa[:n], ap[:n]
+
+
+def set_threads(n: int) -> int:
+    """Threads of the oracle's parallel loops (0: unchanged); returns the count."""
+    return lib().ref_set_threads(n)
 
 
 def mxfp4_value(code, e8m0):

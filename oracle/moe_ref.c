@@ -7,6 +7,9 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 /* ---------------------------------------------------------------- inputs */
 
@@ -575,4 +578,16 @@ void ref_forward_dense(const ref_cfg* c, const ref_weights* w, const ref_mat* x,
   }
   free(logits); free(idx); free(wt); free(scores); free(s); free(sg);
   free(xr); free(hv); free(y);
+}
+
+/* Threads of the parallel-over-tokens loops (the CPU baseline times the
+ * oracle with one thread and with all of them); returns the count set. */
+int32_t ref_set_threads(int32_t n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+  return (int32_t)omp_get_max_threads();
+#else
+  (void)n;
+  return 1;
+#endif
 }

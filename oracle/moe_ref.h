@@ -154,6 +154,10 @@ void ref_forward(const ref_cfg* c, const ref_weights* w, const ref_mat* x, int32
 void ref_forward_dense(const ref_cfg* c, const ref_weights* w, const ref_mat* x, int32_t T,
                        const float* logits_in, double* out);
 
+/* Threads used by the parallel-over-tokens loops (n <= 0 leaves the count
+ * unchanged); returns the current count. */
+int32_t ref_set_threads(int32_t n);
+
 #ifdef __cplusplus
 }
 #endif
