@@ -130,12 +130,10 @@ __device__ __forceinline__ void pipe_issue(const Pipe& p, int s, int wid, uint8_
   }
 }
 
-// Issue step s2 of the pair (p, q): p's step s2 while s2 < p.nk, else q's
-// step s2 - p.nk.  Every field is chosen with a select on a wave-uniform
+// The pipe whose step s2 comes next: p while s2 < p.nk, else q (its step
+// s2 - p.nk).  Every field is chosen with a select on a wave-uniform
 // condition, so a single copy of the loads is emitted.
-__device__ __forceinline__ void pipe_issue_pq(const Pipe& p, const Pipe& q, int s2, int wid, uint8_t* __restrict__ la,
-                                              uint8_t* __restrict__ lb, CodeRegs& cr) {
-  const bool uq = s2 >= p.nk;
+__device__ __forceinline__ Pipe pipe_pick(const Pipe& p, const Pipe& q, bool uq) {
   Pipe x;
   x.ra = uq ? q.ra : p.ra;
   x.rw0 = uq ? q.rw0 : p.rw0;
@@ -150,7 +148,14 @@ __device__ __forceinline__ void pipe_issue_pq(const Pipe& p, const Pipe& q, int 
   x.mx = uq ? q.mx : p.mx;
   x.nk = uq ? q.nk : p.nk;
   x.k0 = uq ? q.k0 : p.k0;
-  pipe_issue(x, uq ? s2 - p.nk : s2, wid, la, lb, cr);
+  return x;
+}
+
+// Issue step s2 of the pair (p, q) all at once (MXFP4 kernels).
+__device__ __forceinline__ void pipe_issue_pq(const Pipe& p, const Pipe& q, int s2, int wid, uint8_t* __restrict__ la,
+                                              uint8_t* __restrict__ lb, CodeRegs& cr) {
+  const bool uq = s2 >= p.nk;
+  pipe_issue(pipe_pick(p, q, uq), uq ? s2 - p.nk : s2, wid, la, lb, cr);
 }
 
 // MXFP4 staging: thread t decodes 32-element block mx_blk(t) of tile row
@@ -234,6 +239,53 @@ __device__ __forceinline__ void pipe_compute(const Frag& f, f32x16_t (&acc)[2][2
   mfma4(acc, k2);
   lds_wait<0>(k3);
   mfma4(acc, k3);
+}
+
+__device__ __forceinline__ void mfma1(f32x16_t (&acc)[2][2], const KFrag& o, int i, int j) {
+  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.a[i], o.b[j], acc[i][j], 0, 0, 0);
+}
+
+// The same K step for bf16 weights, with the six buffer->LDS loads of step s
+// of pipe x (into stage la2 / lb2) issued one at a time between the MFMAs of
+// the first two sub-steps.  Issued as a burst at the step's start, a load
+// that waits for room in the address queue holds the wave before its first
+// MFMA; spread out, the MFMAs already issued keep the matrix pipe busy
+// meanwhile (7-9% faster grouped GEMMs).  The scheduling barriers keep this
+// order.
+__device__ __forceinline__ void pipe_compute_issue(const Frag& f, f32x16_t (&acc)[2][2], const uint8_t* la,
+                                                   const uint8_t* lb, const Pipe& x, int s, int wid,
+                                                   uint8_t* __restrict__ la2, uint8_t* __restrict__ lb2) {
+  const uint32_t kb = s < x.nk ? (uint32_t)(x.k0 + s) * BK * 2 : kOutOfRange;
+  auto ld_a = [&](int i) { dma16(x.ra, la2 + (i * kThreads + wid * kWave) * 16, x.a_off[i] + kb); };
+  auto ld_b = [&](int i) {
+    const bool up = x.two_mats && i >= kBChunks / 2;  // pieces i >= 2 are tile rows >= 128
+    dma16(up ? x.rw1 : x.rw0, lb2 + (i * kThreads + wid * kWave) * 16, x.b_off[i] + kb);
+  };
+  KFrag k0, k1, k2, k3;
+  read_kfrag(f, 0, la, lb, k0);
+  read_kfrag(f, 1, la, lb, k1);
+  lds_wait<4>(k0);
+  read_kfrag(f, 2, la, lb, k2);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma1(acc, k0, 0, 0); __builtin_amdgcn_sched_barrier(0); ld_a(0); __builtin_amdgcn_sched_barrier(0);
+  mfma1(acc, k0, 0, 1); __builtin_amdgcn_sched_barrier(0); ld_a(1); __builtin_amdgcn_sched_barrier(0);
+  mfma1(acc, k0, 1, 0); __builtin_amdgcn_sched_barrier(0); ld_b(0); __builtin_amdgcn_sched_barrier(0);
+  mfma1(acc, k0, 1, 1); __builtin_amdgcn_sched_barrier(0);
+  lds_wait<4>(k1);
+  read_kfrag(f, 3, la, lb, k3);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma1(acc, k1, 0, 0); __builtin_amdgcn_sched_barrier(0); ld_b(1); __builtin_amdgcn_sched_barrier(0);
+  mfma1(acc, k1, 0, 1); __builtin_amdgcn_sched_barrier(0); ld_b(2); __builtin_amdgcn_sched_barrier(0);
+  mfma1(acc, k1, 1, 0); __builtin_amdgcn_sched_barrier(0); ld_b(3); __builtin_amdgcn_sched_barrier(0);
+  mfma1(acc, k1, 1, 1); __builtin_amdgcn_sched_barrier(0);
+  lds_wait<4>(k2);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma4(acc, k2);
+  __builtin_amdgcn_sched_barrier(0);
+  lds_wait<0>(k3);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma4(acc, k3);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Segment tables in LDS: offsets[0..nseg] and the exclusive prefix of the
@@ -525,8 +577,13 @@ __device__ __forceinline__ void tile_loop(const GemmArgs& a, const Pipe& p, Pipe
     lds_barrier();                                                      \
     const int s2 = (KT) + 2;                                            \
     if (s2 == p.nk) finish_pipe<MODE>(a, q);                            \
-    pipe_issue_pq(p, q, s2, wid, LA2, LB2, CRN);                        \
-    pipe_compute(fr, acc, LA, LB);                                      \
+    if (MX) {                                                           \
+      pipe_issue_pq(p, q, s2, wid, LA2, LB2, CRN);                      \
+      pipe_compute(fr, acc, LA, LB);                                    \
+    } else {                                                            \
+      const bool uq = s2 >= p.nk;                                       \
+      pipe_compute_issue(fr, acc, LA, LB, pipe_pick(p, q, uq), uq ? s2 - p.nk : s2, wid, LA2, LB2); \
+    }                                                                   \
     if (MX && ((KT) + 1 < p.nk ? p.mx : q.mx)) {                        \
       wait_vm<4>();                                                     \
       pipe_put_codes(CRP, LB1);                                         \
