@@ -483,7 +483,7 @@ __device__ __forceinline__ void burst_dot(const uint4 (&w)[2][NPL], const uint32
         const bf16x2_t u3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c1[q], s1, 3);
 #pragma unroll
         for (int i = 0; i < NT; ++i) {
-          const uint4 xv = reinterpret_cast<const uint4*>(xs + (size_t)i * K + (size_t)p * 32)[q];
+          const uint4 xv = reinterpret_cast<const uint4*>(xs + (size_t)i * K)[q * P + p];
           const bf16x2_t x0 = __builtin_bit_cast(bf16x2_t, xv.x), x1 = __builtin_bit_cast(bf16x2_t, xv.y);
           const bf16x2_t x2 = __builtin_bit_cast(bf16x2_t, xv.z), x3 = __builtin_bit_cast(bf16x2_t, xv.w);
           float a0 = acc[0][i], a1 = acc[1][i];
@@ -514,14 +514,19 @@ __device__ __forceinline__ void burst_dot_n(int nt, const uint4 (&w)[2][NPL], co
 }
 
 // Stage activation rows [tb, tb + nt) of the segment (row i of src_row(i))
-// into xs, 16 bytes per thread per step.
+// into xs, 16 bytes per thread per step.  A row's 16-byte chunk g (quarter
+// g % 4 of 32-element piece g / 4) goes to chunk (g % 4) * P + g / 4: the 16
+// lanes of a row pair, which read one quarter of 16 consecutive pieces at a
+// time, then read 256 contiguous bytes, one 16-byte group of banks each (at
+// the piece-major layout their 64-byte stride was a 4-way bank conflict).
 template <typename RowOf>
 __device__ __forceinline__ void stage_rows(uint16_t* xs, int nt, int K, RowOf src_row) {
-  const int pieces = K / 8;  // 16-byte pieces per row
+  const int chunks = K / 8;  // 16-byte chunks per row
+  const int P = K / 32;
   for (int j = 0; j < nt; ++j) {
     const uint4* src = reinterpret_cast<const uint4*>(src_row(j));
     uint4* dst = reinterpret_cast<uint4*>(xs + (size_t)j * K);
-    for (int q = threadIdx.x; q < pieces; q += kBThreads) dst[q] = src[q];
+    for (int g = threadIdx.x; g < chunks; g += kBThreads) dst[(g & 3) * P + (g >> 2)] = src[g];
   }
 }
 

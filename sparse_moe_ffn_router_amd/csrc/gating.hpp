@@ -188,30 +188,33 @@ template <> struct RouterVec<float> {
 // time; every row is reduced in the same order, so bit-equal router rows
 // give bit-equal logits.  PIECES: 16-byte pieces per lane and token held at
 // once; all of a chunk's loads are issued before its first product.
-template <typename XT, int PIECES>
+// The wave takes tokens [t_begin, t_end) in groups of TG.
+template <typename XT, int PIECES, int TG = kRouterTokens>
 __device__ __forceinline__ void router_row(const XT* __restrict__ x, const XT* __restrict__ wr,
                                            const XT* __restrict__ br, const XT* __restrict__ wsg, int T, int H,
-                                           int E, int r, float* __restrict__ logits, float* __restrict__ sgate_pre) {
+                                           int E, int r, float* __restrict__ logits, float* __restrict__ sgate_pre,
+                                           int t_begin = 0, int t_end = -1) {
   constexpr int N = RouterVec<XT>::N;
   const int lane = threadIdx.x & (kWave - 1);
   const uint4* wrow = reinterpret_cast<const uint4*>(r < E ? wr + (size_t)r * H : wsg);
   const int npieces = H / N;
   const float bias = (r < E && br) ? RouterVec<XT>::scalar(br, r) : 0.f;
-  for (int t0 = 0; t0 < T; t0 += kRouterTokens) {
-    float acc[kRouterTokens];
+  if (t_end < 0) t_end = T;
+  for (int t0 = t_begin; t0 < t_end; t0 += TG) {
+    float acc[TG];
 #pragma unroll
-    for (int j = 0; j < kRouterTokens; ++j) acc[j] = 0.f;
+    for (int j = 0; j < TG; ++j) acc[j] = 0.f;
     for (int p0 = 0; p0 < npieces; p0 += PIECES * kWave) {
       // every load of the chunk (row pieces and the tokens' pieces) is
       // issued before the first product, so the wave waits once per chunk
-      uint4 w[PIECES], xv[kRouterTokens][PIECES];
+      uint4 w[PIECES], xv[TG][PIECES];
 #pragma unroll
       for (int i = 0; i < PIECES; ++i) {
         const int pc = p0 + i * kWave + lane;
         w[i] = pc < npieces ? wrow[pc] : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
-      for (int j = 0; j < kRouterTokens; ++j) {
+      for (int j = 0; j < TG; ++j) {
         const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)min(t0 + j, T - 1) * H);
 #pragma unroll
         for (int i = 0; i < PIECES; ++i) {
@@ -220,16 +223,16 @@ __device__ __forceinline__ void router_row(const XT* __restrict__ x, const XT* _
         }
       }
 #pragma unroll
-      for (int j = 0; j < kRouterTokens; ++j)
+      for (int j = 0; j < TG; ++j)
 #pragma unroll
         for (int i = 0; i < PIECES; ++i) acc[j] = RouterVec<XT>::dot(w[i], xv[j][i], acc[j]);
     }
 #pragma unroll
-    for (int j = 0; j < kRouterTokens; ++j) acc[j] = wave_sum(acc[j]);
-    if (lane < kRouterTokens && t0 + lane < T) {
+    for (int j = 0; j < TG; ++j) acc[j] = wave_sum(acc[j]);
+    if (lane < TG && t0 + lane < t_end) {
       float v = acc[0];
 #pragma unroll
-      for (int j = 1; j < kRouterTokens; ++j) v = lane == j ? acc[j] : v;
+      for (int j = 1; j < TG; ++j) v = lane == j ? acc[j] : v;
       if (r < E)
         logits[(size_t)(t0 + lane) * E + r] = v + bias;
       else

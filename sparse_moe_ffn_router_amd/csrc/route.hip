@@ -14,15 +14,19 @@ constexpr int kRouterWaves = 1;   // router rows per workgroup (one per wave)
 
 // Extended router rows: r < E is router_w[r] (written to logits[t][r] with
 // the bias), r == E the shared-expert gate row (written to sgate_pre[t]).
-// One wave per row (router_row).
-template <typename XT>
+// One wave per (row, group of TG tokens): blockIdx.y is the token group.
+// PIECES 16-byte pieces per lane and token are loaded at once (the whole
+// row when PIECES * 64 covers it), so a wave waits for memory once per
+// chunk; a lane's pieces are summed in the same order whatever PIECES is.
+template <typename XT, int PIECES, int TG>
 __global__ __launch_bounds__(kRouterWaves * kWave) void k_router_gemv(
     const XT* __restrict__ x, const XT* __restrict__ wr, const XT* __restrict__ br,
     const XT* __restrict__ wsg, int32_t T, int32_t H, int32_t E, int32_t row0, int32_t row1,
     float* __restrict__ logits, float* __restrict__ sgate_pre) {
   const int r = row0 + blockIdx.x * kRouterWaves + (threadIdx.x / kWave);
   if (r >= row1) return;
-  router_row<XT, 4>(x, wr, br, wsg, T, H, E, r, logits, sgate_pre);
+  const int t0 = blockIdx.y * TG;
+  router_row<XT, PIECES, TG>(x, wr, br, wsg, T, H, E, r, logits, sgate_pre, t0, min(T, t0 + TG));
 }
 
 // The same rows with the pre-norm block's prologue for few tokens: x is the
@@ -98,15 +102,27 @@ hipError_t launch_router_logits(const moe_config* c, const moe_weights* w, const
   const int row1 = (c->shared_ff > 0 && !mfma) ? E + 1 : E;
   if (row1 <= row0 || T == 0) return hipSuccess;
   if (mfma) return launch_router_mfma(c, w, x, T, logits, sgate_pre, s, part);
-  dim3 grid((row1 - row0 + kRouterWaves - 1) / kRouterWaves);
-  if (c->x_dtype == MOE_DTYPE_BF16)
-    k_router_gemv<uint16_t><<<grid, kRouterWaves * kWave, 0, s>>>(
-        (const uint16_t*)x, (const uint16_t*)w->router_w, (const uint16_t*)w->router_b,
-        (const uint16_t*)w->sh_gate_inp, T, c->hidden, E, row0, row1, logits, sgate_pre);
-  else
-    k_router_gemv<float><<<grid, kRouterWaves * kWave, 0, s>>>(
+  const unsigned rows = (unsigned)((row1 - row0 + kRouterWaves - 1) / kRouterWaves);
+  // rows of up to 256 pieces per lane set: 8 tokens per wave; longer rows
+  // (whole row in flight, 6 or 8 pieces per lane): 4 tokens per wave
+  const int pieces = c->hidden / (c->x_dtype == MOE_DTYPE_BF16 ? 8 : 4);
+  if (c->x_dtype == MOE_DTYPE_BF16) {
+    const uint16_t *xx = (const uint16_t*)x, *wr = (const uint16_t*)w->router_w, *br = (const uint16_t*)w->router_b,
+                   *wg = (const uint16_t*)w->sh_gate_inp;
+    if (pieces <= 4 * kWave)
+      k_router_gemv<uint16_t, 4, 8><<<dim3(rows, (T + 7) / 8), kRouterWaves * kWave, 0, s>>>(
+          xx, wr, br, wg, T, c->hidden, E, row0, row1, logits, sgate_pre);
+    else if (pieces <= 6 * kWave)
+      k_router_gemv<uint16_t, 6, 4><<<dim3(rows, (T + 3) / 4), kRouterWaves * kWave, 0, s>>>(
+          xx, wr, br, wg, T, c->hidden, E, row0, row1, logits, sgate_pre);
+    else
+      k_router_gemv<uint16_t, 8, 4><<<dim3(rows, (T + 3) / 4), kRouterWaves * kWave, 0, s>>>(
+          xx, wr, br, wg, T, c->hidden, E, row0, row1, logits, sgate_pre);
+  } else {
+    k_router_gemv<float, 4, 8><<<dim3(rows, (T + 7) / 8), kRouterWaves * kWave, 0, s>>>(
         (const float*)x, (const float*)w->router_w, (const float*)w->router_b, (const float*)w->sh_gate_inp, T,
         c->hidden, E, row0, row1, logits, sgate_pre);
+  }
   return hipGetLastError();
 }
 
