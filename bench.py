@@ -70,10 +70,14 @@ def parse():
     ap.add_argument("--no-gptoss", action="store_true",
                     help="skip the gpt-oss-20b-shaped layers (bf16 T=2048, MXFP4 T=16 and T=2048)")
     ap.add_argument("--batches", type=int, default=N_BATCHES, help="seeded token batches the decode steps rotate over")
+    ap.add_argument("--only", choices=("decode", "prefill", "gptoss"),
+                    help="measure one workload only (counter runs); no JSON line")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
-                    help="after the decode measurement, copy a buffer of this many MiB 5 times (counter calibration)")
+                    help="after the measurements, copy a buffer of this many MiB 5 times (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc output folders and exit")
+    ap.add_argument("--pmc-kernels", default=GATEUP_KERNEL,
+                    help="semicolon-separated kernel name fragments the summary reports (first: the traffic line)")
     return ap.parse_args()
 
 
@@ -257,38 +261,46 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def _pmc_means(folder, counter):
-    """Mean counter value per dispatch (KiB for FETCH_SIZE / WRITE_SIZE) of the
-    gate/up kernel and of the calibration copies, from a rocprofv3 --pmc csv
-    folder.  The calibration copies are the copy dispatches issued after the
-    last gate/up dispatch."""
+def _pmc_means(folder, counter, kernels):
+    """Mean counter value per dispatch (KiB for FETCH_SIZE / WRITE_SIZE) of
+    each kernel (name fragment) and of the calibration copies, from a
+    rocprofv3 --pmc csv folder.  The calibration copies are the copy
+    dispatches issued after every measured kernel's last dispatch."""
     rows = []
     for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
         with open(f) as fh:
             rows += [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
-    gate = [r for r in rows if GATEUP_KERNEL in r["Kernel_Name"]]
-    last = max(int(r["Dispatch_Id"]) for r in gate)
-    copy = [r for r in rows if r["Kernel_Name"] == COPY_KERNEL and int(r["Dispatch_Id"]) > last]
-    mean = lambda rs: (sum(float(r["Counter_Value"]) for r in rs) / len(rs), len(rs))
-    return {GATEUP_KERNEL: mean(gate), COPY_KERNEL: mean(copy)}
+    mean = lambda rs: (sum(float(r["Counter_Value"]) for r in rs) / len(rs), len(rs)) if rs else (0.0, 0)
+    out, last = {}, 0
+    for k in kernels:
+        ks = [r for r in rows if k in r["Kernel_Name"]]
+        out[k] = mean(ks)
+        if ks:
+            last = max(last, max(int(r["Dispatch_Id"]) for r in ks))
+    out[COPY_KERNEL] = mean([r for r in rows if r["Kernel_Name"] == COPY_KERNEL and int(r["Dispatch_Id"]) > last])
+    return out
 
 
-def pmc_summary(fetch_dir, write_dir, copy_mib):
-    """Text summary: the gate/up kernel's FETCH_SIZE and WRITE_SIZE per launch,
-    each scaled by copy bytes / the copy kernel's counter."""
+def pmc_summary(fetch_dir, write_dir, copy_mib, kernels):
+    """Text summary: each kernel's FETCH_SIZE and WRITE_SIZE per launch, each
+    scaled by copy bytes / the copy kernel's counter.  The first kernel's
+    total is the traffic line the JSON output reads back."""
     copy_bytes = copy_mib * 2 ** 20
-    out, total = [], 0.0
+    out, total = [], {k: 0.0 for k in kernels}
     for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        m = _pmc_means(folder, counter)
-        (ck, cn), (gk, gn) = m[COPY_KERNEL], m[GATEUP_KERNEL]
+        m = _pmc_means(folder, counter, kernels)
+        ck, cn = m[COPY_KERNEL]
         factor = copy_bytes / (ck * 1024.0)
-        b = gk * 1024.0 * factor
-        total += b
-        out += ["%s: copy of %d bytes counts %.1f KiB/dispatch (%d dispatches) -> factor %.4f" %
-                (counter, copy_bytes, ck, cn, factor),
-                "%s: %s %.1f KiB/dispatch (%d dispatches) -> %.0f bytes per launch" %
-                (counter, GATEUP_KERNEL, gk, gn, b)]
-    out += ["traffic_bytes_per_launch = %.0f" % total, "source_sha256 = %s" % kernel_source_hash()]
+        out.append("%s: copy of %d bytes counts %.1f KiB/dispatch (%d dispatches) -> factor %.4f" %
+                   (counter, copy_bytes, ck, cn, factor))
+        for k in kernels:
+            gk, gn = m[k]
+            b = gk * 1024.0 * factor
+            total[k] += b
+            out.append("%s: %s %.1f KiB/dispatch (%d dispatches) -> %.0f bytes per launch" % (counter, k, gk, gn, b))
+    for k in kernels[1:]:
+        out.append("traffic %s = %.0f bytes per launch" % (k, total[k]))
+    out += ["traffic_bytes_per_launch = %.0f" % total[kernels[0]], "source_sha256 = %s" % kernel_source_hash()]
     return "\n".join(out)
 
 
@@ -342,7 +354,7 @@ def cpu_baseline(case, run_seconds):
 def main():
     a = parse()
     if a.pmc_summary:
-        print(pmc_summary(a.pmc_summary[0], a.pmc_summary[1], a.copy_calib_mib or 1024))
+        print(pmc_summary(a.pmc_summary[0], a.pmc_summary[1], a.copy_calib_mib or 1024, a.pmc_kernels.split(";")))
         return
     if a.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (requested --gpus %d)" % a.gpus,
@@ -358,78 +370,73 @@ def main():
     # seeded token batches of the same layer: batch 0 is the case's own x
     xs = [dec.t["x"]] + [synth.normal("x", (dec.T, dec.H), 1.0, "bf16", synth.BASE_SEED + b) for b in range(1, a.batches)]
     log("decode case generated in %.1f s" % (time.perf_counter() - t0))
-    layer = Layer(dec, a.copies, xs=xs)
-    per_batch = []
-    for b in range(len(xs)):
-        b_ms, _ = time_loop(layer.forward_batch(b), max(a.steps // 2, 20), a.warmup)
-        per_batch.append({"batch": b, "ms_per_step": round(b_ms, 5), "tokens_per_s": round(dec.T / (b_ms * 1e-3), 1),
-                          "active_experts": active_experts(layer.idx.cpu().numpy(), dec.E)})
-    ms, wall = time_loop(layer.forward, a.steps, a.warmup)
-    actives = [p_["active_experts"] for p_ in per_batch]
-    tok_s = dec.T / (ms * 1e-3)
-    log("decode: %.4f ms/step, %.0f tokens/s over %d batches (active experts %s)" % (ms, tok_s, len(xs), actives))
-    g_ms = graph_replay_ms(layer, a.steps, a.warmup)
-    log("decode, HIP graph replay: %.4f ms/step" % g_ms)
-    block = None
-    if not a.no_block:
-        b_ms, _ = time_loop(layer.block, a.steps, a.warmup)
-        b_active = active_experts(layer.idx.cpu().numpy(), dec.E)
-        bx_ms, _ = time_loop(layer.forward_on_xn, a.steps, a.warmup)
-        log("decode, pre-norm block (RMSNorm + layer + residual): %.4f ms/step; the layer alone on the same "
-            "normalised rows %.4f ms (%d active experts)" % (b_ms, bx_ms, b_active))
-        block = {"ms_per_step": round(b_ms, 5), "tokens_per_s": round(dec.T / (b_ms * 1e-3), 1),
-                 "layer_on_same_rows_ms": round(bx_ms, 5), "over_layer_ms": round(b_ms - bx_ms, 5),
-                 "active_experts": b_active,
-                 "note": "moe_forward_prenorm on residual rows (RMSNorm in the router-product kernel, "
-                         "residual add in the combine) against moe_forward on the rows it normalised"}
+    result = {}
+    if a.only in (None, "decode"):
+        layer = Layer(dec, a.copies, xs=xs)
+        per_batch = []
+        for b in range(len(xs)):
+            b_ms, _ = time_loop(layer.forward_batch(b), max(a.steps // 2, 20), a.warmup)
+            per_batch.append({"batch": b, "ms_per_step": round(b_ms, 5), "tokens_per_s": round(dec.T / (b_ms * 1e-3), 1),
+                              "active_experts": active_experts(layer.idx.cpu().numpy(), dec.E)})
+        ms, wall = time_loop(layer.forward, a.steps, a.warmup)
+        actives = [p_["active_experts"] for p_ in per_batch]
+        tok_s = dec.T / (ms * 1e-3)
+        log("decode: %.4f ms/step, %.0f tokens/s over %d batches (active experts %s)" % (ms, tok_s, len(xs), actives))
+        g_ms = graph_replay_ms(layer, a.steps, a.warmup)
+        log("decode, HIP graph replay: %.4f ms/step" % g_ms)
+        block = None
+        if not a.no_block:
+            b_ms, _ = time_loop(layer.block, a.steps, a.warmup)
+            b_active = active_experts(layer.idx.cpu().numpy(), dec.E)
+            bx_ms, _ = time_loop(layer.forward_on_xn, a.steps, a.warmup)
+            log("decode, pre-norm block (RMSNorm + layer + residual): %.4f ms/step; the layer alone on the same "
+                "normalised rows %.4f ms (%d active experts)" % (b_ms, bx_ms, b_active))
+            block = {"ms_per_step": round(b_ms, 5), "tokens_per_s": round(dec.T / (b_ms * 1e-3), 1),
+                     "layer_on_same_rows_ms": round(bx_ms, 5), "over_layer_ms": round(b_ms - bx_ms, 5),
+                     "active_experts": b_active,
+                     "note": "moe_forward_prenorm on residual rows (RMSNorm in the router-product kernel, "
+                             "residual add in the combine) against moe_forward on the rows it normalised"}
 
-    # dominant kernel (expert gate/up), timed with events on the launch stream
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
-    for s in range(a.warmup):
-        layer.ops(s)
-    torch.cuda.synchronize()
-    for s in range(a.steps):
-        layer.ops(a.warmup + s, evs[s])
-    torch.cuda.synchronize()
-    k_times = [e0.elapsed_time(e1) for e0, e1 in evs]
-    k_ms = float(np.mean(k_times))
-    k_bytes = [gateup_bytes(dec, actives[(a.warmup + s) % len(xs)], dec.T) for s in range(a.steps)]
-    gb = float(np.mean(k_bytes))
-    achieved = sum(k_bytes) / (sum(k_times) * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "kernel": "k_gateup_gemv (expert gate/up + SwiGLU)", "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": recorded_traffic(),
-                "kernel_ms": round(k_ms, 5), "algorithmic_bytes": round(gb)}
-    if a.copy_calib_mib:
-        src = torch.empty(a.copy_calib_mib * 2 ** 20, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
+        # dominant kernel (expert gate/up), timed with events on the launch stream
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+        for s in range(a.warmup):
+            layer.ops(s)
         torch.cuda.synchronize()
-        del src, dst
-    lb = float(np.mean([layer_bytes(dec, n, dec.T) for n in actives]))
-    layer_gbs = lb / (ms * 1e-3) / 1e9
+        for s in range(a.steps):
+            layer.ops(a.warmup + s, evs[s])
+        torch.cuda.synchronize()
+        k_times = [e0.elapsed_time(e1) for e0, e1 in evs]
+        k_ms = float(np.mean(k_times))
+        k_bytes = [gateup_bytes(dec, actives[(a.warmup + s) % len(xs)], dec.T) for s in range(a.steps)]
+        gb = float(np.mean(k_bytes))
+        achieved = sum(k_bytes) / (sum(k_times) * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": "k_gateup_gemv (expert gate/up + SwiGLU)", "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": recorded_traffic(),
+                    "kernel_ms": round(k_ms, 5), "algorithmic_bytes": round(gb)}
+        lb = float(np.mean([layer_bytes(dec, n, dec.T) for n in actives]))
+        layer_gbs = lb / (ms * 1e-3) / 1e9
 
-    result = {
-        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
-        "warmup": a.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "qwen35moe-shaped decode MoE layer", "tokens": dec.T, "hidden": dec.H,
-                   "n_expert": dec.E, "top_k": dec.k, "expert_ff": dec.F, "shared_ff": dec.Fs,
-                   "token_batches_rotated": len(xs), "active_experts_per_batch": actives,
-                   "weight_copies_rotated": a.copies,
-                   "layer_algorithmic_bytes": round(lb), "layer_GBps": round(layer_gbs, 1),
-                   "layer_frac_hbm": round(layer_gbs / HBM_PEAK_GBS, 4), "wall_s": round(wall, 3),
-                   "per_batch": per_batch},
-        "graph_replay": {"ms_per_step": round(g_ms, 5), "tokens_per_s": round(dec.T / (g_ms * 1e-3), 1),
-                         "note": "the same moe_forward passes captured once per (batch, weight copy) in HIP graphs"},
-        "prenorm_block": block,
-        "roofline": roofline,
-    }
-    del layer
-    torch.cuda.empty_cache()
+        result = {
+            "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+            "warmup": a.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "qwen35moe-shaped decode MoE layer", "tokens": dec.T, "hidden": dec.H,
+                       "n_expert": dec.E, "top_k": dec.k, "expert_ff": dec.F, "shared_ff": dec.Fs,
+                       "token_batches_rotated": len(xs), "active_experts_per_batch": actives,
+                       "weight_copies_rotated": a.copies,
+                       "layer_algorithmic_bytes": round(lb), "layer_GBps": round(layer_gbs, 1),
+                       "layer_frac_hbm": round(layer_gbs / HBM_PEAK_GBS, 4), "wall_s": round(wall, 3),
+                       "per_batch": per_batch},
+            "graph_replay": {"ms_per_step": round(g_ms, 5), "tokens_per_s": round(dec.T / (g_ms * 1e-3), 1),
+                             "note": "the same moe_forward passes captured once per (batch, weight copy) in HIP graphs"},
+            "prenorm_block": block,
+            "roofline": roofline,
+        }
+        del layer
+        torch.cuda.empty_cache()
 
-    if not a.no_prefill:
+    if not a.no_prefill and a.only in (None, "prefill"):
         T = 4096
         pre = synth.make_case("qwen35moe_prefill_zipf", T=T, only={"x", "logits"})
         pre.t.update({k: v for k, v in dec.t.items() if k != "x"})
@@ -456,7 +463,7 @@ def main():
         del pl, rt
         torch.cuda.empty_cache()
 
-    if not a.no_gptoss:
+    if not a.no_gptoss and a.only in (None, "gptoss"):
         result["gptoss"] = {}
         for name, T, aq in (("gptoss20b_bf16", 2048, "none"), ("gptoss20b_mxfp4", 16, "none"),
                             ("gptoss20b_mxfp4", 2048, "none"), ("gptoss20b_mxfp4", 16, "mxfp8"),
@@ -494,6 +501,15 @@ def main():
             del gl, c
             torch.cuda.empty_cache()
 
+    if a.copy_calib_mib:
+        src = torch.empty(a.copy_calib_mib * 2 ** 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if a.only:
+        return
     if not a.no_cpu:
         result["cpu_baseline"] = cpu_baseline(dec, a.cpu_run_seconds)
         log("cpu oracle: %s" % result["cpu_baseline"])
