@@ -522,9 +522,31 @@ __device__ __forceinline__ void finish_pipe(const GemmArgs& a, Pipe& p) {
   }
 }
 
+// Field by field (a whole-struct copy left never-read slices of the
+// structs in scratch memory, whose copies waited for every load in flight).
+__device__ __forceinline__ void pipe_copy(Pipe& d, const Pipe& s) {
+  d.ra = s.ra;
+  d.rw0 = s.rw0;
+  d.rw1 = s.rw1;
+  d.rsc = s.rsc;
+#pragma unroll
+  for (int i = 0; i < kAChunks; ++i) {
+    d.a_off[i] = s.a_off[i];
+    d.a_ok[i] = s.a_ok[i];
+  }
+#pragma unroll
+  for (int i = 0; i < kBChunks; ++i) d.b_off[i] = s.b_off[i];
+  d.sc_off = s.sc_off;
+  d.ids = s.ids;
+  d.k0 = s.k0;
+  d.two_mats = s.two_mats;
+  d.mx = s.mx;
+  d.nk = s.nk;
+}
+
 // A pipe with no steps: its loads all read zeros.
 __device__ __forceinline__ void null_pipe(const Pipe& like, Pipe& p) {
-  p = like;
+  pipe_copy(p, like);
   p.nk = 0;
 #pragma unroll
   for (int i = 0; i < kAChunks; ++i) {
@@ -599,9 +621,9 @@ __device__ __forceinline__ void tile_loop(const GemmArgs& a, const Pipe& p, Pipe
 
 // Epilogue.  Lane l of a 32x32 block holds column (l & 31) and rows
 // (q / 4) * 8 + (l / 32) * 4 + (q % 4), q = 0..15.
-template <int MODE>
+template <int MODE, bool BIAS_LDS = false>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, const Tile& t, const f32x16_t (&acc)[2][2], int wm,
-                                         int wn, const int32_t* ids) {
+                                         int wn, const int32_t* ids, const uint32_t* bias_lds = nullptr) {
   const int lane = threadIdx.x & (kWave - 1);
   const int colin = lane & 31;
   const int64_t nas = (int64_t)a.T * a.k;
@@ -609,7 +631,11 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const Tile& t, const
     const int f = t.c0 + wn * 32 + colin;
     if (f < t.Fe) {
       float bg = 0.f, bu = 0.f;
-      if (a.oai && !t.sh && a.bias) {
+      if (BIAS_LDS) {
+        const uint32_t gu = (uint32_t)ds_read4_sync(reinterpret_cast<const int32_t*>(bias_lds) + wn * 32 + colin);
+        bg = __uint_as_float(gu << 16);
+        bu = __uint_as_float(gu & 0xFFFF0000u);
+      } else if (a.oai && !t.sh && a.bias) {
         bg = __uint_as_float((uint32_t)a.bias[(size_t)t.seg * 2 * a.F + 2 * f] << 16);
         bu = __uint_as_float((uint32_t)a.bias[(size_t)t.seg * 2 * a.F + 2 * f + 1] << 16);
       }
@@ -647,7 +673,12 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, const Tile& t, const
       if (o < t.ncols) {
         float bias = 0.f;
         if (MODE == MODE_ROUTER && a.bias) bias = __uint_as_float((uint32_t)a.bias[o] << 16);
-        if (MODE == MODE_DOWN && !t.sh && a.bias) bias = __uint_as_float((uint32_t)a.bias[(size_t)t.seg * a.H + o] << 16);
+        if (MODE == MODE_DOWN && BIAS_LDS) {
+          const uint32_t w = (uint32_t)ds_read4_sync(reinterpret_cast<const int32_t*>(bias_lds) + (o - t.c0) / 2);
+          bias = __uint_as_float(((o - t.c0) & 1 ? w >> 16 : w & 0xFFFFu) << 16);
+        } else if (MODE == MODE_DOWN && !t.sh && a.bias) {
+          bias = __uint_as_float((uint32_t)a.bias[(size_t)t.seg * a.H + o] << 16);
+        }
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -761,8 +792,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
     epilogue<MODE>(a, tc, acc, wm, wn, pc.ids);
     if (!more) break;
     phase = (phase + pc.nk) % 3;
-    tc = tn;
-    pc = pn;
+    tile_at<MODE>(a, st, lin, total_m, tc);  // the tile of pn
+    pipe_copy(pc, pn);
     lin += nslots;
     more = next_tile<MODE>(a, st, lin, lin_end, nslots, total_m, tn);
     if (more)
@@ -785,7 +816,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
 // of 64 code bytes (slot p ^ ((n >> 2) & 3) of a row n: 16 consecutive rows
 // read at one logical piece fall in 16 distinct 16-byte bank groups) and the
 // activation rows' scale words; the tile's weight scales, contiguous in the
-// caller's [rows][K/32] layout, are loaded into LDS once per tile.
+// caller's [rows][K/32] layout, sit in LDS as one block per tile (the next
+// tile's block streams in while the current tile runs).
 //
 // Lane layout of the scaled MFMA (measured on gfx950): lane l holds operand
 // row l % 32; for the E4M3 operand, K elements 16h..16h+15 of the slice's
@@ -795,8 +827,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
 // result layout is the 32x32 one of the bf16 MFMA.
 
 constexpr int BK8 = 128;
-constexpr int kMaxScaleRow = 4096 / 32;  // E8M0 bytes per weight row at most (K <= 4096)
-constexpr int kLoads8 = 5;               // loads per thread per step: 2 A, 2 B, 1 scale word
+constexpr int kLoads8 = 6;  // loads per thread per step: 2 A, 2 B, 1 activation scale word, 1 scale block chunk
 
 __device__ __forceinline__ int swz_slot4(int n, int p) { return p ^ ((n >> 2) & 3); }
 
@@ -830,14 +861,146 @@ template <int N, int S> __device__ __forceinline__ void mx8_wait(Mx8Frag& f) {
   asm volatile("" : "+v"(f.sa[0]), "+v"(f.sa[1]));
 }
 
+// Bytes of a tile's weight scale block in LDS: 256 weight rows of K/32
+// bytes, contiguous in the caller's layout, copied as the aligned dwords
+// that cover them.
+__host__ __device__ constexpr int mx8_block_bytes(int K) { return BN * (K / 32) + 256; }
+
+// Load state of one tile of the MXFP8 kernel: the segment's weight
+// descriptor and this thread's source offsets of step 0 (a step adds
+// s * 128 to the activation offset, s * 64 to the weight offset, s * 4 to
+// the activation scale offset).
+struct Mx8Pipe {
+  __amdgpu_buffer_rsrc_t rw;
+  uint32_t aoff[2], boff[2], soff;
+  uint32_t sc_start;  // first byte of the tile's weight scale block
+  bool a_ok[2], s_ok;
+  int32_t* ids;
+  uint32_t* bias;  // the tile's bias in LDS (gate/up: 128 (gate, up) bf16 pairs; down: 256 bf16)
+  int nk;
+  int seg, c0;
+};
+
+// Weight row (in the segment's matrix) of tile row n.
 template <int MODE>
-__global__ __launch_bounds__(kThreads, 1) void k_mx8_gemm(GemmArgs a) {
+__device__ __forceinline__ int mx8_wrow(const GemmArgs& a, int c0, int n) {
+  if (MODE == MODE_GATEUP) return 2 * min(c0 + (n & (BN / 2 - 1)), a.F - 1) + (n >= BN / 2);
+  return min(c0 + n, a.H - 1);
+}
+
+// Set up tile t: descriptors and the offsets that do not need the tile's
+// assignment ids; the ids themselves go to LDS through buffer->LDS loads of
+// waves 0 and 1 (gate/up takes its activation rows from them in
+// mx8_finish_pipe, once a wait and a barrier have covered those loads).
+template <int MODE>
+__device__ void mx8_make_pipe(const GemmArgs& a, const Tile& t, int K, int32_t* ids, uint32_t* bias, Mx8Pipe& p) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int rows_e = MODE == MODE_GATEUP ? 2 * a.F : a.H;
+  const size_t wbytes = (size_t)rows_e * (K / 2);
+  p.rw = make_rsrc((const uint8_t*)a.w0 + (size_t)t.seg * wbytes, (uint32_t)wbytes);
+  p.ids = ids;
+  p.nk = (K + BK8 - 1) / BK8;
+  p.seg = t.seg;
+  p.c0 = t.c0;
+  p.bias = bias;
+  if (tid < BM) {
+    const __amdgpu_buffer_rsrc_t ri = make_rsrc(a.sorted_assign + t.p0, (uint32_t)t.rows * 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ri, (lds_ptr_t)(ids + (tid & ~(kWave - 1))), 4, (int)(tid * 4), 0, 0, 0);
+  } else if (tid < 2 * BM) {
+    // the tile's bias, 512 bytes from dword-aligned offsets (columns past
+    // the matrix read zeros), so the epilogue has no global load to wait for
+    const size_t e0 = MODE == MODE_GATEUP ? (size_t)t.seg * 2 * a.F + 2 * t.c0 : (size_t)t.seg * a.H + t.c0;
+    const int n = MODE == MODE_GATEUP ? 2 * (a.F - t.c0) : a.H - t.c0;
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.bias ? a.bias + e0 : a.bias, a.bias ? (uint32_t)n * 2 : 0u);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(bias + ((tid - BM) & ~(kWave - 1))), 4,
+                                             (int)((tid - BM) * 4), 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = tid + i * kThreads;
+    const int r = q / 8;
+    p.a_ok[i] = r < t.rows;
+    p.aoff[i] = MODE == MODE_DOWN && r < t.rows ? (uint32_t)((size_t)(t.p0 + r) * K) + (swz_slot(r, q % 8) << 4)
+                                                : kOutOfRange;
+  }
+  {
+    const int r = (tid / kWave) * 16 + (lane & 15);  // lanes 0..15 of each wave: one activation row's scale word
+    p.s_ok = lane < 16 && r < t.rows;
+    p.soff = MODE == MODE_DOWN && p.s_ok ? (uint32_t)((size_t)(t.p0 + r) * a.a8s_stride) : kOutOfRange;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = tid + i * kThreads;
+    const int n = q / 4;
+    p.boff[i] = (uint32_t)((size_t)mx8_wrow<MODE>(a, t.c0, n) * (K / 2)) + (swz_slot4(n, q % 4) << 4);
+  }
+  const int rb0 = MODE == MODE_GATEUP ? 2 * t.c0 : t.c0;
+  p.sc_start = (uint32_t)(((size_t)t.seg * rows_e + rb0) * (K / 32));
+}
+
+template <int MODE>
+__device__ __forceinline__ void mx8_finish_pipe(const GemmArgs& a, int K, Mx8Pipe& p) {
+  if (MODE != MODE_GATEUP) return;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = tid + i * kThreads;
+    const int id = ds_read4_sync(p.ids + q / 8);
+    if (p.a_ok[i]) p.aoff[i] = (uint32_t)((size_t)(id / a.k) * K) + (swz_slot(q / 8, q % 8) << 4);
+  }
+  const int id = ds_read4_sync(p.ids + (tid / kWave) * 16 + (lane & 15));
+  if (p.s_ok) p.soff = (uint32_t)((size_t)(id / a.k) * a.a8s_stride);
+}
+
+__device__ __forceinline__ void mx8_pipe_copy(Mx8Pipe& d, const Mx8Pipe& s) {
+  d.rw = s.rw;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    d.aoff[i] = s.aoff[i];
+    d.boff[i] = s.boff[i];
+    d.a_ok[i] = s.a_ok[i];
+  }
+  d.soff = s.soff;
+  d.sc_start = s.sc_start;
+  d.s_ok = s.s_ok;
+  d.ids = s.ids;
+  d.bias = s.bias;
+  d.nk = s.nk;
+  d.seg = s.seg;
+  d.c0 = s.c0;
+}
+
+// A pipe with no steps and no tile: all its loads read zeros.
+__device__ __forceinline__ void mx8_null_pipe(const Mx8Pipe& like, Mx8Pipe& p) {
+  mx8_pipe_copy(p, like);
+  p.nk = 0;
+  p.s_ok = false;
+  p.soff = kOutOfRange;
+  p.sc_start = kOutOfRange;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    p.a_ok[i] = false;
+    p.aoff[i] = kOutOfRange;
+  }
+}
+
+// One workgroup runs a contiguous share of the tiles, as the bf16 kernel
+// does: the LDS ring runs on across tiles (the last two K steps of a tile
+// issue the first two of the next), the next tile's assignment ids go out
+// when it is set up, and its weight scale block streams into the second
+// block buffer during the current tile, one 256-byte chunk per wave per
+// step.  A launch with fewer than three K steps per tile gives every
+// workgroup one tile and has a single block buffer.
+template <int MODE>
+__global__ __launch_bounds__(kThreads, 1) void k_mx8_gemm(GemmArgs a, int persistent) {
   __shared__ __attribute__((aligned(1024))) uint8_t la[3][BM * 128];
   __shared__ __attribute__((aligned(1024))) uint8_t lb[3][BN * 64];
   __shared__ __attribute__((aligned(16))) uint32_t lsa[3][(kThreads / kWave) * kWave];
-  __shared__ __attribute__((aligned(16))) uint8_t lsb[BN * kMaxScaleRow + 256];
   __shared__ SegTables st;
-  __shared__ int32_t ids_s[BM];
+  __shared__ int32_t ids_s[3][BM];
+  __shared__ uint32_t bias_s[3][BM];
+  __shared__ __attribute__((aligned(16))) uint32_t dump[kWave];  // target of the chunk loads with no block to fill
+  extern __shared__ __attribute__((aligned(16))) uint8_t lsb_dyn[];  // one or two weight scale blocks
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -845,91 +1008,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_mx8_gemm(GemmArgs a) {
   const int wm = wid >> 2, wn = wid & 3;
   const int hh = lane >> 5;
 
-  // one tile per workgroup; each XCD takes a contiguous range of tiles
   const int total_m = __builtin_amdgcn_readfirstlane(build_tables(a.offsets, a.E, st));
   const int total = total_m * a.n_tiles;
   const int per_xcd = (total + 7) / 8;
-  const int slot = blockIdx.x / 8;
-  const int lin = (blockIdx.x % 8) * per_xcd + slot;
-  if (slot >= per_xcd || lin >= total) return;
-  Tile t;
-  if (!tile_at<MODE>(a, st, lin, total_m, t)) return;
-  const int K = t.K;
-  const int nk = (K + BK8 - 1) / BK8;
+  const int nslots = gridDim.x / 8;
+  const int xcd = blockIdx.x % 8;
+  int lin = xcd * per_xcd + blockIdx.x / 8;
+  const int lin_end = min((xcd + 1) * per_xcd, total);
+  Tile tc, tn;
+  if (!next_tile<MODE>(a, st, lin, lin_end, nslots, total_m, tc)) return;
+  const int K = MODE == MODE_GATEUP ? a.H : a.F;
   const int kb = K / 32;  // scale bytes per row
+  const int bbytes = mx8_block_bytes(K);
 
-  // assignment ids of the tile's rows (gate/up: token rows to gather; down:
-  // y rows to write); rows past the segment read as -1
-  if (tid < BM) ids_s[tid] = tid < t.rows ? a.sorted_assign[t.p0 + tid] : -1;
-
-  // the tile's weight scales: rows [rb0, rb0 + BN) of the segment's matrix,
-  // contiguous bytes, copied as aligned dwords
-  const int rows_e = MODE == MODE_GATEUP ? 2 * a.F : a.H;
-  const int rb0 = MODE == MODE_GATEUP ? 2 * t.c0 : t.c0;
-  const uint32_t sc_start = (uint32_t)(((size_t)t.seg * rows_e + rb0) * kb);
-  const int sc_shift = (int)(sc_start & 3u);
-  {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales, (uint32_t)((size_t)a.E * rows_e * kb));
-    const int ndw = (BN * kb + sc_shift + 3) / 4;
-    const int nchunk = (ndw + kWave - 1) / kWave;
-    for (int c = wid; c < nchunk; c += kThreads / kWave)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(lsb + c * 256), 4,
-                                               (int)((sc_start & ~3u) + (uint32_t)(c * 256 + lane * 4)), 0, 0, 0);
-  }
-  __syncthreads();  // ids_s visible
-
-  // per-thread load offsets (step 0); a step adds kt * 128 (A), kt * 64 (B), kt * 4 (scales)
   const int64_t nas = (int64_t)a.T * a.k;
   const size_t arows = MODE == MODE_GATEUP ? (size_t)a.T : (size_t)nas;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.a8, (uint32_t)(arows * K));
   const __amdgpu_buffer_rsrc_t ras = make_rsrc(a.a8s, (uint32_t)(arows * a.a8s_stride));
-  const size_t wbytes = (size_t)rows_e * (K / 2);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc((const uint8_t*)a.w0 + (size_t)t.seg * wbytes, (uint32_t)wbytes);
-  uint32_t aoff[2], boff[2], soff;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int q = tid + i * kThreads;
-    const int r = q / 8;
-    const int id = ids_s[r];
-    uint32_t o = kOutOfRange;
-    if (id >= 0) {
-      const size_t row = MODE == MODE_GATEUP ? (size_t)(id / a.k) : (size_t)(t.p0 + r);
-      o = (uint32_t)(row * K) + (swz_slot(r, q % 8) << 4);
-    }
-    aoff[i] = o;
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int q = tid + i * kThreads;
-    const int n = q / 4;
-    int wr;
-    if (MODE == MODE_GATEUP) {
-      const int f = min(t.c0 + (n & (BN / 2 - 1)), a.F - 1);
-      wr = 2 * f + (n >= BN / 2);
-    } else {
-      wr = min(t.c0 + n, a.H - 1);
-    }
-    boff[i] = (uint32_t)((size_t)wr * (K / 2)) + (swz_slot4(n, q % 4) << 4);
-  }
-  {
-    const int r = wid * 16 + lane;  // lanes 0..15 of each wave: one activation row's scale word
-    const int id = lane < 16 ? ids_s[r] : -1;
-    soff = kOutOfRange;
-    if (id >= 0) {
-      const size_t row = MODE == MODE_GATEUP ? (size_t)(id / a.k) : (size_t)(t.p0 + r);
-      soff = (uint32_t)(row * a.a8s_stride);
-    }
-  }
-  auto issue = [&](int s) {
-    const int sg = s % 3;
-    const bool ok = s < nk;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      dma16(ra, la[sg] + (i * kThreads + wid * kWave) * 16, ok && aoff[i] != kOutOfRange ? aoff[i] + s * BK8 : kOutOfRange);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(rw, lb[sg] + (i * kThreads + wid * kWave) * 16, ok ? boff[i] + s * (BK8 / 2) : kOutOfRange);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, (lds_ptr_t)(lsa[sg] + wid * kWave), 4,
-                                             (int)(ok && soff != kOutOfRange ? soff + s * 4 : kOutOfRange), 0, 0, 0);
+  const int rows_e = MODE == MODE_GATEUP ? 2 * a.F : a.H;
+  // the scale blocks are read as whole dwords from a 4-byte aligned base
+  const uint32_t smis = (uint32_t)((uintptr_t)a.scales & 3u);
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(a.scales - smis, (uint32_t)((smis + (size_t)a.E * rows_e * kb + 3) & ~(size_t)3));
+  const int nchunk = (BN * kb + 3 + 3) / 4 / kWave + 1;  // 256-byte chunks covering a block
+  // chunk c of the block starting at byte sc (relative to the aligned base)
+  auto chunk_off = [&](uint32_t sc, int c) -> uint32_t {
+    return sc == kOutOfRange || c >= nchunk ? kOutOfRange : ((sc + smis) & ~3u) + (uint32_t)(c * 256 + lane * 4);
   };
 
   // fragment rows of this lane
@@ -942,80 +1046,154 @@ __global__ __launch_bounds__(kThreads, 1) void k_mx8_gemm(GemmArgs a) {
     bn[0] = wn * 64 + (lane & 31);
     bn[1] = wn * 64 + 32 + (lane & 31);
   }
-  int bsc[2];  // byte offset of each column row's scales in lsb
+  int li[2];  // row of each column row in the tile's scale block
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int li = MODE == MODE_GATEUP ? (bn[j] < BN / 2 ? 2 * bn[j] : 2 * (bn[j] - BN / 2) + 1) : bn[j];
-    bsc[j] = sc_shift + li * kb;
-  }
+  for (int j = 0; j < 2; ++j)
+    li[j] = MODE == MODE_GATEUP ? (bn[j] < BN / 2 ? 2 * bn[j] : 2 * (bn[j] - BN / 2) + 1) : bn[j];
 
-  f32x16_t acc[2][2];
+  auto issue = [&](const Mx8Pipe& x, int s, int sg) {
+    const bool ok = s < x.nk;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i)
+      dma16(ra, la[sg] + (i * kThreads + wid * kWave) * 16,
+            ok && x.aoff[i] != kOutOfRange ? x.aoff[i] + s * BK8 : kOutOfRange);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    for (int i = 0; i < 2; ++i)
+      dma16(x.rw, lb[sg] + (i * kThreads + wid * kWave) * 16, ok ? x.boff[i] + s * (BK8 / 2) : kOutOfRange);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, (lds_ptr_t)(lsa[sg] + wid * kWave), 4,
+                                             (int)(ok && x.soff != kOutOfRange ? x.soff + s * 4 : kOutOfRange), 0, 0,
+                                             0);
+  };
 
-  issue(0);
-  issue(1);
-  wait_vm<kLoads8>();  // the tile's weight scales and step 0
+  Mx8Pipe pc, pn;
+  int ntile = 0;  // tiles set up so far; tile n's ids and bias live in slot n % 3, its block in buffer n % 2
+  mx8_make_pipe<MODE>(a, tc, K, ids_s[ntile % 3], bias_s[ntile % 3], pc);
+  ++ntile;
+  // the first tile's scale block, whole
+  for (int c = wid; c < nchunk; c += kThreads / kWave)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(lsb_dyn + c * 256), 4, (int)chunk_off(pc.sc_start, c), 0,
+                                             0, 0);
+  wait_vm<0>();
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt) {
+  mx8_finish_pipe<MODE>(a, K, pc);
+  issue(pc, 0, 0);
+  issue(pc, 1, 1);
+  lin += nslots;
+  bool more = persistent && next_tile<MODE>(a, st, lin, lin_end, nslots, total_m, tn);
+  if (more)
+    mx8_make_pipe<MODE>(a, tn, K, ids_s[ntile % 3], bias_s[ntile % 3], pn), ++ntile;
+  else
+    mx8_null_pipe(pc, pn);
+
+  int sg = 0;   // stage of the next step to compute
+  int cur = 0;  // block buffer of the current tile
+  f32x16_t acc[2][2];
+  for (;;) {
+    const uint8_t* lsb = lsb_dyn + cur * bbytes;
+    uint8_t* lsb_next = lsb_dyn + (cur ^ 1) * bbytes;
+    const int shift = (int)((pc.sc_start + smis) & 3u);
+    int bsc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) bsc[j] = shift + li[j] * kb + hh;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // Per step: wait for this thread's loads of step kt (at most the next
+    // step's remain), barrier (all threads' loads landed; everyone finished
+    // step kt - 1, whose stage the next loads reuse), issue step kt + 2 of
+    // this tile or, past its end, of the next, and one chunk of the next
+    // tile's scale block, then compute step kt.  The next tile's ids went
+    // out before this tile's step 2 loads, so the wait and barrier of step
+    // nk - 2 (nk >= 3 in persistent launches) covered them.
+    for (int kt = 0; kt < pc.nk; ++kt) {
       wait_vm<kLoads8>();
       lds_barrier();
-    }
-    issue(kt + 2);
-    const int sg = kt % 3;
-    const uint8_t* A = la[sg];
-    const uint8_t* B = lb[sg];
-    Mx8Frag f;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = ar0 + 32 * i;
-      f.sa[i] = ds_read_b32a(lsa[sg] + (r / 16) * kWave + (r % 16));
-    }
-    // slice 1's reads are in flight during slice 0's MFMAs
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
+      const int s2 = kt + 2;
+      if (s2 == pc.nk) mx8_finish_pipe<MODE>(a, K, pn);
+      const bool uq = s2 >= pc.nk;
+      Mx8Pipe x;
+      x.rw = uq ? pn.rw : pc.rw;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        f.a[s][i][0] = ds_read16(A + swz(ar0 + 32 * i, 4 * s + hh));
-        f.a[s][i][1] = ds_read16(A + swz(ar0 + 32 * i, 4 * s + 2 + hh));
+        x.aoff[i] = uq ? pn.aoff[i] : pc.aoff[i];
+        x.boff[i] = uq ? pn.boff[i] : pc.boff[i];
       }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int p = 2 * s + hh;
-        f.b[s][j] = ds_read16(B + bn[j] * 64 + (swz_slot4(bn[j], p) << 4));
-        f.sb[s][j] = ds_read_u8a(lsb + bsc[j] + 4 * kt + p);
+      x.soff = uq ? pn.soff : pc.soff;
+      x.nk = uq ? pn.nk : pc.nk;
+      issue(x, uq ? s2 - pc.nk : s2, sg == 0 ? 2 : sg - 1);
+      {
+        // chunk c of the next tile's block (a launch with one tile per
+        // workgroup has no second buffer: its chunk loads read zeros into dump)
+        const int c = kt * (kThreads / kWave) + wid;
+        const bool fill = persistent && c < nchunk;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(fill ? (void*)(lsb_next + c * 256) : (void*)dump), 4,
+                                                 (int)(fill ? chunk_off(pn.sc_start, c) : kOutOfRange), 0, 0, 0);
       }
-    }
-    const int nsl = K - kt * BK8 >= BK8 ? 2 : 1;
-    auto slice = [&](int s) {
+
+      const uint8_t* A = la[sg];
+      const uint8_t* B = lb[sg];
+      Mx8Frag f;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const uint32_t* p0 = reinterpret_cast<const uint32_t*>(&f.a[s][i][0]);
-        const uint32_t* p1 = reinterpret_cast<const uint32_t*>(&f.a[s][i][1]);
-        const i32x8_t av = {(int)p0[0], (int)p0[1], (int)p0[2], (int)p0[3],
-                            (int)p1[0], (int)p1[1], (int)p1[2], (int)p1[3]};
-        const int sa = (int)((f.sa[i] >> (8 * (2 * s + hh))) & 0xFFu);
+        const int r = ar0 + 32 * i;
+        f.sa[i] = ds_read_b32a(lsa[sg] + (r / 16) * kWave + (r % 16));
+      }
+      // slice 1's reads are in flight during slice 0's MFMAs
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          f.a[s][i][0] = ds_read16(A + swz(ar0 + 32 * i, 4 * s + hh));
+          f.a[s][i][1] = ds_read16(A + swz(ar0 + 32 * i, 4 * s + 2 + hh));
+        }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const uint32_t* pb = reinterpret_cast<const uint32_t*>(&f.b[s][j]);
-          const i32x8_t bv = {(int)pb[0], (int)pb[1], (int)pb[2], (int)pb[3], 0, 0, 0, 0};
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 0, 4, 0, sa, 0,
-                                                                       (int)f.sb[s][j]);
+          const int p = 2 * s + hh;
+          f.b[s][j] = ds_read16(B + bn[j] * 64 + (swz_slot4(bn[j], p) << 4));
+          f.sb[s][j] = ds_read_u8a(lsb + bsc[j] + 4 * kt + 2 * s);
         }
       }
-    };
-    mx8_wait<8, 0>(f);
-    slice(0);
-    mx8_wait<0, 1>(f);
-    if (nsl == 2) slice(1);
+      const int nsl = K - kt * BK8 >= BK8 ? 2 : 1;
+      auto slice = [&](int s) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint32_t* p0 = reinterpret_cast<const uint32_t*>(&f.a[s][i][0]);
+          const uint32_t* p1 = reinterpret_cast<const uint32_t*>(&f.a[s][i][1]);
+          const i32x8_t av = {(int)p0[0], (int)p0[1], (int)p0[2], (int)p0[3],
+                              (int)p1[0], (int)p1[1], (int)p1[2], (int)p1[3]};
+          const int sa = (int)((f.sa[i] >> (8 * (2 * s + hh))) & 0xFFu);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const uint32_t* pb = reinterpret_cast<const uint32_t*>(&f.b[s][j]);
+            const i32x8_t bv = {(int)pb[0], (int)pb[1], (int)pb[2], (int)pb[3], 0, 0, 0, 0};
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 0, 4, 0, sa, 0,
+                                                                         (int)f.sb[s][j]);
+          }
+        }
+      };
+      mx8_wait<8, 0>(f);
+      slice(0);
+      mx8_wait<0, 1>(f);
+      if (nsl == 2) slice(1);
+      sg = sg == 2 ? 0 : sg + 1;
+    }
+    epilogue<MODE, true>(a, tc, acc, wm, wn, pc.ids, pc.bias);
+    if (!more) break;
+    tile_at<MODE>(a, st, lin, total_m, tc);  // the tile of pn
+    mx8_pipe_copy(pc, pn);
+    cur ^= 1;
+    lin += nslots;
+    more = next_tile<MODE>(a, st, lin, lin_end, nslots, total_m, tn);
+    if (more)
+      mx8_make_pipe<MODE>(a, tn, K, ids_s[ntile % 3], bias_s[ntile % 3], pn), ++ntile;
+    else
+      mx8_null_pipe(pc, pn);
   }
-  wait_vm<0>();  // the zero-reading loads of the steps past the end
-  epilogue<MODE>(a, t, acc, wm, wn, ids_s);
+  wait_vm<0>();  // the zero-reading loads of the steps past the last tile
 }
 
 int row_tiles_bound(const moe_config* c, int32_t T) {
@@ -1050,6 +1228,26 @@ hipError_t launch(const GemmArgs& a, bool mx, int min_k, hipStream_t s) {
     k_grouped_gemm<MODE, true><<<blocks, kThreads, 0, s>>>(a);
   else
     k_grouped_gemm<MODE, false><<<blocks, kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// Static LDS of k_mx8_gemm besides the scale block buffers (the ring, the
+// segment tables, the ids and biases of three tiles, the dump target).
+constexpr int kMx8StaticLds =
+    3 * BM * 128 + 3 * BN * 64 + 3 * kThreads * 4 + (int)sizeof(SegTables) + 2 * 3 * BM * 4 + kWave * 4;
+constexpr int kLdsBytes = 160 * 1024;
+
+// Persistent (two scale block buffers) when a tile has at least three K
+// steps and two blocks fit in LDS; otherwise one tile per workgroup.
+template <int MODE>
+hipError_t launch_mx8(const GemmArgs& a, int K, hipStream_t s) {
+  const int64_t tiles = (int64_t)a.n_tiles * a.m_tiles_max;
+  const int nk = (K + BK8 - 1) / BK8;
+  const bool persistent = nk >= 3 && kMx8StaticLds + 2 * mx8_block_bytes(K) + 1024 <= kLdsBytes;
+  const size_t dyn = (size_t)(persistent ? 2 : 1) * mx8_block_bytes(K);
+  if (kMx8StaticLds + dyn + 1024 > (size_t)kLdsBytes) return hipErrorInvalidValue;
+  const unsigned blocks = (unsigned)grid_size(tiles, persistent);
+  k_mx8_gemm<MODE><<<blocks, kThreads, dyn, s>>>(a, persistent ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -1159,9 +1357,7 @@ hipError_t launch_gateup_mx8(const moe_config* c, const moe_weights* w, const ui
   a.m_tiles_max = row_tiles_bound(c, T);
   a.ksplit = 1;
   a.split_steps = c->hidden / BK;
-  const int64_t tiles = (int64_t)a.n_tiles * a.m_tiles_max;
-  k_mx8_gemm<MODE_GATEUP><<<(unsigned)((tiles + 7) / 8 * 8), kThreads, 0, s>>>(a);
-  return hipGetLastError();
+  return launch_mx8<MODE_GATEUP>(a, c->hidden, s);
 }
 
 hipError_t launch_down_mx8(const moe_config* c, const moe_weights* w, const uint8_t* hq, const uint8_t* hs,
@@ -1182,9 +1378,7 @@ hipError_t launch_down_mx8(const moe_config* c, const moe_weights* w, const uint
   a.m_tiles_max = row_tiles_bound(c, T);
   a.ksplit = 1;
   a.split_steps = c->expert_ff / BK;
-  const int64_t tiles = (int64_t)a.n_tiles * a.m_tiles_max;
-  k_mx8_gemm<MODE_DOWN><<<(unsigned)((tiles + 7) / 8 * 8), kThreads, 0, s>>>(a);
-  return hipGetLastError();
+  return launch_mx8<MODE_DOWN>(a, c->expert_ff, s);
 }
 
 }  // namespace moe
