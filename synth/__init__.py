@@ -289,3 +289,6 @@ def add_block_inputs(c: Case, seed: int = BASE_SEED) -> Case:
 def make_case(name: str, T: int | None = None, **kw) -> Case:
     builder, t_default = CASES[name]
     return builder(t_default if T is None else T, **kw)
+
+
+from . import vecfile  # noqa: E402  (self-describing vector files and the on-disk case cache)

@@ -4,6 +4,7 @@ Output tolerances are normwise, max|gpu - ref| <= tol * max|ref|: 1e-4 for
 fp32 layers, 2e-2 for bf16 weights, 3e-2 for MXFP4 weights.  Routing weights
 and the shared gate: <= 1e-5 relative per element (softmax / sigmoid in
 fp32, "qwen35moe CPU-reference golden vectors", Kernel 4 tolerance)."""
+import os
 import sys
 
 import numpy as np
@@ -27,7 +28,12 @@ _WEIGHTS = {}
 
 def cached_case(name, T, only=None):
     """make_case(name, T), with the weights of each named case generated once
-    per process (they do not depend on T; tokens and drawn logits do)."""
+    per process (they do not depend on T; tokens and drawn logits do).  With
+    MOE_CASE_CACHE set to a directory, cases are also kept there as vector
+    files (synth.vecfile) and read back by later runs."""
+    cache_dir = os.environ.get("MOE_CASE_CACHE")
+    if cache_dir and only is None:
+        return synth.vecfile.cached_case(cache_dir, name, T)
     if only is not None or name == "tiny_fp32":
         return synth.make_case(name, T=T, only=None if only is None else set(only))
     if name not in _WEIGHTS:
