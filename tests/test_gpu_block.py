@@ -40,6 +40,8 @@ BLOCKS = [
     ("gptoss20b_bf16", 64, None, dict(E=8, H=320, F=192, k=2)),           # 8 router waves write 64 rows
     ("qwen35moe_prefill_zipf", 8, None, {}),                              # drawn logits at decode size: RMSNorm launch
     ("tiny_fp32", 100, None, {}),                                         # fp32 rows past 64 tokens
+    ("qwen35moe_decode", 13, None, dict(E=8, H=4096, F=128, Fs=128, k=2)),  # widest rows normalised in the router
+    ("qwen35moe_decode", 6, None, dict(E=8, H=3072, F=128, Fs=128, k=2)),   # 6 pieces per lane
 ]
 
 

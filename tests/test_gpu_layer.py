@@ -41,6 +41,12 @@ LAYERS = [
     ("gptoss20b_bf16", 16, None, dict(E=8, H=320, F=192, k=2, Fs=128)),
     ("gptoss20b_bf16", 400, None, dict(E=4, H=320, F=192, k=2)),             # ~200-row segments, odd K steps
     ("qwen35moe_decode", 700, None, dict(E=4, H=256, F=128, Fs=128, k=2)),   # long segments, shared expert
+    ("qwen35moe_decode", 13, None, dict(E=8, H=4096, F=4096, Fs=4096, k=2)),  # widest rows: 8 pieces per lane
+    ("qwen35moe_decode", 70, 12, dict(E=8, H=4096, F=4096, Fs=4096, k=2)),    # widest rows on the MFMA tiles
+    ("qwen35moe_decode", 9, None, dict(E=8, H=3072, F=3072, Fs=64, k=2)),     # 384 pieces: 6 per lane exactly
+    ("qwen35moe_decode", 5, None, dict(E=8, H=2112, F=64, Fs=64, k=2)),       # 264 pieces: 6 per lane, ragged
+    ("gptoss20b_mxfp4", 13, None, dict(E=4, H=4096, F=4096, k=2)),            # widest MXFP4 rows (burst kernels)
+    ("gptoss20b_mxfp4", 150, 12, dict(E=4, H=4096, F=4096, k=2)),             # MXFP4 MFMA tiles at K = 4096
 ]
 
 

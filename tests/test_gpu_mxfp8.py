@@ -60,6 +60,8 @@ LAYERS = [
     ("gptoss20b_mxfp4", 97, None, dict(E=16, H=512, F=320, k=4)),    # ragged column tiles (F = 2.5 tiles)
     ("gptoss20b_mxfp4", 16, None, {}),                               # gpt-oss decode shape
     ("gptoss20b_mxfp4", 2048, 20, {}),                               # gpt-oss prefill shape, sampled tokens
+    ("gptoss20b_mxfp4", 2000, 64, dict(E=8, H=384, F=2048, k=2)),   # 3 K steps, several tiles per workgroup
+    ("gptoss20b_mxfp4", 300, 16, dict(E=4, H=4096, F=4096, k=2)),   # K = 4096: one tile per workgroup
 ]
 
 

@@ -142,6 +142,34 @@ def test_router_product_keeps_planted_ties(dtype, T):
     assert np.array_equal(idx, ref_idx)
 
 
+@pytest.mark.parametrize("H,T", [(4096, 13), (4096, 64), (3072, 5), (2112, 9)])
+def test_router_product_long_rows(H, T):
+    """Router rows of 264 to 512 16-byte pieces (6 or 8 per lane, whole row in
+    flight, 4 tokens per pass, a ragged last pass): bit-equal rows give
+    bit-equal logits, the logits sit within the fp32 dot bound of the
+    oracle's, the indices are the oracle's on them, and the shared gate
+    (the extra row of the same kernel) is within 1e-5 relative plus the
+    dot's fp32 bound through the sigmoid."""
+    case = synth.make_case("qwen35moe_decode", T=T, E=64, H=H, F=64, Fs=64, k=4, only=set(ROUTE_ONLY))
+    rw = case.t["router_w"]
+    rw[41] = rw[3]
+    rw[63] = rw[3]
+    lg, idx, wt, sg = _route(case, None, with_router=True)
+    assert np.array_equal(lg[:, 3], lg[:, 41]) and np.array_equal(lg[:, 3], lg[:, 63])
+    L = oracle.Layer(case)
+    ref = L.router_logits()
+    xa = np.abs(_f64(case.t["x"], case.x_dtype))
+    wa = np.abs(_f64(rw, case.router_dtype))
+    bound = case.H * 2.0 ** -24 * (xa @ wa.T) + 2.0 ** -24 * np.abs(ref)
+    assert np.all(np.abs(lg.astype(np.float64) - ref) <= bound)
+    ref_idx, ref_w = L.route(lg)
+    assert np.array_equal(idx, ref_idx)
+    assert_rel(wt, ref_w, 1e-5, 1e-30, "routing weights")
+    ref_s = oracle.sigmoid(shared_logit_ref(case))
+    xs = np.abs(_f64(case.t["x"], case.x_dtype)) @ np.abs(_f64(case.t["sh_gate_inp"], case.x_dtype))
+    assert np.all(np.abs(sg.astype(np.float64) - ref_s) <= 1e-5 * np.abs(ref_s) + 0.25 * case.H * 2.0 ** -24 * xs)
+
+
 def test_router_product_split_over_hidden():
     """With scratch, a many-token bf16 router product runs in ranges of the
     hidden dimension summed by the gating kernel in a fixed order: logits
