@@ -206,6 +206,29 @@ def graph_replay_ms(layer, steps, warmup):
     return ms
 
 
+def graph_chain_ms(layer, steps, warmup):
+    """The passes of the whole (batch, weight copy) rotation captured one
+    after the other in a single HIP graph -- as a model's graph holds its
+    consecutive layers -- replayed; time per pass."""
+    import math
+    import torch
+    n = len(layer.weights) * len(layer.xs) // math.gcd(len(layer.weights), len(layer.xs))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for c in range(n):
+            layer.forward(c)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in range(n):
+            layer.forward(c)
+    torch.cuda.synchronize()
+    ms, _ = time_loop(lambda st: g.replay(), max(steps // n, 10), max(warmup // n, 2))
+    return ms / n, n
+
+
 def active_experts(idx_np, E):
     import numpy as np
     return int(np.unique(idx_np.reshape(-1)).size)
@@ -384,6 +407,8 @@ def main():
         log("decode: %.4f ms/step, %.0f tokens/s over %d batches (active experts %s)" % (ms, tok_s, len(xs), actives))
         g_ms = graph_replay_ms(layer, a.steps, a.warmup)
         log("decode, HIP graph replay: %.4f ms/step" % g_ms)
+        gc_ms, gc_n = graph_chain_ms(layer, a.steps, a.warmup)
+        log("decode, %d passes in one HIP graph: %.4f ms/pass" % (gc_n, gc_ms))
         block = None
         if not a.no_block:
             b_ms, _ = time_loop(layer.block, a.steps, a.warmup)
@@ -430,6 +455,10 @@ def main():
                        "per_batch": per_batch},
             "graph_replay": {"ms_per_step": round(g_ms, 5), "tokens_per_s": round(dec.T / (g_ms * 1e-3), 1),
                              "note": "the same moe_forward passes captured once per (batch, weight copy) in HIP graphs"},
+            "graph_chain": {"ms_per_step": round(gc_ms, 5), "tokens_per_s": round(dec.T / (gc_ms * 1e-3), 1),
+                            "passes_per_graph": gc_n,
+                            "note": "the rotation's passes captured one after the other in a single HIP graph, as "
+                                    "a model's graph holds consecutive layers; time per pass"},
             "prenorm_block": block,
             "roofline": roofline,
         }

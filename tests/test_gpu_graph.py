@@ -116,3 +116,50 @@ def test_prenorm_graph_replay(name, T, over):
         torch.cuda.synchronize()
         assert torch.equal(out_g.view(torch.int32), out_e.view(torch.int32)), \
             "replay %d: output differs from the eager pass" % rep
+
+
+@pytest.mark.parametrize("name,T,over", CASES[:2], ids=[_ids(p) for p in CASES[:2]])
+def test_chain_of_passes_in_one_graph(name, T, over):
+    """Four passes captured one after the other in a single graph (each its
+    own input and output, one shared workspace, as consecutive layers would
+    share it), replayed on new inputs with eager passes between the replays:
+    every pass of every replay bit-equal to an eager pass on its input."""
+    log("graph chain: %s T=%d %s" % (name, T, over))
+    case = synth.make_case(name, T=T, **over)
+    cfg = config_of(case)
+    w = device_weights(case)
+    L = 4
+
+    def draw(r):
+        return [synth.make_case(name, T=T, seed=synth.BASE_SEED + 10 * r + i, only={"x"}, **over).t["x"]
+                for i in range(L)]
+
+    x_static = [to_torch(x) for x in draw(0)]
+    outs = [torch.empty((T, case.H), dtype=torch.float32, device="cuda") for _ in range(L)]
+    ws = torch.empty(moe.moe_workspace_bytes(cfg, T), dtype=torch.uint8, device="cuda")
+    out_e = torch.empty_like(outs[0])
+    ws_e = torch.empty_like(ws)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(L):
+            moe.moe_forward(cfg, w, x_static[i], T, outs[i], ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(L):
+            moe.moe_forward(cfg, w, x_static[i], T, outs[i], ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        xs = draw(rep)
+        for i in range(L):
+            x_static[i].copy_(to_torch(xs[i]))
+            outs[i].fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(L):
+            moe.moe_forward(cfg, w, to_torch(xs[i]), T, out_e, ws_e)
+            torch.cuda.synchronize()
+            assert torch.equal(outs[i].view(torch.int32), out_e.view(torch.int32)), \
+                "replay %d, pass %d: output differs from the eager pass" % (rep, i)
