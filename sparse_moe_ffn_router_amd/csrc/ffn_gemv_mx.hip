@@ -3,10 +3,10 @@
 // Routed segments run through the burst kernels (k_gateup_mx_burst,
 // k_down_mx_burst): a wavefront owns 4 row pairs of one segment, 16 lanes
 // per pair, and issues the loads of all its pieces (16 bytes = one
-// 32-element block, with its E8M0 exponent) at once; the workgroup then
-// stages the segment's activation rows in LDS and every piece is decoded
-// to bf16 once, with the scaled fp4 conversion, and multiplied with each
-// staged token.  The shared expert, when a layer has one, keeps bf16
+// 32-element block, with its E8M0 exponent) at once, right after those of
+// the first activation rows the workgroup stages in LDS; every piece is
+// decoded to bf16 once, with the scaled fp4 conversion, and multiplied with
+// each staged token.  The shared expert, when a layer has one, keeps bf16
 // weights and runs through the streaming kernels (k_gateup_gemv_mx,
 // k_down_gemv_mx): 64 row pairs per workgroup, a group of 4 lanes streams
 // one row pair with two 16-byte pieces per row in flight.
@@ -422,9 +422,14 @@ __global__ __launch_bounds__(kThreads) void k_down_gemv_mx(DownArgs a) {
 // Routed MXFP4 segments: burst kernels.  A wavefront owns 4 row pairs of one
 // segment, 16 lanes per pair; a lane issues the loads of all its pieces of
 // both rows at once (pieces l, l + 16, ... of a row; 6 per row at K = 2880,
-// i.e. 11.5 KiB in flight per wavefront), like the bf16 decode kernels, and
-// only then does the workgroup stage the segment's activation rows in LDS
-// (kBStage at a time; the weights stay in registers for every batch).  Each
+// i.e. 11.5 KiB in flight per wavefront), like the bf16 decode kernels.
+// The first kBStage activation rows of the segment (and the rows' biases)
+// are loaded just before the weights, so they arrive while the weights are
+// in flight, and go to LDS once the weight loads are out; later groups of
+// kBStage rows are staged the plain way (the weights stay in registers for
+// every group).  Loaded after the weights, as before, the rows' loads and
+// an early use of the biases waited for every weight load first
+// (gpt-oss MXFP4 T = 16: gate/up 68.3 -> 57.6 us, down 36.8 -> 32.4 us).  Each
 // piece is decoded once and multiplied with every staged token; the (row,
 // token) sums are reduced over the pair's 16 lanes with DPP.  Against the
 // streaming kernels above this keeps about three times the weight bytes in
@@ -530,6 +535,35 @@ __device__ __forceinline__ void stage_rows(uint16_t* xs, int nt, int K, RowOf sr
   }
 }
 
+// The first staged group's rows loaded into registers (before the weights,
+// so their data arrives while the weight loads are still in flight), then
+// written to LDS in stage_rows' layout.  Rows of at most 2 * kBThreads
+// 16-byte chunks (K <= 4096).
+template <typename RowOf>
+__device__ __forceinline__ void pre_stage(uint4 (&xr)[kBStage][2], int nt, int K, RowOf src_row) {
+  const int chunks = K / 8;
+#pragma unroll
+  for (int j = 0; j < kBStage; ++j) {
+    const uint4* src = reinterpret_cast<const uint4*>(src_row(j < nt ? j : 0));
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int g = (int)threadIdx.x + c * kBThreads;
+      xr[j][c] = j < nt && g < chunks ? src[g] : make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+__device__ __forceinline__ void put_stage(uint16_t* xs, const uint4 (&xr)[kBStage][2], int nt, int K) {
+  const int chunks = K / 8;
+  const int P = K / 32;
+#pragma unroll
+  for (int j = 0; j < kBStage; ++j)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int g = (int)threadIdx.x + c * kBThreads;
+      if (j < nt && g < chunks) reinterpret_cast<uint4*>(xs + (size_t)j * K)[(g & 3) * P + (g >> 2)] = xr[j][c];
+    }
+}
+
 // Gate/up of the routed segments (interleaved gate_up rows 2f, 2f + 1, bias
 // and clamped activation).  Grid: (groups of kBPairs features, routed
 // segment slot).
@@ -555,25 +589,33 @@ __global__ __launch_bounds__(kBThreads) void k_gateup_mx_burst(GateUpArgs a) {
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + wrow * P, nrows * (uint32_t)P);
   const uint32_t lr = (uint32_t)(2 * (fr - fw));  // this lane's first row in the wavefront's span
   const uint32_t co[2] = {lr * rb, (lr + 1) * rb}, so[2] = {lr * (uint32_t)P, (lr + 1) * (uint32_t)P};
+  const int p0 = a.offsets[e];
+  const int n = a.offsets[e + 1] - p0;
+  uint4 xr[kBStage][2];
+  pre_stage(xr, min(kBStage, n), a.H, [&](int j) {
+    const int sa = a.sorted_assign[p0 + j];
+    return (const uint16_t*)a.x + (size_t)(sa / a.k) * a.H;
+  });
+  // the (gate, up) bias pair as one word, loaded ahead of the weights and
+  // unpacked after them: a use right after the weight loads would wait for
+  // all of them
+  const size_t row0 = (size_t)e * 2 * a.F + 2 * (size_t)fr;
+  const uint32_t braw = a.gate_up_b ? *reinterpret_cast<const uint32_t*>((const uint16_t*)a.gate_up_b + row0) : 0u;
   uint4 w[2][NPL];
   uint32_t sc[2][NPL];
   burst_load<NPL>(rc, rs, co, so, P, l, w, sc);
-  const size_t row0 = (size_t)e * 2 * a.F + 2 * (size_t)fr;
-  float bg = 0.f, bu = 0.f;
-  if (a.gate_up_b) {
-    bg = xscalar<uint16_t>((const uint16_t*)a.gate_up_b, row0);
-    bu = xscalar<uint16_t>((const uint16_t*)a.gate_up_b, row0 + 1);
-  }
-  const int p0 = a.offsets[e];
-  const int n = a.offsets[e + 1] - p0;
-  const int nas = a.T * a.k;
+  __builtin_amdgcn_sched_barrier(0);
+  const float bg = __uint_as_float(braw << 16), bu = __uint_as_float(braw & 0xFFFF0000u);
+  put_stage(xs, xr, min(kBStage, n), a.H);
   for (int tb = 0; tb < n; tb += kBStage) {
     const int nt = min(kBStage, n - tb);
-    if (tb) __syncthreads();
-    stage_rows(xs, nt, a.H, [&](int j) {
-      const int sa = a.sorted_assign[p0 + tb + j];
-      return (const uint16_t*)a.x + (size_t)(sa / a.k) * a.H;
-    });
+    if (tb) {
+      __syncthreads();
+      stage_rows(xs, nt, a.H, [&](int j) {
+        const int sa = a.sorted_assign[p0 + tb + j];
+        return (const uint16_t*)a.x + (size_t)(sa / a.k) * a.H;
+      });
+    }
     __syncthreads();
     float acc[2][kBStage];
 #pragma unroll
@@ -625,22 +667,30 @@ __global__ __launch_bounds__(kBThreads) void k_down_mx_burst(DownArgs a) {
   const uint32_t lr = (uint32_t)(o0 - ow);
   const uint32_t co[2] = {lr * rb, two ? (lr + 1) * rb : kOutOfRange};
   const uint32_t so[2] = {lr * (uint32_t)P, two ? (lr + 1) * (uint32_t)P : kOutOfRange};
-  uint4 w[2][NPL];
-  uint32_t sc[2][NPL];
-  burst_load<NPL>(rc, rs, co, so, P, l, w, sc);
-  const size_t row0 = (size_t)e * a.H + o0;
-  float b0 = 0.f, b1 = 0.f;
-  if (a.down_b) {
-    b0 = xscalar<uint16_t>((const uint16_t*)a.down_b, row0);
-    if (two) b1 = xscalar<uint16_t>((const uint16_t*)a.down_b, row0 + 1);
-  }
   const int p0 = a.offsets[e];
   const int n = a.offsets[e + 1] - p0;
   const uint16_t* hseg = (const uint16_t*)a.h + (size_t)p0 * a.F;
+  uint4 xr[kBStage][2];
+  pre_stage(xr, min(kBStage, n), a.F, [&](int j) { return hseg + (size_t)j * a.F; });
+  // the pair's two biases as one word (the second half unused when H is
+  // odd and the pair has one row), loaded ahead of the weights and unpacked
+  // after them
+  const size_t row0 = (size_t)e * a.H + o0;
+  const uint32_t braw = a.down_b ? (two ? *reinterpret_cast<const uint32_t*>((const uint16_t*)a.down_b + row0)
+                                        : (uint32_t)((const uint16_t*)a.down_b)[row0])
+                                 : 0u;
+  uint4 w[2][NPL];
+  uint32_t sc[2][NPL];
+  burst_load<NPL>(rc, rs, co, so, P, l, w, sc);
+  __builtin_amdgcn_sched_barrier(0);
+  const float b0 = __uint_as_float(braw << 16), b1 = __uint_as_float(braw & 0xFFFF0000u);
+  put_stage(hs, xr, min(kBStage, n), a.F);
   for (int tb = 0; tb < n; tb += kBStage) {
     const int nt = min(kBStage, n - tb);
-    if (tb) __syncthreads();
-    stage_rows(hs, nt, a.F, [&](int j) { return hseg + (size_t)(tb + j) * a.F; });
+    if (tb) {
+      __syncthreads();
+      stage_rows(hs, nt, a.F, [&](int j) { return hseg + (size_t)(tb + j) * a.F; });
+    }
     __syncthreads();
     float acc[2][kBStage];
 #pragma unroll
