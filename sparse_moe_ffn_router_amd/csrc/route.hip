@@ -64,11 +64,33 @@ __global__ __launch_bounds__(kGateWaves * kWave) void k_gating(
   const int t = blockIdx.x * kGateWaves + threadIdx.x / kWave;
   if (t >= T) return;
   if (nsplit > 1) {
-    for (int e = lane; e < E; e += kWave) {
-      float v = part[(size_t)t * E + e];
-      for (int s = 1; s < nsplit; ++s) v += part[((size_t)s * T + t) * E + e];
-      if (br) v += RouterVec<XT>::scalar(br, e);
-      logits[(size_t)t * E + e] = v;
+    // the ranges' partial sums, added in range order; the loads of up to 8
+    // ranges of 4 chunks of 64 experts go out together
+    constexpr int kC = 4, kU = 8;
+    for (int e0 = 0; e0 < E; e0 += kC * kWave) {
+      float v[kC];
+#pragma unroll
+      for (int c = 0; c < kC; ++c) v[c] = 0.f;
+      for (int s0 = 0; s0 < nsplit; s0 += kU) {
+        float pv[kC][kU];
+#pragma unroll
+        for (int c = 0; c < kC; ++c)
+#pragma unroll
+          for (int u = 0; u < kU; ++u) {
+            const int e = e0 + c * kWave + lane, sp = s0 + u;
+            pv[c][u] = e < E && sp < nsplit ? part[((size_t)sp * T + t) * E + e] : 0.f;
+          }
+#pragma unroll
+        for (int c = 0; c < kC; ++c)
+#pragma unroll
+          for (int u = 0; u < kU; ++u)
+            if (s0 + u < nsplit) v[c] = s0 + u == 0 ? pv[c][u] : v[c] + pv[c][u];
+      }
+#pragma unroll
+      for (int c = 0; c < kC; ++c) {
+        const int e = e0 + c * kWave + lane;
+        if (e < E) logits[(size_t)t * E + e] = br ? v[c] + RouterVec<XT>::scalar(br, e) : v[c];
+      }
     }
   }
   gate_token(logits + (size_t)t * E, E, k, softmax_first, renorm, scale, topk_idx + (size_t)t * k,
