@@ -8,7 +8,10 @@
 // ahead; each 128-byte LDS row holds its eight 16-byte pieces in XOR-swizzled
 // order (piece c of row r at slot c ^ ((r >> 1) & 7)) so MFMA operand reads
 // spread over the banks.  Waves sit 2 (rows) x 4 (columns), each 64 x 64 as 2 x 2
-// v_mfma_f32_32x32x16_bf16 blocks.
+// v_mfma_f32_32x32x16_bf16 blocks.  The MFMAs take the weight rows as their
+// first operand and the activation rows as their second, so a lane ends with
+// one activation row and runs of four consecutive outputs of it, which the
+// epilogue writes as 8-byte (bf16) or 16-byte (fp32) pieces.
 //
 //  gate/up: A = x rows gathered by token; the 256 weight rows are 128 gate
 //           rows and the 128 matching up rows (for the interleaved gpt-oss
@@ -201,6 +204,42 @@ __device__ __forceinline__ int32_t ds_read4_sync(const int32_t* p) {
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"((uint32_t)(uintptr_t)p) : "memory");
   return r;
 }
+// Wait for every vector memory operation of the wave, as an s_waitcnt the
+// compiler's own wait placement knows about (bias words loaded in uniform
+// control flow are then complete before the per-row branches that use them,
+// and are not taken as pending where the tile loop comes round again).
+__device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+// Epilogue staging through LDS (inline asm, like the operand reads): an
+// 8-byte write, and a 16-byte read whose wait is tied to its registers.
+__device__ __forceinline__ void ds_write8(uint32_t addr, uint32_t lo, uint32_t hi) {
+  const uint64_t v = (uint64_t)hi << 32 | lo;
+  asm volatile("ds_write_b64 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ u32x4_t ds_read16u(uint32_t addr) {
+  u32x4_t r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+  return r;
+}
+__device__ __forceinline__ void lds_wait4(u32x4_t (&v)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
+}
+__device__ __forceinline__ int32_t ds_read4(const int32_t* p) {
+  int32_t r;
+  asm volatile("ds_read_b32 %0, %1" : "=v"(r) : "v"((uint32_t)(uintptr_t)p) : "memory");
+  return r;
+}
+// 8- and 16-byte LDS reads (8- / 16-byte aligned), completed likewise.
+__device__ __forceinline__ uint2 ds_read8_sync(const uint32_t* p) {
+  uint2 r;
+  asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"((uint32_t)(uintptr_t)p) : "memory");
+  return r;
+}
+__device__ __forceinline__ uint4 ds_read16_sync(const uint32_t* p) {
+  uint4 r;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"((uint32_t)(uintptr_t)p) : "memory");
+  return r;
+}
 
 struct KFrag {
   bf16x8_t a[2], b[2];
@@ -219,7 +258,7 @@ __device__ __forceinline__ void mfma4(f32x16_t (&acc)[2][2], const KFrag& o) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.a[i], o.b[j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.b[j], o.a[i], acc[i][j], 0, 0, 0);
 }
 
 // One K step: four 16-deep sub-steps, the operand reads of sub-step kk + 1
@@ -242,7 +281,7 @@ __device__ __forceinline__ void pipe_compute(const Frag& f, f32x16_t (&acc)[2][2
 }
 
 __device__ __forceinline__ void mfma1(f32x16_t (&acc)[2][2], const KFrag& o, int i, int j) {
-  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.a[i], o.b[j], acc[i][j], 0, 0, 0);
+  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.b[j], o.a[i], acc[i][j], 0, 0, 0);
 }
 
 // The same K step for bf16 weights, with the six buffer->LDS loads of step s
@@ -337,15 +376,16 @@ __device__ int build_tables(const int32_t* __restrict__ offsets, int nseg, SegTa
   return all;
 }
 
-// Segment holding row tile mt (wave-uniform), from the LDS tables.
 // Segment holding tile lin when each segment's tiles are contiguous in lin
-// (scale = column tiles per row tile).
-__device__ int find_segment(const SegTables& t, int nseg, int lin, int scale) {
+// (scale = column tiles per row tile), searched from segment `from` on (a
+// workgroup's tiles only move forward, so the previous tile's segment is a
+// lower bound): 64 segments per LDS read, no per-lane branches.
+__device__ int find_segment(const SegTables& t, int nseg, int lin, int scale, int from) {
   const int lane = threadIdx.x & (kWave - 1);
-  for (int base = 0; base < nseg; base += kWave) {
-    const int e = base + lane;
-    const bool hit = e < nseg && t.tpre[e] * scale <= lin && lin < t.tpre[e + 1] * scale;
-    const uint64_t m = __ballot(hit);
+  for (int base = from; base < nseg; base += kWave) {
+    const int e = min(base + lane, nseg - 1);
+    const int lo = t.tpre[e] * scale, hi = t.tpre[e + 1] * scale;
+    const uint64_t m = __ballot((base + lane < nseg) & (lo <= lin) & (lin < hi));
     if (m) return base + __ffsll((unsigned long long)m) - 1;
   }
   return -1;
@@ -359,7 +399,7 @@ __device__ int find_segment(const SegTables& t, int nseg, int lin, int scale) {
 // gathered activation rows, follow each other (same XCD, same L2).
 // Router: column tiles (and K ranges) outermost.
 template <int MODE>
-__device__ bool tile_at(const GemmArgs& a, const SegTables& st, int lin, int total_m, Tile& t) {
+__device__ bool tile_at(const GemmArgs& a, const SegTables& st, int lin, int total_m, Tile& t, int from) {
   int nt = lin / total_m;
   const int mt = lin % total_m;  // router row tile
   const int nseg = a.E + a.shared;
@@ -371,7 +411,7 @@ __device__ bool tile_at(const GemmArgs& a, const SegTables& st, int lin, int tot
     t.p0 = mt * BM;
     t.rows = min(BM, a.T - t.p0);
   } else {
-    const int seg = __builtin_amdgcn_readfirstlane(find_segment(st, nseg, lin, a.n_tiles));
+    const int seg = __builtin_amdgcn_readfirstlane(find_segment(st, nseg, lin, a.n_tiles, from));
     const int r0 = __builtin_amdgcn_readfirstlane(st.tpre[seg]);
     const int nr = __builtin_amdgcn_readfirstlane(st.tpre[seg + 1]) - r0;  // row tiles of the segment
     const int local = lin - r0 * a.n_tiles;
@@ -619,98 +659,265 @@ __device__ __forceinline__ void tile_loop(const GemmArgs& a, const Pipe& p, Pipe
 #undef MOE_STEP
 }
 
-// Epilogue.  Lane l of a 32x32 block holds column (l & 31) and rows
-// (q / 4) * 8 + (l / 32) * 4 + (q % 4), q = 0..15.
-template <int MODE, bool BIAS_LDS = false>
-__device__ __forceinline__ void epilogue(const GemmArgs& a, const Tile& t, const f32x16_t (&acc)[2][2], int wm,
-                                         int wn, const int32_t* ids, const uint32_t* bias_lds = nullptr) {
+// Epilogue.  acc[i][j] is the product of weight block j (first MFMA
+// operand) and activation block i (second): lane l holds activation row
+// i * 32 + (l & 31) of the wave's 64 and weight rows
+// (q / 4) * 8 + (l / 32) * 4 + (q % 4), q = 0..15, of block j; group
+// g = q / 4 is a run of four consecutive outputs of that row.  BIAS: 0 none,
+// 1 from LDS (the tile's, staged when the tile was set up), 2 from HBM, all
+// of the lane's bias words requested at once from in-range addresses (a load
+// under a branch would make the compiler wait for every load in flight
+// where the branches meet, on the path without it too).
+//
+// STG (gate/up and down of the bf16 kernel): the results go through the
+// LDS stage that the tile's last K step read, idle until the next tile's
+// step 0 refills it (behind that step's barrier): after a barrier (every
+// wave is done with that step's operand reads), each wave writes its block
+// as bf16 to its own 4 KiB there (16-byte pieces XOR-swizzled by row, so
+// the 8-byte writes of a wave hit every bank equally), reads it back row-
+// major and stores whole 64- (h) or 128-byte (y) row segments — a store
+// instruction then covers 16 or 8 rows instead of 32 partial ones.
+template <int MODE, int BIAS, bool STG>
+__device__ __forceinline__ void epilogue_b(const GemmArgs& a, const Tile& t, const f32x16_t (&acc)[2][2], int wm,
+                                           int wn, const int32_t* ids, const uint32_t* bias_lds, uint8_t* stage,
+                                           int wid) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int colin = lane & 31;
+  const int rl = lane & 31, hq = lane >> 5;
   const int64_t nas = (int64_t)a.T * a.k;
   if (MODE == MODE_GATEUP) {
-    const int f = t.c0 + wn * 32 + colin;
-    if (f < t.Fe) {
-      float bg = 0.f, bu = 0.f;
-      if (BIAS_LDS) {
-        const uint32_t gu = (uint32_t)ds_read4_sync(reinterpret_cast<const int32_t*>(bias_lds) + wn * 32 + colin);
-        bg = __uint_as_float(gu << 16);
-        bu = __uint_as_float(gu & 0xFFFF0000u);
-      } else if (a.oai && !t.sh && a.bias) {
-        bg = __uint_as_float((uint32_t)a.bias[(size_t)t.seg * 2 * a.F + 2 * f] << 16);
-        bu = __uint_as_float((uint32_t)a.bias[(size_t)t.seg * 2 * a.F + 2 * f + 1] << 16);
+    // feature of group g, element e: fb + g * 8 + e; gate and up biases as
+    // one word per feature (gate in the low half, up in the high half)
+    const int fb = t.c0 + wn * 32 + hq * 4;
+    const bool oai = a.oai && !t.sh;
+    uint4 bw[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if (BIAS == 1)
+        bw[g] = ds_read16_sync(bias_lds + wn * 32 + g * 8 + hq * 4);
+      else if (BIAS == 2)
+        bw[g] = *reinterpret_cast<const uint4*>(a.bias + (size_t)t.seg * 2 * a.F + 2 * min(fb + g * 8, t.Fe - 4));
+      else
+        bw[g] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    if (BIAS == 2) vm_wait_all();
+    uint16_t* h = (uint16_t*)a.out;
+    if (STG) {
+      lds_barrier();
+      if (t.c0 + wn * 32 >= t.Fe) return;  // the wave's 32 features lie past a narrower segment
+      const uint32_t R = (uint32_t)(uintptr_t)stage + wid * 4096;  // 64 rows x 64 bytes
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = i * 32 + rl;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t bb[4] = {bw[g].x, bw[g].y, bw[g].z, bw[g].w};
+          uint32_t hv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int q = g * 4 + e;
+            float v;
+            if (oai) {
+              const float gg = fminf(acc[i][0][q] + bf16lo(bb[e]), a.limit);
+              const float u = fminf(fmaxf(acc[i][1][q] + bf16hi(bb[e]), -a.limit), a.limit);
+              v = (u + 1.f) * (gg / (1.f + expf(-a.alpha * gg)));
+            } else {
+              const float gg = acc[i][0][q];
+              v = gg / (1.f + expf(-gg)) * acc[i][1][q];
+            }
+            hv[e] = f32_to_bf16(v);
+          }
+          ds_write8(R + r * 64 + ((g ^ ((r >> 1) & 3)) << 4) + hq * 8, hv[0] | hv[1] << 16, hv[2] | hv[3] << 16);
+        }
       }
-      uint16_t* h = (uint16_t*)a.out;
+      u32x4_t v[4];
+      const int c = lane & 3;
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int r = it * 16 + (lane >> 2);
+        v[it] = ds_read16u(R + r * 64 + ((c ^ ((r >> 1) & 3)) << 4));
+      }
+      lds_wait4(v);
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int r = wm * 64 + it * 16 + (lane >> 2);
+        if (r < t.rows) {
+          const int p = t.p0 + r;
+          uint16_t* hrow = h + (p < nas ? (size_t)p * a.F : (size_t)nas * a.F + (size_t)(p - nas) * a.Fs);
+          *reinterpret_cast<u32x4_t*>(hrow + t.c0 + wn * 32 + c * 8) = v[it];
+        }
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = wm * 64 + i * 32 + rl;
+      if (r < t.rows) {
+        const int p = t.p0 + r;
+        uint16_t* hrow = h + (p < nas ? (size_t)p * a.F : (size_t)nas * a.F + (size_t)(p - nas) * a.Fs);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int f = fb + g * 8;
+          if (f < t.Fe) {
+            const uint32_t bb[4] = {bw[g].x, bw[g].y, bw[g].z, bw[g].w};
+            uint32_t hv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int q = g * 4 + e;
+              float v;
+              if (oai) {
+                const float gg = fminf(acc[i][0][q] + bf16lo(bb[e]), a.limit);
+                const float u = fminf(fmaxf(acc[i][1][q] + bf16hi(bb[e]), -a.limit), a.limit);
+                v = (u + 1.f) * (gg / (1.f + expf(-a.alpha * gg)));
+              } else {
+                const float gg = acc[i][0][q];
+                v = gg / (1.f + expf(-gg)) * acc[i][1][q];
+              }
+              hv[e] = f32_to_bf16(v);
+            }
+            *reinterpret_cast<uint2*>(hrow + f) = make_uint2(hv[0] | hv[1] << 16, hv[2] | hv[3] << 16);
+          }
+        }
+      }
+    }
+  } else {
+    // output column of (j, g, e): ob + j * 32 + g * 8 + e; router rows of a
+    // width that is not a multiple of four are written element by element
+    const int ob = t.c0 + wn * 64 + hq * 4;
+    const bool split = MODE == MODE_ROUTER && a.ksplit > 1;  // partial sums: no bias
+    const bool vec = MODE != MODE_ROUTER || t.ncols % 4 == 0;
+    uint2 bb[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int o = ob + j * 32 + g * 8;
+        if (BIAS == 1)
+          bb[j][g] = ds_read8_sync(bias_lds + (o - t.c0) / 2);
+        else if (BIAS == 2 && vec)
+          bb[j][g] = *reinterpret_cast<const uint2*>(a.bias + (MODE == MODE_DOWN ? (size_t)t.seg * a.H : 0) +
+                                                     min(o, t.ncols - 4));
+        else
+          bb[j][g] = make_uint2(0u, 0u);
+      }
+    if (BIAS == 2) vm_wait_all();
+    if (STG && MODE == MODE_DOWN) {
+      lds_barrier();
+      if (t.c0 + wn * 64 >= t.ncols) return;
+      const uint32_t R = (uint32_t)(uintptr_t)stage + wid * 4096;  // 32 rows x 128 bytes
+      const int c = lane & 7;
+      int32_t id[2][4];  // y rows (assignment ids) of the rows this lane stores
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int r = wm * 64 + i * 32 + (q / 4) * 8 + (lane >> 5) * 4 + (q & 3);
-          if (r < t.rows) {
-            float hv;
-            if (a.oai && !t.sh) {
-              const float g = fminf(acc[i][0][q] + bg, a.limit);
-              const float u = fminf(fmaxf(acc[i][1][q] + bu, -a.limit), a.limit);
-              hv = (u + 1.f) * (g / (1.f + expf(-a.alpha * g)));
-            } else {
-              const float g = acc[i][0][q];
-              hv = g / (1.f + expf(-g)) * acc[i][1][q];
-            }
-            const int p = t.p0 + r;
-            const size_t rowoff = p < nas ? (size_t)p * a.F : (size_t)nas * a.F + (size_t)(p - nas) * a.Fs;
-            h[rowoff + f] = (uint16_t)f32_to_bf16(hv);
+        for (int it = 0; it < 4; ++it) id[i][it] = ds_read4(ids + min(wm * 64 + i * 32 + it * 8 + (lane >> 3), BM - 1));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const uint32_t y0 = f32_to_bf16(acc[i][j][g * 4] + bf16lo(bb[j][g].x));
+            const uint32_t y1 = f32_to_bf16(acc[i][j][g * 4 + 1] + bf16hi(bb[j][g].x));
+            const uint32_t y2 = f32_to_bf16(acc[i][j][g * 4 + 2] + bf16lo(bb[j][g].y));
+            const uint32_t y3 = f32_to_bf16(acc[i][j][g * 4 + 3] + bf16hi(bb[j][g].y));
+            ds_write8(R + rl * 128 + (((j * 4 + g) ^ (rl & 7)) << 4) + hq * 8, y0 | y1 << 16, y2 | y3 << 16);
           }
+        u32x4_t v[4];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int r = it * 8 + (lane >> 3);
+          v[it] = ds_read16u(R + r * 128 + ((c ^ (r & 7)) << 4));
         }
-    }
-  } else {
-    float* lg = (float*)a.out;
-    uint16_t* y = (uint16_t*)a.out;
-    // down: the y row of tile row wm*64 + i*32 + (q/4)*8 + h*4 + (q%4) is
-    // the assignment id that lane (row - wm*64) reads here
-    const int32_t ep_id = MODE == MODE_DOWN ? ds_read4_sync(ids + wm * 64 + lane) : 0;
+        lds_wait4(v);
+        asm volatile("" : "+v"(id[i][0]), "+v"(id[i][1]), "+v"(id[i][2]), "+v"(id[i][3]));
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int o = t.c0 + wn * 64 + j * 32 + colin;
-      if (o < t.ncols) {
-        float bias = 0.f;
-        if (MODE == MODE_ROUTER && a.bias) bias = __uint_as_float((uint32_t)a.bias[o] << 16);
-        if (MODE == MODE_DOWN && BIAS_LDS) {
-          const uint32_t w = (uint32_t)ds_read4_sync(reinterpret_cast<const int32_t*>(bias_lds) + (o - t.c0) / 2);
-          bias = __uint_as_float(((o - t.c0) & 1 ? w >> 16 : w & 0xFFFFu) << 16);
-        } else if (MODE == MODE_DOWN && !t.sh && a.bias) {
-          bias = __uint_as_float((uint32_t)a.bias[(size_t)t.seg * a.H + o] << 16);
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int r = wm * 64 + i * 32 + (q / 4) * 8 + (lane >> 5) * 4 + (q & 3);
-            if (r < t.rows) {
-              if (MODE == MODE_ROUTER && a.ksplit > 1)
-                a.part[((size_t)t.ks * a.T + t.p0 + r) * t.ncols + o] = acc[i][j][q];
-              else if (MODE == MODE_ROUTER)
-                lg[(size_t)(t.p0 + r) * t.ncols + o] = acc[i][j][q] + bias;
-              else {
-                const int src = i * 32 + (q / 4) * 8 + (q & 3);
-                const int id0 = __builtin_amdgcn_readlane(ep_id, src);
-                const int id1 = __builtin_amdgcn_readlane(ep_id, src + 4);
-                const int id = (lane >> 5) ? id1 : id0;
-                y[(size_t)id * t.ncols + o] = (uint16_t)f32_to_bf16(acc[i][j][q] + bias);
-              }
-            }
-          }
+        for (int it = 0; it < 4; ++it)
+          if (wm * 64 + i * 32 + it * 8 + (lane >> 3) < t.rows)
+            *reinterpret_cast<u32x4_t*>((uint16_t*)a.out + (size_t)id[i][it] * t.ncols + t.c0 + wn * 64 + c * 8) =
+                v[it];
       }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = wm * 64 + i * 32 + rl;
+      if (r >= t.rows) continue;
+      size_t row;
+      if (MODE == MODE_DOWN)
+        row = (size_t)ds_read4_sync(ids + r);  // y row = the assignment id
+      else if (split)
+        row = (size_t)t.ks * a.T + t.p0 + r;
+      else
+        row = (size_t)(t.p0 + r);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int o = ob + j * 32 + g * 8;
+          if (o >= t.ncols) continue;
+          const float v[4] = {acc[i][j][g * 4], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]};
+          // + bias (+0 without one), as the few-token kernels do
+          const float v0 = v[0] + bf16lo(bb[j][g].x), v1 = v[1] + bf16hi(bb[j][g].x);
+          const float v2 = v[2] + bf16lo(bb[j][g].y), v3 = v[3] + bf16hi(bb[j][g].y);
+          if (MODE == MODE_DOWN) {
+            *reinterpret_cast<uint2*>((uint16_t*)a.out + row * t.ncols + o) =
+                make_uint2(f32_to_bf16(v0) | f32_to_bf16(v1) << 16, f32_to_bf16(v2) | f32_to_bf16(v3) << 16);
+          } else if (split) {
+            float* dst = a.part + row * t.ncols + o;
+            if (vec)
+              *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+            else
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (o + e < t.ncols) dst[e] = v[e];
+          } else {
+            float* dst = (float*)a.out + row * t.ncols + o;
+            if (vec)
+              *reinterpret_cast<float4*>(dst) = make_float4(v0, v1, v2, v3);
+            else
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (o + e < t.ncols)
+                  dst[e] = v[e] + (BIAS == 2 ? __uint_as_float((uint32_t)a.bias[o + e] << 16) : 0.f);
+          }
+        }
     }
   }
 }
 
+template <int MODE, bool BIAS_LDS = false, bool STG = false>
+__device__ __forceinline__ void epilogue(const GemmArgs& a, const Tile& t, const f32x16_t (&acc)[2][2], int wm,
+                                         int wn, const int32_t* ids, const uint32_t* bias_lds = nullptr,
+                                         uint8_t* stage = nullptr, int wid = 0) {
+  constexpr bool S = STG && MODE != MODE_ROUTER;
+  if (BIAS_LDS) {
+    epilogue_b<MODE, 1, S>(a, t, acc, wm, wn, ids, bias_lds, stage, wid);
+    return;
+  }
+  const bool hb = a.bias && (MODE == MODE_GATEUP   ? a.oai && !t.sh
+                             : MODE == MODE_DOWN ? !t.sh
+                                                 : a.ksplit == 1);
+  if (hb)
+    epilogue_b<MODE, 2, S>(a, t, acc, wm, wn, ids, bias_lds, stage, wid);
+  else
+    epilogue_b<MODE, 0, S>(a, t, acc, wm, wn, ids, bias_lds, stage, wid);
+}
+
 // Next tile of this workgroup's run at or after lin (skipping column tiles
-// past a narrower segment); false when the run is done.
+// past a narrower segment); false when the run is done.  `from` is a
+// segment at or before the tile's (the previous tile's).
 template <int MODE>
 __device__ bool next_tile(const GemmArgs& a, const SegTables& st, int& lin, int lin_end, int step, int total_m,
-                          Tile& t) {
+                          Tile& t, int from) {
   for (; lin < lin_end; lin += step)
-    if (tile_at<MODE>(a, st, lin, total_m, t)) return true;
+    if (tile_at<MODE>(a, st, lin, total_m, t, from)) return true;
   return false;
+}
+
+// Field-by-field copy (a whole-struct copy leaves slices in scratch memory).
+__device__ __forceinline__ void tile_copy(Tile& d, const Tile& s) {
+  d.seg = s.seg, d.p0 = s.p0, d.rows = s.rows, d.c0 = s.c0, d.Fe = s.Fe, d.ncols = s.ncols, d.K = s.K;
+  d.ks = s.ks, d.k0 = s.k0, d.nk = s.nk, d.sh = s.sh;
 }
 
 template <int MODE, bool MX>
@@ -741,7 +948,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
   int lin = xcd * per_xcd + blockIdx.x / 8;
   const int lin_end = min((xcd + 1) * per_xcd, total);
   Tile tc, tn;
-  if (!next_tile<MODE>(a, st, lin, lin_end, nslots, total_m, tc)) return;
+  if (!next_tile<MODE>(a, st, lin, lin_end, nslots, total_m, tc, 0)) return;
 
   Frag fr;
   fr.arow0 = wm * 64 + (lane & 31);
@@ -770,7 +977,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
     pipe_put_codes(cr[0], lds_b0);
   }
   lin += nslots;
-  bool more = next_tile<MODE>(a, st, lin, lin_end, nslots, total_m, tn);
+  bool more = next_tile<MODE>(a, st, lin, lin_end, nslots, total_m, tn, tc.seg);
   if (more)
     make_pipe<MODE, MX>(a, tn, ids_s[ntile++ % 3], pn);
   else
@@ -789,13 +996,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
     else
       tile_loop<MODE, MX>(a, pc, pn, fr, wid, acc, cr[2], cr[0], cr[1], lds_a2, lds_a0, lds_a1, lds_b2, lds_b0,
                           lds_b1);
-    epilogue<MODE>(a, tc, acc, wm, wn, pc.ids);
+    {
+      // the stage the tile's last step read (idle until the next tile's step 0)
+      const int ls = (phase + pc.nk + 2) % 3;
+      epilogue<MODE, false, true>(a, tc, acc, wm, wn, pc.ids, nullptr, ls == 0 ? lds_b0 : ls == 1 ? lds_b1 : lds_b2,
+                                  wid);
+    }
     if (!more) break;
     phase = (phase + pc.nk) % 3;
-    tile_at<MODE>(a, st, lin, total_m, tc);  // the tile of pn
+    tile_copy(tc, tn);  // the tile of pn
     pipe_copy(pc, pn);
     lin += nslots;
-    more = next_tile<MODE>(a, st, lin, lin_end, nslots, total_m, tn);
+    more = next_tile<MODE>(a, st, lin, lin_end, nslots, total_m, tn, tc.seg);
     if (more)
       make_pipe<MODE, MX>(a, tn, ids_s[ntile++ % 3], pn);
     else
@@ -998,7 +1210,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mx8_gemm(GemmArgs a, int persis
   __shared__ __attribute__((aligned(16))) uint32_t lsa[3][(kThreads / kWave) * kWave];
   __shared__ SegTables st;
   __shared__ int32_t ids_s[3][BM];
-  __shared__ uint32_t bias_s[3][BM];
+  __shared__ __attribute__((aligned(16))) uint32_t bias_s[3][BM];
   __shared__ __attribute__((aligned(16))) uint32_t dump[kWave];  // target of the chunk loads with no block to fill
   extern __shared__ __attribute__((aligned(16))) uint8_t lsb_dyn[];  // one or two weight scale blocks
 
@@ -1016,7 +1228,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mx8_gemm(GemmArgs a, int persis
   int lin = xcd * per_xcd + blockIdx.x / 8;
   const int lin_end = min((xcd + 1) * per_xcd, total);
   Tile tc, tn;
-  if (!next_tile<MODE>(a, st, lin, lin_end, nslots, total_m, tc)) return;
+  if (!next_tile<MODE>(a, st, lin, lin_end, nslots, total_m, tc, 0)) return;
   const int K = MODE == MODE_GATEUP ? a.H : a.F;
   const int kb = K / 32;  // scale bytes per row
   const int bbytes = mx8_block_bytes(K);
@@ -1079,7 +1291,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mx8_gemm(GemmArgs a, int persis
   issue(pc, 0, 0);
   issue(pc, 1, 1);
   lin += nslots;
-  bool more = persistent && next_tile<MODE>(a, st, lin, lin_end, nslots, total_m, tn);
+  bool more = persistent && next_tile<MODE>(a, st, lin, lin_end, nslots, total_m, tn, tc.seg);
   if (more)
     mx8_make_pipe<MODE>(a, tn, K, ids_s[ntile % 3], bias_s[ntile % 3], pn), ++ntile;
   else
@@ -1170,8 +1382,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_mx8_gemm(GemmArgs a, int persis
           for (int j = 0; j < 2; ++j) {
             const uint32_t* pb = reinterpret_cast<const uint32_t*>(&f.b[s][j]);
             const i32x8_t bv = {(int)pb[0], (int)pb[1], (int)pb[2], (int)pb[3], 0, 0, 0, 0};
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 0, 4, 0, sa, 0,
-                                                                         (int)f.sb[s][j]);
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][j], 4, 0, 0,
+                                                                         (int)f.sb[s][j], 0, sa);
           }
         }
       };
@@ -1183,11 +1395,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_mx8_gemm(GemmArgs a, int persis
     }
     epilogue<MODE, true>(a, tc, acc, wm, wn, pc.ids, pc.bias);
     if (!more) break;
-    tile_at<MODE>(a, st, lin, total_m, tc);  // the tile of pn
+    tile_copy(tc, tn);  // the tile of pn
     mx8_pipe_copy(pc, pn);
     cur ^= 1;
     lin += nslots;
-    more = next_tile<MODE>(a, st, lin, lin_end, nslots, total_m, tn);
+    more = next_tile<MODE>(a, st, lin, lin_end, nslots, total_m, tn, tc.seg);
     if (more)
       mx8_make_pipe<MODE>(a, tn, K, ids_s[ntile % 3], bias_s[ntile % 3], pn), ++ntile;
     else
