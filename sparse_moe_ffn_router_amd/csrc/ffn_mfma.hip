@@ -108,6 +108,7 @@ struct Pipe {
   uint32_t a_off[kAChunks], b_off[kBChunks], sc_off;
   bool a_ok[kAChunks];      // gate/up: the staged row is a row of the tile
   int32_t* ids;             // the tile's assignment ids in LDS (gate/up, down)
+  uint32_t* bias;           // the tile's bias words in LDS (gate/up, down)
   int k0;                   // first K step of the tile
   bool two_mats, mx;
   int nk;
@@ -450,7 +451,7 @@ __device__ bool tile_at(const GemmArgs& a, const SegTables& st, int lin, int tot
 // gathered by token: the assignment ids are loaded here and turned into
 // offsets by finish_pipe, so the loads can be in flight meanwhile.
 template <int MODE, bool MX>
-__device__ void make_pipe(const GemmArgs& a, const Tile& t, int32_t* ids, Pipe& p) {
+__device__ void make_pipe(const GemmArgs& a, const Tile& t, int32_t* ids, uint32_t* bias, Pipe& p) {
   const int tid = threadIdx.x;
   const int64_t nas = (int64_t)a.T * a.k;
   const bool mx = MX && !t.sh && MODE != MODE_ROUTER;
@@ -482,12 +483,25 @@ __device__ void make_pipe(const GemmArgs& a, const Tile& t, int32_t* ids, Pipe& 
   }
   // The assignment ids of the tile's rows (gate/up: which token each row
   // gathers; down: which y row each row writes) go to LDS through
-  // buffer->LDS loads of waves 0 and 1.  The K loop's waits and barriers
-  // cover them before finish_pipe and the epilogue read them.
+  // buffer->LDS loads of waves 0 and 1, and the tile's 512 bias bytes
+  // (gate/up: a gate | up word per feature; down: the 256 outputs) through
+  // those of waves 2 and 3 — columns past the matrix, a shared-expert tile
+  // or a layer without biases read zeros — so the epilogue has no global
+  // load to wait for (such a wait would also wait for the next tile's first
+  // loads).  The K loop's waits and barriers cover both before finish_pipe
+  // and the epilogue read them.
   p.ids = ids;
+  p.bias = bias;
   if (MODE != MODE_ROUTER && tid < BM) {
     const __amdgpu_buffer_rsrc_t ri = make_rsrc(a.sorted_assign + t.p0, (uint32_t)t.rows * 4);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ri, (lds_ptr_t)(ids + (tid & ~(kWave - 1))), 4, (int)(tid * 4), 0, 0, 0);
+  } else if (MODE != MODE_ROUTER && tid < 2 * BM && a.bias) {
+    const bool hb = !t.sh && (MODE == MODE_DOWN || a.oai);
+    const size_t e0 = MODE == MODE_GATEUP ? (size_t)t.seg * 2 * a.F + 2 * t.c0 : (size_t)t.seg * a.H + t.c0;
+    const int n = MODE == MODE_GATEUP ? 2 * (a.F - t.c0) : a.H - t.c0;
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(hb ? a.bias + e0 : a.bias, hb ? (uint32_t)n * 2 : 0u);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(bias + ((tid - BM) & ~(kWave - 1))), 4,
+                                             (int)((tid - BM) * 4), 0, 0, 0);
   }
   auto wrow = [&](int r) -> int {  // row of the segment's weight matrix for tile row r
     if (MODE == MODE_GATEUP) {
@@ -590,6 +604,7 @@ __device__ __forceinline__ void pipe_copy(Pipe& d, const Pipe& s) {
   for (int i = 0; i < kBChunks; ++i) d.b_off[i] = s.b_off[i];
   d.sc_off = s.sc_off;
   d.ids = s.ids;
+  d.bias = s.bias;
   d.k0 = s.k0;
   d.two_mats = s.two_mats;
   d.mx = s.mx;
@@ -946,6 +961,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_b0[BN * 128], lds_b1[BN * 128], lds_b2[BN * 128];
   __shared__ SegTables st;
   __shared__ int32_t ids_s[3][BM];  // assignment ids of three consecutive tiles
+  __shared__ __attribute__((aligned(16))) uint32_t bias_s[3][BM];  // and their bias words
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -983,7 +999,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
 
   Pipe pc, pn;
   int ntile = 0;  // tiles made so far; tile n's ids live in ids_s[n % 3]
-  make_pipe<MODE, MX>(a, tc, ids_s[ntile++ % 3], pc);
+  make_pipe<MODE, MX>(a, tc, ids_s[ntile % 3], bias_s[ntile % 3], pc);
+  ++ntile;
   wait_vm<0>();
   __syncthreads();
   finish_pipe<MODE>(a, pc);
@@ -998,10 +1015,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
   }
   lin += nslots;
   bool more = next_tile<MODE>(a, st, lin, lin_end, nslots, total_m, tn, tc.seg);
-  if (more)
-    make_pipe<MODE, MX>(a, tn, ids_s[ntile++ % 3], pn);
-  else
+  if (more) {
+    make_pipe<MODE, MX>(a, tn, ids_s[ntile % 3], bias_s[ntile % 3], pn);
+    ++ntile;
+  } else {
     null_pipe(pc, pn);
+  }
 
   int phase = 0;  // stage of the current tile's step 0
   f32x16_t acc[2][2];
@@ -1019,8 +1038,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
     {
       // the stage the tile's last step read (idle until the next tile's step 0)
       const int ls = (phase + pc.nk + 2) % 3;
-      epilogue<MODE, false, true>(a, tc, acc, wm, wn, pc.ids, nullptr, ls == 0 ? lds_b0 : ls == 1 ? lds_b1 : lds_b2,
-                                  wid);
+      uint8_t* const stage = ls == 0 ? lds_b0 : ls == 1 ? lds_b1 : lds_b2;
+      if (MODE != MODE_ROUTER && a.bias)
+        epilogue<MODE, true, true>(a, tc, acc, wm, wn, pc.ids, pc.bias, stage, wid);
+      else
+        epilogue<MODE, false, true>(a, tc, acc, wm, wn, pc.ids, nullptr, stage, wid);
     }
     if (!more) break;
     phase = (phase + pc.nk) % 3;
@@ -1028,10 +1050,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
     pipe_copy(pc, pn);
     lin += nslots;
     more = next_tile<MODE>(a, st, lin, lin_end, nslots, total_m, tn, tc.seg);
-    if (more)
-      make_pipe<MODE, MX>(a, tn, ids_s[ntile++ % 3], pn);
-    else
+    if (more) {
+      make_pipe<MODE, MX>(a, tn, ids_s[ntile % 3], bias_s[ntile % 3], pn);
+      ++ntile;
+    } else {
       null_pipe(pc, pn);
+    }
   }
   wait_vm<0>();  // the zero-reading loads of the steps past the last tile
 }
