@@ -704,18 +704,17 @@ __device__ __forceinline__ void tile_loop(const GemmArgs& a, const Pipe& p, Pipe
 // under a branch would make the compiler wait for every load in flight
 // where the branches meet, on the path without it too).
 //
-// STG (gate/up and down of the bf16 kernel): the results go through the
-// LDS stage that the tile's last K step read, idle until the next tile's
-// step 0 refills it (behind that step's barrier): after a barrier (every
-// wave is done with that step's operand reads), each wave writes its block
-// as bf16 to its own 4 KiB there (16-byte pieces XOR-swizzled by row, so
+// STG (gate/up and down): the results go through the LDS stage that the
+// tile's last K step read, idle until the next tile's step 2 loads refill it
+// (behind the next tile's first barrier): after a barrier (every wave is
+// done with that step's operand reads), each wave writes its block as bf16
+// to its own 4 KiB there (`stage`: 16-byte pieces XOR-swizzled by row, so
 // the 8-byte writes of a wave hit every bank equally), reads it back row-
 // major and stores whole 64- (h) or 128-byte (y) row segments — a store
 // instruction then covers 16 or 8 rows instead of 32 partial ones.
 template <int MODE, int BIAS, bool STG>
 __device__ __forceinline__ void epilogue_b(const GemmArgs& a, const Tile& t, const f32x16_t (&acc)[2][2], int wm,
-                                           int wn, const int32_t* ids, const uint32_t* bias_lds, uint8_t* stage,
-                                           int wid) {
+                                           int wn, const int32_t* ids, const uint32_t* bias_lds, uint8_t* stage) {
   const int lane = threadIdx.x & (kWave - 1);
   const int rl = lane & 31, hq = lane >> 5;
   const int64_t nas = (int64_t)a.T * a.k;
@@ -739,7 +738,7 @@ __device__ __forceinline__ void epilogue_b(const GemmArgs& a, const Tile& t, con
     if (STG) {
       lds_barrier();
       if (t.c0 + wn * 32 >= t.Fe) return;  // the wave's 32 features lie past a narrower segment
-      const uint32_t R = (uint32_t)(uintptr_t)stage + wid * 4096;  // 64 rows x 64 bytes
+      const uint32_t R = (uint32_t)(uintptr_t)stage;  // 64 rows x 64 bytes
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int r = i * 32 + rl;
@@ -838,7 +837,7 @@ __device__ __forceinline__ void epilogue_b(const GemmArgs& a, const Tile& t, con
     if (STG && MODE == MODE_DOWN) {
       lds_barrier();
       if (t.c0 + wn * 64 >= t.ncols) return;
-      const uint32_t R = (uint32_t)(uintptr_t)stage + wid * 4096;  // 32 rows x 128 bytes
+      const uint32_t R = (uint32_t)(uintptr_t)stage;  // 32 rows x 128 bytes
       const int c = lane & 7;
       int32_t id[2][4];  // y rows (assignment ids) of the rows this lane stores
 #pragma unroll
@@ -923,19 +922,19 @@ __device__ __forceinline__ void epilogue_b(const GemmArgs& a, const Tile& t, con
 template <int MODE, bool BIAS_LDS = false, bool STG = false>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, const Tile& t, const f32x16_t (&acc)[2][2], int wm,
                                          int wn, const int32_t* ids, const uint32_t* bias_lds = nullptr,
-                                         uint8_t* stage = nullptr, int wid = 0) {
+                                         uint8_t* stage = nullptr) {
   constexpr bool S = STG && MODE != MODE_ROUTER;
   if (BIAS_LDS) {
-    epilogue_b<MODE, 1, S>(a, t, acc, wm, wn, ids, bias_lds, stage, wid);
+    epilogue_b<MODE, 1, S>(a, t, acc, wm, wn, ids, bias_lds, stage);
     return;
   }
   const bool hb = a.bias && (MODE == MODE_GATEUP   ? a.oai && !t.sh
                              : MODE == MODE_DOWN ? !t.sh
                                                  : a.ksplit == 1);
   if (hb)
-    epilogue_b<MODE, 2, S>(a, t, acc, wm, wn, ids, bias_lds, stage, wid);
+    epilogue_b<MODE, 2, S>(a, t, acc, wm, wn, ids, bias_lds, stage);
   else
-    epilogue_b<MODE, 0, S>(a, t, acc, wm, wn, ids, bias_lds, stage, wid);
+    epilogue_b<MODE, 0, S>(a, t, acc, wm, wn, ids, bias_lds, stage);
 }
 
 // Next tile of this workgroup's run at or after lin (skipping column tiles
@@ -1038,11 +1037,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmArgs a) {
     {
       // the stage the tile's last step read (idle until the next tile's step 0)
       const int ls = (phase + pc.nk + 2) % 3;
-      uint8_t* const stage = ls == 0 ? lds_b0 : ls == 1 ? lds_b1 : lds_b2;
+      uint8_t* const stage = (ls == 0 ? lds_b0 : ls == 1 ? lds_b1 : lds_b2) + wid * 4096;  // this wave's 4 KiB
       if (MODE != MODE_ROUTER && a.bias)
-        epilogue<MODE, true, true>(a, tc, acc, wm, wn, pc.ids, pc.bias, stage, wid);
+        epilogue<MODE, true, true>(a, tc, acc, wm, wn, pc.ids, pc.bias, stage);
       else
-        epilogue<MODE, false, true>(a, tc, acc, wm, wn, pc.ids, nullptr, stage, wid);
+        epilogue<MODE, false, true>(a, tc, acc, wm, wn, pc.ids, nullptr, stage);
     }
     if (!more) break;
     phase = (phase + pc.nk) % 3;
@@ -1437,7 +1436,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_mx8_gemm(GemmArgs a, int persis
       if (nsl == 2) slice(1);
       sg = sg == 2 ? 0 : sg + 1;
     }
-    epilogue<MODE, true>(a, tc, acc, wm, wn, pc.ids, pc.bias);
+    {
+      // the stage the tile's last step read (two 16 KiB halves: waves 0-3
+      // take the activation half, 4-7 the weight half)
+      const int ls = sg == 0 ? 2 : sg - 1;
+      uint8_t* const stage = (wid < 4 ? la[ls] : lb[ls]) + (wid & 3) * 4096;
+      epilogue<MODE, true, true>(a, tc, acc, wm, wn, pc.ids, pc.bias, stage);
+    }
     if (!more) break;
     tile_copy(tc, tn);  // the tile of pn
     mx8_pipe_copy(pc, pn);
