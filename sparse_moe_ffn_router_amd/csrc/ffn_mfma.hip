@@ -691,6 +691,9 @@ __device__ __forceinline__ void tile_loop(const GemmArgs& a, const Pipe& p, Pipe
     if (kt + 1 < p.nk) MOE_STEP(kt + 1, a1, b1, a0, b0, a2, b2, c0, c2)
     if (kt + 2 < p.nk) MOE_STEP(kt + 2, a2, b2, a1, b1, a0, b0, c1, c0)
   }
+  // (a tile has at least one step, whose reads complete kn; this wait only
+  // spells that out for the compiler, whose register reuse sees no load)
+  if (!MX) lds_wait<0>(kn);
 #undef MOE_STEP
 }
 
