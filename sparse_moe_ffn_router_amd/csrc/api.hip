@@ -62,6 +62,8 @@ int make_plan(const moe_config* c, int32_t T, Plan* p) {
   p->off_offsets = o; o += up256((size_t)(p->nseg + 1) * 4);
   p->off_sorted = o; o += up256((size_t)p->n_rows * 4);
   p->off_pos = o; o += up256((size_t)p->n_rows * 4);
+  p->nslots = can_fuse_gate_permute(T) ? gemv_slots(c, T) : 0;
+  p->off_segtab = o; o += up256((size_t)p->nslots * 16);
   p->off_perm = o; o += p->perm_bytes;
   p->off_h = o; o += up256((size_t)(p->n_assign * c->expert_ff + (p->shared ? (int64_t)T * c->shared_ff : 0)) * p->elem_x);
   p->off_y = o; o += p->y_bytes;
@@ -183,8 +185,11 @@ static int forward_steps(const moe_config* cfg, const moe_weights* w, const Plan
     e = launch_router_logits(cfg, w, x, T, lg, sg, stream, part);
   }
   if (e != hipSuccess) return MOE_EHIP;
+  int32_t* segtab = nullptr;
   if (can_fuse_gate_permute(T)) {
-    if ((e = launch_gate_permute(cfg, lg, sg, T, idx, wt, sg, offsets, sorted, pos, stream)) != hipSuccess)
+    if (p.nslots) segtab = (int32_t*)(b + p.off_segtab);
+    if ((e = launch_gate_permute(cfg, lg, sg, T, idx, wt, sg, offsets, sorted, pos, stream, segtab, p.nslots)) !=
+        hipSuccess)
       return MOE_EHIP;
   } else {
     if ((e = launch_gating(cfg, w, x, lg, sg, T, idx, wt, sg, stream, part, part ? p.nsplit : 1)) != hipSuccess)
@@ -195,8 +200,8 @@ static int forward_steps(const moe_config* cfg, const moe_weights* w, const Plan
     if ((e = expert_ffn_aq(cfg, w, p, x, offsets, sorted, T, h, b + p.off_aqx, stream)) != hipSuccess) return MOE_EHIP;
     if ((e = down_aq(cfg, w, p, h, offsets, sorted, T, y, b + p.off_aqh, stream)) != hipSuccess) return MOE_EHIP;
   } else {
-    if ((e = launch_expert_ffn(cfg, w, x, offsets, sorted, T, h, stream)) != hipSuccess) return MOE_EHIP;
-    if ((e = launch_down(cfg, w, h, offsets, sorted, T, y, stream)) != hipSuccess) return MOE_EHIP;
+    if ((e = launch_expert_ffn(cfg, w, x, offsets, sorted, T, h, stream, segtab)) != hipSuccess) return MOE_EHIP;
+    if ((e = launch_down(cfg, w, h, offsets, sorted, T, y, stream, segtab)) != hipSuccess) return MOE_EHIP;
   }
   return hip_status(launch_combine_gather(cfg, y, wt, sg, T, out, stream, pn ? pn->resid : nullptr));
 }

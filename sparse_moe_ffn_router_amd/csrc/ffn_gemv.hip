@@ -107,8 +107,17 @@ __device__ Seg find_segment(const int32_t* __restrict__ off, int nseg, int s) {
 // with the most tokens, hence the longest compute), so it starts first and
 // does not trail at the end; slot s > 0 is the (s-1)-th non-empty routed
 // segment (the s-th without a shared expert).
-__device__ __forceinline__ Seg block_segment(const int32_t* off, int E, int shared) {
+// With segtab (the permutation's slot table) the segment is one scalar load
+// that never queues behind other workgroups' weight loads; without it, a
+// search of the offsets.
+__device__ __forceinline__ Seg block_segment(const int32_t* off, int E, int shared,
+                                             const int32_t* __restrict__ segtab) {
   const int slot = blockIdx.y;
+  if (segtab) {
+    const int4 v = reinterpret_cast<const int4*>(segtab)[slot];
+    return Seg{__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
+               __builtin_amdgcn_readfirstlane(v.z)};
+  }
   Seg s;
   if (shared && slot == 0) {
     const int p0 = off[E];
@@ -159,6 +168,7 @@ struct GateUpArgs {
   const int32_t* offsets;
   const int32_t* sorted_assign;
   void* h;
+  const int32_t* segtab;    // the permutation's slot table, or NULL
   int32_t T, k, H, E, F, Fs, shared, oai;
   float alpha, limit;
 };
@@ -169,12 +179,13 @@ struct GateUpArgs {
 // sorted_assign is passed on its own, read-only and unaliased, so the
 // uniform reads of it are scalar loads that never wait behind weight loads.
 template <typename XT, int WK, int NP>
-__global__ __launch_bounds__(kWaves * kWave) void k_gateup_gemv(GateUpArgs a, const int32_t* __restrict__ sorted) {
+__global__ __launch_bounds__(kWaves * kWave) void k_gateup_gemv(GateUpArgs a, const int32_t* __restrict__ sorted,
+                                                                const int32_t* __restrict__ segtab) {
   constexpr int RPW = gateup_rows_per_wave(NP);
   constexpr int XQ = Wp<WK>::kXq;
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const Seg sg = block_segment(a.offsets, a.E, a.shared);
+  const Seg sg = block_segment(a.offsets, a.E, a.shared, segtab);
   if (sg.e < 0) return;
   const bool sh = sg.e == a.E;
   const int Fe = sh ? a.Fs : a.F;
@@ -296,6 +307,7 @@ struct DownArgs {
   const int32_t* offsets;
   const int32_t* sorted_assign;
   float* y;                 // [T*k (+T)][H], row = assignment id
+  const int32_t* segtab;    // the permutation's slot table, or NULL
   int32_t T, k, H, E, F, Fs, shared;
 };
 
@@ -303,12 +315,13 @@ struct DownArgs {
 // segment, written at the row of its assignment id a.  Grid: (groups of
 // kWaves * RPW output rows, segment slot).
 template <typename XT, int WK, int NP>
-__global__ __launch_bounds__(kWaves * kWave) void k_down_gemv(DownArgs a, const int32_t* __restrict__ sorted) {
+__global__ __launch_bounds__(kWaves * kWave) void k_down_gemv(DownArgs a, const int32_t* __restrict__ sorted,
+                                                              const int32_t* __restrict__ segtab) {
   constexpr int RPW = rows_per_wave(NP);
   constexpr int XQ = Wp<WK>::kXq;
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const Seg sg = block_segment(a.offsets, a.E, a.shared);
+  const Seg sg = block_segment(a.offsets, a.E, a.shared, segtab);
   if (sg.e < 0) return;
   const bool sh = sg.e == a.E;
   const int Fe = sh ? a.Fs : a.F;
@@ -479,9 +492,10 @@ hipError_t launch_down_mfma(const moe_config* c, const moe_weights* w, const voi
 bool mfma_shapes_ok(const moe_config* c);
 // Defined in ffn_gemv_mx.hip (MXFP4 experts).
 hipError_t launch_expert_ffn_mx(const moe_config* c, const moe_weights* w, const void* x, const int32_t* offsets,
-                                const int32_t* sorted_assign, int32_t T, void* h, hipStream_t s);
+                                const int32_t* sorted_assign, int32_t T, void* h, hipStream_t s,
+                                const int32_t* segtab);
 hipError_t launch_down_mx(const moe_config* c, const moe_weights* w, const void* h, const int32_t* offsets,
-                          const int32_t* sorted_assign, int32_t T, float* y, hipStream_t s);
+                          const int32_t* sorted_assign, int32_t T, float* y, hipStream_t s, const int32_t* segtab);
 
 static int max_routed_segments(const moe_config* c, int32_t T) {
   const int64_t nk = (int64_t)T * c->top_k;
@@ -498,10 +512,10 @@ static size_t row_bytes_of(int wdt, int cols) {
 }
 
 template <typename XT, int WK, int NP> static void gateup_launch(dim3 g, const GateUpArgs& a, hipStream_t s) {
-  k_gateup_gemv<XT, WK, NP><<<g, kWaves * kWave, 0, s>>>(a, a.sorted_assign);
+  k_gateup_gemv<XT, WK, NP><<<g, kWaves * kWave, 0, s>>>(a, a.sorted_assign, a.segtab);
 }
 template <typename XT, int WK, int NP> static void down_launch(dim3 g, const DownArgs& a, hipStream_t s) {
-  k_down_gemv<XT, WK, NP><<<g, kWaves * kWave, 0, s>>>(a, a.sorted_assign);
+  k_down_gemv<XT, WK, NP><<<g, kWaves * kWave, 0, s>>>(a, a.sorted_assign, a.segtab);
 }
 
 #define MOE_NP_SWITCH(FN, XT, WK, np, grid, args, s) \
@@ -537,11 +551,14 @@ static void down_dispatch(const moe_config* c, const DownArgs& a, int wdt, int n
 }
 #undef MOE_NP_SWITCH
 
+int gemv_slots(const moe_config* c, int32_t T) { return max_routed_segments(c, T) + (c->shared_ff > 0); }
+
 hipError_t launch_expert_ffn(const moe_config* c, const moe_weights* w, const void* x, const int32_t* offsets,
-                             const int32_t* sorted_assign, int32_t T, void* h, hipStream_t s) {
+                             const int32_t* sorted_assign, int32_t T, void* h, hipStream_t s,
+                             const int32_t* segtab) {
   if (T == 0) return hipSuccess;
   if (T > kGemvMaxT && mfma_shapes_ok(c)) return launch_gateup_mfma(c, w, x, offsets, sorted_assign, T, h, s);
-  if (c->w_dtype == MOE_DTYPE_MXFP4) return launch_expert_ffn_mx(c, w, x, offsets, sorted_assign, T, h, s);
+  if (c->w_dtype == MOE_DTYPE_MXFP4) return launch_expert_ffn_mx(c, w, x, offsets, sorted_assign, T, h, s, segtab);
   GateUpArgs a;
   const bool oai = c->act == MOE_ACT_SWIGLU_OAI;
   a.x = x;
@@ -553,21 +570,22 @@ hipError_t launch_expert_ffn(const moe_config* c, const moe_weights* w, const vo
   a.offsets = offsets;
   a.sorted_assign = sorted_assign;
   a.h = h;
+  a.segtab = segtab;
   a.T = T; a.k = c->top_k; a.H = c->hidden; a.E = c->n_expert; a.F = c->expert_ff; a.Fs = c->shared_ff;
   a.shared = c->shared_ff > 0; a.oai = oai; a.alpha = c->act_alpha; a.limit = c->act_limit;
   const int fmax = c->expert_ff > c->shared_ff ? c->expert_ff : c->shared_ff;
-  gateup_dispatch(c, a, c->w_dtype, max_routed_segments(c, T) + a.shared, fmax, s);
+  gateup_dispatch(c, a, c->w_dtype, gemv_slots(c, T), fmax, s);
   return hipGetLastError();
 }
 
 bool y_is_bf16(const moe_config* c, int32_t T) { return T > kGemvMaxT && mfma_shapes_ok(c); }
 
 hipError_t launch_down(const moe_config* c, const moe_weights* w, const void* h, const int32_t* offsets,
-                       const int32_t* sorted_assign, int32_t T, void* yv, hipStream_t s) {
+                       const int32_t* sorted_assign, int32_t T, void* yv, hipStream_t s, const int32_t* segtab) {
   if (T == 0) return hipSuccess;
   if (y_is_bf16(c, T)) return launch_down_mfma(c, w, h, offsets, sorted_assign, T, (uint16_t*)yv, s);
   float* y = (float*)yv;
-  if (c->w_dtype == MOE_DTYPE_MXFP4) return launch_down_mx(c, w, h, offsets, sorted_assign, T, y, s);
+  if (c->w_dtype == MOE_DTYPE_MXFP4) return launch_down_mx(c, w, h, offsets, sorted_assign, T, y, s, segtab);
   DownArgs a;
   a.h = h;
   a.down_w = w->down_w;
@@ -576,11 +594,12 @@ hipError_t launch_down(const moe_config* c, const moe_weights* w, const void* h,
   a.offsets = offsets;
   a.sorted_assign = sorted_assign;
   a.y = y;
+  a.segtab = segtab;
   a.T = T; a.k = c->top_k; a.H = c->hidden; a.E = c->n_expert; a.F = c->expert_ff; a.Fs = c->shared_ff;
   a.shared = c->shared_ff > 0;
   // one piece count for both: the wider of the routed and shared rows
   const int cols = c->expert_ff >= c->shared_ff ? c->expert_ff : c->shared_ff;
-  down_dispatch(c, a, c->w_dtype, max_routed_segments(c, T) + a.shared, cols, s);
+  down_dispatch(c, a, c->w_dtype, gemv_slots(c, T), cols, s);
   return hipGetLastError();
 }
 

@@ -440,9 +440,24 @@ constexpr int kBLanes = 16;                   // lanes per row pair
 constexpr int kBPairs = kBThreads / kBLanes;  // row pairs per workgroup
 constexpr int kBStage = 2;                    // tokens staged per pass (126 VGPRs, 4 waves per SIMD; 4 tokens: 164, 3 waves, 6% slower)
 
-// The s-th non-empty routed segment (blockIdx.y), or -1.
-__device__ __forceinline__ int routed_segment(const int32_t* __restrict__ offsets, int E) {
-  return __builtin_amdgcn_readfirstlane(find_segment(offsets, E, blockIdx.y));
+// The s-th non-empty routed segment (s = blockIdx.y): expert (-1: none),
+// first sorted position and rows.  With segtab (the permutation's slot
+// table, the routed segments after the shared expert's slot) one scalar
+// load; without, a search of the offsets and the segment's bounds.
+struct BSeg {
+  int e, p0, n;
+};
+__device__ __forceinline__ BSeg routed_segment(const int32_t* __restrict__ offsets, int E, int shared,
+                                               const int32_t* __restrict__ segtab) {
+  if (segtab) {
+    const int4 v = reinterpret_cast<const int4*>(segtab)[shared + (int)blockIdx.y];
+    return BSeg{__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
+                __builtin_amdgcn_readfirstlane(v.z)};
+  }
+  const int e = __builtin_amdgcn_readfirstlane(find_segment(offsets, E, blockIdx.y));
+  if (e < 0) return BSeg{-1, 0, 0};
+  const int p0 = offsets[e];
+  return BSeg{e, p0, offsets[e + 1] - p0};
 }
 
 // Both rows' pieces of this lane (codes and E8M0 exponents).  The buffer
@@ -568,10 +583,11 @@ __device__ __forceinline__ void put_stage(uint16_t* xs, const uint4 (&xr)[kBStag
 // and clamped activation).  Grid: (groups of kBPairs features, routed
 // segment slot).
 template <int NPL>
-__global__ __launch_bounds__(kBThreads) void k_gateup_mx_burst(GateUpArgs a) {
+__global__ __launch_bounds__(kBThreads) void k_gateup_mx_burst(GateUpArgs a, const int32_t* __restrict__ segtab) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-  const int e = routed_segment(a.offsets, a.E);
+  const BSeg sg = routed_segment(a.offsets, a.E, a.shared, segtab);
+  const int e = sg.e;
   if (e < 0) return;
   const int l = threadIdx.x & (kBLanes - 1);
   const int f = blockIdx.x * kBPairs + threadIdx.x / kBLanes;
@@ -589,8 +605,7 @@ __global__ __launch_bounds__(kBThreads) void k_gateup_mx_burst(GateUpArgs a) {
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + wrow * P, nrows * (uint32_t)P);
   const uint32_t lr = (uint32_t)(2 * (fr - fw));  // this lane's first row in the wavefront's span
   const uint32_t co[2] = {lr * rb, (lr + 1) * rb}, so[2] = {lr * (uint32_t)P, (lr + 1) * (uint32_t)P};
-  const int p0 = a.offsets[e];
-  const int n = a.offsets[e + 1] - p0;
+  const int p0 = sg.p0, n = sg.n;
   uint4 xr[kBStage][2];
   pre_stage(xr, min(kBStage, n), a.H, [&](int j) {
     const int sa = a.sorted_assign[p0 + j];
@@ -644,10 +659,11 @@ __global__ __launch_bounds__(kBThreads) void k_gateup_mx_burst(GateUpArgs a) {
 // Down of the routed segments: a pair is output rows 2o', 2o' + 1.  Grid:
 // (groups of kBPairs row pairs, routed segment slot).
 template <int NPL>
-__global__ __launch_bounds__(kBThreads) void k_down_mx_burst(DownArgs a) {
+__global__ __launch_bounds__(kBThreads) void k_down_mx_burst(DownArgs a, const int32_t* __restrict__ segtab) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* hs = reinterpret_cast<uint16_t*>(smem);
-  const int e = routed_segment(a.offsets, a.E);
+  const BSeg sg = routed_segment(a.offsets, a.E, a.shared, segtab);
+  const int e = sg.e;
   if (e < 0) return;
   const int l = threadIdx.x & (kBLanes - 1);
   const int npairs = (a.H + 1) / 2;
@@ -667,8 +683,7 @@ __global__ __launch_bounds__(kBThreads) void k_down_mx_burst(DownArgs a) {
   const uint32_t lr = (uint32_t)(o0 - ow);
   const uint32_t co[2] = {lr * rb, two ? (lr + 1) * rb : kOutOfRange};
   const uint32_t so[2] = {lr * (uint32_t)P, two ? (lr + 1) * (uint32_t)P : kOutOfRange};
-  const int p0 = a.offsets[e];
-  const int n = a.offsets[e + 1] - p0;
+  const int p0 = sg.p0, n = sg.n;
   const uint16_t* hseg = (const uint16_t*)a.h + (size_t)p0 * a.F;
   uint4 xr[kBStage][2];
   pre_stage(xr, min(kBStage, n), a.F, [&](int j) { return hseg + (size_t)j * a.F; });
@@ -732,20 +747,21 @@ static int burst_npl(int K) {
   return np <= 1 ? 1 : np <= 2 ? 2 : np <= 4 ? 4 : np <= 6 ? 6 : 8;
 }
 
-#define MOE_NPL_SWITCH(KERNEL, npl, grid, lds, s, args)                   \
+#define MOE_NPL_SWITCH(KERNEL, npl, grid, lds, s, ...)                    \
   switch (npl) {                                                          \
-    case 1: KERNEL<1><<<grid, kBThreads, lds, s>>>(args); break;          \
-    case 2: KERNEL<2><<<grid, kBThreads, lds, s>>>(args); break;          \
-    case 4: KERNEL<4><<<grid, kBThreads, lds, s>>>(args); break;          \
-    case 6: KERNEL<6><<<grid, kBThreads, lds, s>>>(args); break;          \
-    default: KERNEL<8><<<grid, kBThreads, lds, s>>>(args); break;         \
+    case 1: KERNEL<1><<<grid, kBThreads, lds, s>>>(__VA_ARGS__); break;          \
+    case 2: KERNEL<2><<<grid, kBThreads, lds, s>>>(__VA_ARGS__); break;          \
+    case 4: KERNEL<4><<<grid, kBThreads, lds, s>>>(__VA_ARGS__); break;          \
+    case 6: KERNEL<6><<<grid, kBThreads, lds, s>>>(__VA_ARGS__); break;          \
+    default: KERNEL<8><<<grid, kBThreads, lds, s>>>(__VA_ARGS__); break;         \
   }
 
 // Routed segments through the burst kernel; the shared expert (bf16 rows),
 // if any, through the streaming kernel with a single segment slot (slot 0
 // is the shared expert there).
 hipError_t launch_expert_ffn_mx(const moe_config* c, const moe_weights* w, const void* x, const int32_t* offsets,
-                                const int32_t* sorted_assign, int32_t T, void* h, hipStream_t s) {
+                                const int32_t* sorted_assign, int32_t T, void* h, hipStream_t s,
+                                const int32_t* segtab) {
   GateUpArgs a;
   a.x = x;
   a.gate_w = w->gate_up_w;
@@ -762,7 +778,7 @@ hipError_t launch_expert_ffn_mx(const moe_config* c, const moe_weights* w, const
   {
     const dim3 grid((c->expert_ff + kBPairs - 1) / kBPairs, max_routed_mx(c, T));
     const size_t lds = stage_rows_burst(T) * c->hidden * 2;
-    MOE_NPL_SWITCH(k_gateup_mx_burst, burst_npl(c->hidden), grid, lds, s, a)
+    MOE_NPL_SWITCH(k_gateup_mx_burst, burst_npl(c->hidden), grid, lds, s, a, segtab)
   }
   if (a.shared) {
     const dim3 grid((c->shared_ff + kPairsPerBlock - 1) / kPairsPerBlock, 1);
@@ -773,7 +789,7 @@ hipError_t launch_expert_ffn_mx(const moe_config* c, const moe_weights* w, const
 }
 
 hipError_t launch_down_mx(const moe_config* c, const moe_weights* w, const void* h, const int32_t* offsets,
-                          const int32_t* sorted_assign, int32_t T, float* y, hipStream_t s) {
+                          const int32_t* sorted_assign, int32_t T, float* y, hipStream_t s, const int32_t* segtab) {
   DownArgs a;
   a.h = h;
   a.down_w = w->down_w;
@@ -788,7 +804,7 @@ hipError_t launch_down_mx(const moe_config* c, const moe_weights* w, const void*
   {
     const dim3 grid(((c->hidden + 1) / 2 + kBPairs - 1) / kBPairs, max_routed_mx(c, T));
     const size_t lds = stage_rows_burst(T) * c->expert_ff * 2;
-    MOE_NPL_SWITCH(k_down_mx_burst, burst_npl(c->expert_ff), grid, lds, s, a)
+    MOE_NPL_SWITCH(k_down_mx_burst, burst_npl(c->expert_ff), grid, lds, s, a, segtab)
   }
   if (a.shared) {
     const dim3 grid((c->hidden + 2 * kPairsPerBlock - 1) / (2 * kPairsPerBlock), 1);

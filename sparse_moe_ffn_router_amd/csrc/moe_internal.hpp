@@ -144,6 +144,10 @@ struct Plan {
   size_t elem_x;      // bytes per activation / h element
   size_t off_logits, off_idx, off_w, off_sgate, off_offsets, off_sorted, off_pos;
   size_t off_perm, off_h, off_y, off_part, off_aqx, off_aqh, off_xn, total;
+  // few tokens: the segment-slot table the permutation writes for the
+  // decode expert kernels (nslots entries of {expert, first row, rows, 0})
+  size_t off_segtab;
+  int nslots;
   int32_t nsplit;     // router split-K ranges (1: none)
   size_t perm_bytes, y_bytes;  // scratch needed by moe_permute / moe_combine alone
   // act_quant: rounded x (moe_expert_ffn's scratch) and rounded h (after y in
@@ -174,16 +178,26 @@ hipError_t launch_permute(const moe_config* c, const int32_t* topk_idx, int32_t 
 size_t permute_scratch_bytes(int32_t T, int32_t E, int32_t k);
 // Gating + permutation in one launch for small batches.
 bool can_fuse_gate_permute(int32_t T);
+// segtab (or NULL): also write the segment-slot table, slot 0 the shared
+// expert when there is one, then the non-empty routed segments in expert
+// order, then {-1, 0, 0, 0} up to nslots.
 hipError_t launch_gate_permute(const moe_config* c, const float* logits, const float* sgate_pre, int32_t T,
                                int32_t* topk_idx, float* topk_w, float* sgate, int32_t* offsets,
-                               int32_t* sorted_assign, int32_t* assign_pos, hipStream_t s);
+                               int32_t* sorted_assign, int32_t* assign_pos, hipStream_t s, int32_t* segtab = nullptr,
+                               int nslots = 0);
+// Segment slots of the few-token expert launches (routed ones + shared).
+int gemv_slots(const moe_config* c, int32_t T);
+// segtab: the permutation's slot table (the kernels take their segment
+// from it with one scalar load) or NULL (they search the offsets).
 hipError_t launch_expert_ffn(const moe_config* c, const moe_weights* w, const void* x, const int32_t* offsets,
-                             const int32_t* sorted_assign, int32_t T, void* h, hipStream_t s);
+                             const int32_t* sorted_assign, int32_t T, void* h, hipStream_t s,
+                             const int32_t* segtab = nullptr);
 // y rows are indexed by assignment id a (routed a = t*k + j, shared a = T*k + t);
 // y is bf16 when the MFMA grouped GEMM computes it (y_is_bf16), fp32 otherwise.
 bool y_is_bf16(const moe_config* c, int32_t T);
 hipError_t launch_down(const moe_config* c, const moe_weights* w, const void* h, const int32_t* offsets,
-                       const int32_t* sorted_assign, int32_t T, void* y, hipStream_t s);
+                       const int32_t* sorted_assign, int32_t T, void* y, hipStream_t s,
+                       const int32_t* segtab = nullptr);
 // resid: NULL, or [T][H] x_dtype rows added to out (the block's residual).
 hipError_t launch_combine_gather(const moe_config* c, const void* y, const float* topk_w, const float* sgate,
                                  int32_t T, float* out, hipStream_t s, const void* resid = nullptr);

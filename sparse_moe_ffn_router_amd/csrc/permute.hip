@@ -82,10 +82,14 @@ __device__ int block_excl_scan(int v, int* wsum, int* total) {
 }
 
 // Permutation of up to kBlockTokens tokens inside one workgroup, from the
-// picks in LDS (idx_s, T*k entries).
+// picks in LDS (idx_s, T*k entries); with segtab, also the segment-slot
+// table of nslots entries {expert, first sorted position, rows, 0}: slot 0
+// the shared expert when there is one, then the non-empty routed segments
+// in expert order, then {-1, 0, 0, 0}.
 __device__ void permute_one_block(const int32_t* idx_s, int32_t T, int32_t k, int32_t E, int32_t shared,
                                   uint64_t* mask, int* base, int* wsum, int32_t* __restrict__ offsets,
-                                  int32_t* __restrict__ sorted_assign, int32_t* __restrict__ assign_pos) {
+                                  int32_t* __restrict__ sorted_assign, int32_t* __restrict__ assign_pos,
+                                  int32_t* __restrict__ segtab = nullptr, int nslots = 0) {
   const int tid = threadIdx.x;
   const int n = T * k;
   const int W = (T + 63) / 64;
@@ -110,6 +114,14 @@ __device__ void permute_one_block(const int32_t* idx_s, int32_t T, int32_t k, in
     if (shared) offsets[E + 1] = n + T;
   }
   __syncthreads();
+  if (segtab) {
+    int nact;
+    const int r = block_excl_scan(tid < E && cnt > 0 ? 1 : 0, wsum, &nact);
+    int4* tab = reinterpret_cast<int4*>(segtab);
+    if (tid < E && cnt > 0 && shared + r < nslots) tab[shared + r] = make_int4(tid, excl, cnt, 0);
+    if (tid == 0 && shared) tab[0] = make_int4(E, n, T, 0);
+    for (int q = shared + nact + tid; q < nslots; q += kThreadsBig) tab[q] = make_int4(-1, 0, 0, 0);
+  }
   for (int a = tid; a < n; a += kThreadsBig) {
     const int t = a / k, e = idx_s[a];
     int r = __popcll(mask[e * W + t / 64] & lower_bits(t & 63));
@@ -148,7 +160,8 @@ __global__ __launch_bounds__(kThreadsBig) void k_gate_permute_small(
     const float* __restrict__ logits, const float* __restrict__ sgate_pre, int32_t T, int32_t E, int32_t k,
     int32_t softmax_first, int32_t renorm, float scale, int32_t shared, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, float* __restrict__ sgate, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted_assign, int32_t* __restrict__ assign_pos) {
+    int32_t* __restrict__ sorted_assign, int32_t* __restrict__ assign_pos, int32_t* __restrict__ segtab,
+    int32_t nslots) {
   __shared__ uint64_t mask[kMaxExperts];
   __shared__ int32_t idx_s[16 * kMaxTopK];
   __shared__ int base[kMaxExperts];
@@ -161,7 +174,7 @@ __global__ __launch_bounds__(kThreadsBig) void k_gate_permute_small(
     if (shared && lane == 0) sgate[t] = 1.f / (1.f + expf(-sgate_pre[t]));
   }
   __syncthreads();
-  permute_one_block(idx_s, T, k, E, shared, mask, base, wsum, offsets, sorted_assign, assign_pos);
+  permute_one_block(idx_s, T, k, E, shared, mask, base, wsum, offsets, sorted_assign, assign_pos, segtab, nslots);
 }
 
 // Large batches, pass 1: masks and counts of one block of kBlockTokens
@@ -291,12 +304,14 @@ bool can_fuse_gate_permute(int32_t T) { return T > 0 && T <= 16; }
 
 hipError_t launch_gate_permute(const moe_config* c, const float* logits, const float* sgate_pre, int32_t T,
                                int32_t* topk_idx, float* topk_w, float* sgate, int32_t* offsets,
-                               int32_t* sorted_assign, int32_t* assign_pos, hipStream_t s) {
+                               int32_t* sorted_assign, int32_t* assign_pos, hipStream_t s, int32_t* segtab,
+                               int nslots) {
   const int softmax_first = c->gating == MOE_GATING_SOFTMAX_TOPK;
   const int shared = c->shared_ff > 0;
   k_gate_permute_small<<<1, kThreadsBig, 0, s>>>(logits, sgate_pre, T, c->n_expert, c->top_k, softmax_first,
                                                  c->norm_topk_prob, c->weights_scale, shared, topk_idx, topk_w,
-                                                 shared ? sgate : nullptr, offsets, sorted_assign, assign_pos);
+                                                 shared ? sgate : nullptr, offsets, sorted_assign, assign_pos,
+                                                 segtab, segtab ? nslots : 0);
   return hipGetLastError();
 }
 
