@@ -482,6 +482,90 @@ __global__ __launch_bounds__(256) void k_combine_gather(const YT* __restrict__ y
   reinterpret_cast<float4*>(out + (size_t)t * H)[o4] = acc;
 }
 
+// The same sum for bf16 y (the grouped GEMMs' output): 8 outputs per thread,
+// so each y row piece is one 16-byte load (the 4-output form above loads 8
+// bytes per row and thread).  Same operations in the same order per output.
+template <int RD, bool SH>
+__global__ __launch_bounds__(256) void k_combine_gather8(const uint16_t* __restrict__ y,
+                                                         const float* __restrict__ topk_w,
+                                                         const float* __restrict__ sgate, int32_t T, int32_t k,
+                                                         int32_t H, float* __restrict__ out,
+                                                         const void* __restrict__ resid) {
+  constexpr int kBatch = 8;
+  const int t = blockIdx.y;
+  const int o8 = blockIdx.x * blockDim.x + threadIdx.x;  // index of 8 outputs
+  if (o8 * 8 >= H) return;
+  auto load8 = [&](size_t row, float (&v)[8]) {
+    const uint4 q = reinterpret_cast<const uint4*>(y + row * H)[o8];
+    const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16lo(w4[i]);
+      v[2 * i + 1] = bf16hi(w4[i]);
+    }
+  };
+  float g = 0.f;
+  uint4 sraw = make_uint4(0, 0, 0, 0);
+  if constexpr (SH) {
+    g = sgate[t];
+    sraw = reinterpret_cast<const uint4*>(y + ((size_t)T * k + t) * H)[o8];
+  }
+  uint4 rraw[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+  if constexpr (RD == 1) {
+    rraw[0] = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(resid) + (size_t)t * H)[o8];
+  } else if constexpr (RD == 2) {
+    rraw[0] = reinterpret_cast<const uint4*>(static_cast<const float*>(resid) + (size_t)t * H)[2 * o8];
+    rraw[1] = reinterpret_cast<const uint4*>(static_cast<const float*>(resid) + (size_t)t * H)[2 * o8 + 1];
+  }
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int j0 = 0; j0 < k; j0 += kBatch) {
+    uint4 q[kBatch];
+    float wj[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const bool ok = j0 + j < k;
+      wj[j] = ok ? topk_w[(size_t)t * k + j0 + j] : 0.f;
+      q[j] = ok ? reinterpret_cast<const uint4*>(y + ((size_t)t * k + j0 + j) * H)[o8] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (j0 + j < k) {
+        const uint32_t w4[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = fmaf(wj[j], bf16lo(w4[i]), acc[2 * i]);
+          acc[2 * i + 1] = fmaf(wj[j], bf16hi(w4[i]), acc[2 * i + 1]);
+        }
+      }
+    }
+  }
+  if constexpr (SH) {
+    const uint32_t w4[4] = {sraw.x, sraw.y, sraw.z, sraw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] = fmaf(g, bf16lo(w4[i]), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(g, bf16hi(w4[i]), acc[2 * i + 1]);
+    }
+  }
+  if constexpr (RD == 1) {
+    const uint32_t w4[4] = {rraw[0].x, rraw[0].y, rraw[0].z, rraw[0].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] = bf16lo(w4[i]) + acc[2 * i];
+      acc[2 * i + 1] = bf16hi(w4[i]) + acc[2 * i + 1];
+    }
+  } else if constexpr (RD == 2) {
+    const uint32_t w8[8] = {rraw[0].x, rraw[0].y, rraw[0].z, rraw[0].w, rraw[1].x, rraw[1].y, rraw[1].z, rraw[1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = __uint_as_float(w8[i]) + acc[i];
+  }
+  float4* dst = reinterpret_cast<float4*>(out + (size_t)t * H) + 2 * o8;
+  dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+}
+
 }  // namespace
 
 // Defined in ffn_mfma.hip.
@@ -631,7 +715,17 @@ hipError_t launch_combine_gather(const moe_config* c, const void* y, const float
   dim3 grid((c->hidden / 4 + threads - 1) / threads, T);
   const float* sg = c->shared_ff > 0 ? sgate : nullptr;
   const int rd = !resid ? 0 : c->x_dtype == MOE_DTYPE_BF16 ? 1 : 2;
-  if (y_is_bf16(c, T))
+  if (y_is_bf16(c, T) && c->hidden % 8 == 0) {
+    const dim3 g8((c->hidden / 8 + threads - 1) / threads, T);
+    const uint16_t* yb = (const uint16_t*)y;
+#define MOE_C8(RD, SH) k_combine_gather8<RD, SH><<<g8, threads, 0, s>>>(yb, topk_w, sg, T, c->top_k, c->hidden, out, resid)
+    if (sg) {
+      if (rd == 1) MOE_C8(1, true); else if (rd == 2) MOE_C8(2, true); else MOE_C8(0, true);
+    } else {
+      if (rd == 1) MOE_C8(1, false); else if (rd == 2) MOE_C8(2, false); else MOE_C8(0, false);
+    }
+#undef MOE_C8
+  } else if (y_is_bf16(c, T))
     combine_launch<uint16_t>(rd, grid, threads, s, y, topk_w, sg, T, c->top_k, c->hidden, out, resid);
   else
     combine_launch<float>(rd, grid, threads, s, y, topk_w, sg, T, c->top_k, c->hidden, out, resid);
