@@ -275,11 +275,9 @@ __global__ __launch_bounds__(kWaves * kWave) void k_gateup_gemv(GateUpArgs a, co
           if (oai) {
             gs += bias_elem<XT>(bw[r][0], 0);
             us += sizeof(XT) == 4 ? __uint_as_float(bw[r][1]) : bias_elem<XT>(bw[r][0], 1);
-            const float g = fminf(gs, a.limit);
-            const float u = fminf(fmaxf(us, -a.limit), a.limit);
-            v = (u + 1.f) * (g / (1.f + expf(-a.alpha * g)));
+            v = oai_act(gs, us, a.alpha, a.limit);
           } else {
-            v = gs / (1.f + expf(-gs)) * us;
+            v = swiglu_act(gs, us);
           }
           hv = lane == r ? v : hv;
         }

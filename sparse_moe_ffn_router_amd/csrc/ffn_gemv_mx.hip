@@ -304,12 +304,9 @@ __global__ __launch_bounds__(kThreads) void k_gateup_gemv_mx(GateUpArgs a) {
         if (i < nt && i % kGroup == lig) {
           float hv;
           if (a.oai && !sh) {
-            const float g = fminf(acc[0][i] + bg, a.limit);
-            const float u = fminf(fmaxf(acc[1][i] + bu, -a.limit), a.limit);
-            hv = (u + 1.f) * (g / (1.f + expf(-a.alpha * g)));
+            hv = oai_act(acc[0][i] + bg, acc[1][i] + bu, a.alpha, a.limit);
           } else {
-            const float g = acc[0][i];
-            hv = g / (1.f + expf(-g)) * acc[1][i];
+            hv = swiglu_act(acc[0][i], acc[1][i]);
           }
           const int p = p0 + tb + i;
           const size_t row = p < nas ? (size_t)p * a.F : (size_t)nas * a.F + (size_t)(p - nas) * a.Fs;
@@ -648,9 +645,7 @@ __global__ __launch_bounds__(kBThreads) void k_gateup_mx_burst(GateUpArgs a, con
       }
     }
     if (active && l < nt) {
-      const float g = fminf(gs + bg, a.limit);
-      const float u = fminf(fmaxf(us + bu, -a.limit), a.limit);
-      const float hv = (u + 1.f) * (g / (1.f + expf(-a.alpha * g)));
+      const float hv = oai_act(gs + bg, us + bu, a.alpha, a.limit);
       xstore<uint16_t>((uint16_t*)a.h, (size_t)(p0 + tb + l) * a.F + f, hv);
     }
   }

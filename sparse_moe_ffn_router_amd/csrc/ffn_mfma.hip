@@ -748,22 +748,19 @@ __device__ __forceinline__ void epilogue_b(const GemmArgs& a, const Tile& t, con
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const uint32_t bb[4] = {bw[g].x, bw[g].y, bw[g].z, bw[g].w};
-          uint32_t hv[4];
+          float hv[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int q = g * 4 + e;
             float v;
             if (oai) {
-              const float gg = fminf(acc[i][0][q] + bf16lo(bb[e]), a.limit);
-              const float u = fminf(fmaxf(acc[i][1][q] + bf16hi(bb[e]), -a.limit), a.limit);
-              v = (u + 1.f) * (gg / (1.f + expf(-a.alpha * gg)));
+              v = oai_act(acc[i][0][q] + bf16lo(bb[e]), acc[i][1][q] + bf16hi(bb[e]), a.alpha, a.limit);
             } else {
-              const float gg = acc[i][0][q];
-              v = gg / (1.f + expf(-gg)) * acc[i][1][q];
+              v = swiglu_act(acc[i][0][q], acc[i][1][q]);
             }
-            hv[e] = f32_to_bf16(v);
+            hv[e] = v;
           }
-          ds_write8(R + r * 64 + ((g ^ ((r >> 1) & 3)) << 4) + hq * 8, hv[0] | hv[1] << 16, hv[2] | hv[3] << 16);
+          ds_write8(R + r * 64 + ((g ^ ((r >> 1) & 3)) << 4) + hq * 8, pack_bf16(hv[0], hv[1]), pack_bf16(hv[2], hv[3]));
         }
       }
       u32x4_t v[4];
@@ -796,22 +793,19 @@ __device__ __forceinline__ void epilogue_b(const GemmArgs& a, const Tile& t, con
           const int f = fb + g * 8;
           if (f < t.Fe) {
             const uint32_t bb[4] = {bw[g].x, bw[g].y, bw[g].z, bw[g].w};
-            uint32_t hv[4];
+            float hv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int q = g * 4 + e;
               float v;
               if (oai) {
-                const float gg = fminf(acc[i][0][q] + bf16lo(bb[e]), a.limit);
-                const float u = fminf(fmaxf(acc[i][1][q] + bf16hi(bb[e]), -a.limit), a.limit);
-                v = (u + 1.f) * (gg / (1.f + expf(-a.alpha * gg)));
+                v = oai_act(acc[i][0][q] + bf16lo(bb[e]), acc[i][1][q] + bf16hi(bb[e]), a.alpha, a.limit);
               } else {
-                const float gg = acc[i][0][q];
-                v = gg / (1.f + expf(-gg)) * acc[i][1][q];
+                v = swiglu_act(acc[i][0][q], acc[i][1][q]);
               }
-              hv[e] = f32_to_bf16(v);
+              hv[e] = v;
             }
-            *reinterpret_cast<uint2*>(hrow + f) = make_uint2(hv[0] | hv[1] << 16, hv[2] | hv[3] << 16);
+            *reinterpret_cast<uint2*>(hrow + f) = make_uint2(pack_bf16(hv[0], hv[1]), pack_bf16(hv[2], hv[3]));
           }
         }
       }
@@ -853,11 +847,10 @@ __device__ __forceinline__ void epilogue_b(const GemmArgs& a, const Tile& t, con
         for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const uint32_t y0 = f32_to_bf16(acc[i][j][g * 4] + bf16lo(bb[j][g].x));
-            const uint32_t y1 = f32_to_bf16(acc[i][j][g * 4 + 1] + bf16hi(bb[j][g].x));
-            const uint32_t y2 = f32_to_bf16(acc[i][j][g * 4 + 2] + bf16lo(bb[j][g].y));
-            const uint32_t y3 = f32_to_bf16(acc[i][j][g * 4 + 3] + bf16hi(bb[j][g].y));
-            ds_write8(R + rl * 128 + (((j * 4 + g) ^ (rl & 7)) << 4) + hq * 8, y0 | y1 << 16, y2 | y3 << 16);
+            const uint32_t y01 = pack_bf16(acc[i][j][g * 4] + bf16lo(bb[j][g].x), acc[i][j][g * 4 + 1] + bf16hi(bb[j][g].x));
+            const uint32_t y23 =
+                pack_bf16(acc[i][j][g * 4 + 2] + bf16lo(bb[j][g].y), acc[i][j][g * 4 + 3] + bf16hi(bb[j][g].y));
+            ds_write8(R + rl * 128 + (((j * 4 + g) ^ (rl & 7)) << 4) + hq * 8, y01, y23);
           }
         u32x4_t v[4];
 #pragma unroll
@@ -898,7 +891,7 @@ __device__ __forceinline__ void epilogue_b(const GemmArgs& a, const Tile& t, con
           const float v2 = v[2] + bf16lo(bb[j][g].y), v3 = v[3] + bf16hi(bb[j][g].y);
           if (MODE == MODE_DOWN) {
             *reinterpret_cast<uint2*>((uint16_t*)a.out + row * t.ncols + o) =
-                make_uint2(f32_to_bf16(v0) | f32_to_bf16(v1) << 16, f32_to_bf16(v2) | f32_to_bf16(v3) << 16);
+                make_uint2(pack_bf16(v0, v1), pack_bf16(v2, v3));
           } else if (split) {
             float* dst = a.part + row * t.ncols + o;
             if (vec)

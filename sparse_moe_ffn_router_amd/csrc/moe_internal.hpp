@@ -38,6 +38,33 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+// Two fp32 values -> packed bf16 (lo in the low half), round to nearest
+// even, one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v_t));
+}
+
+// Logistic sigma(x) = 1 / (1 + e^-x) on the hardware base-2 exponential and
+// reciprocal (v_exp_f32, v_rcp_f32: about one ulp each in fp32; e^-x = 2^(-x
+// log2 e), whose product rounding grows the relative error to ~|x| 2^-24).
+// The expert activations x sigma(x) and the gpt-oss form use it: their
+// results are rounded to bf16 (2^-9) or summed at that tolerance, so five
+// instructions replace the ~25 of a full-precision exponential and IEEE
+// divide.  Large |x|: 2^(+inf) -> sigma = 0, 2^(-inf) -> sigma = 1.
+__device__ __forceinline__ float sigmoid_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.44269504088896341f * x));
+}
+// SwiGLU's x sigma(x) * up and the clamped gpt-oss activation
+// (up + 1) * g sigma(alpha g) (g clamped above, up to [-limit, limit]).
+__device__ __forceinline__ float swiglu_act(float g, float u) { return g * sigmoid_fast(g) * u; }
+__device__ __forceinline__ float oai_act(float g, float u, float alpha, float limit) {
+  g = fminf(g, limit);
+  u = fminf(fmaxf(u, -limit), limit);
+  return (u + 1.f) * (g * sigmoid_fast(alpha * g));
+}
+
 // Order-preserving map of an fp32 value to uint32 with -0 folded into +0:
 // a > b (as floats, NaN excluded) <=> key(a) > key(b); -0 and +0 tie.  The
 // key is never 0 (the top-k's mark for a picked or absent expert): the one
