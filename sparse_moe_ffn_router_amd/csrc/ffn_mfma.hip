@@ -225,20 +225,19 @@ __device__ __forceinline__ u32x4_t ds_read16u(uint32_t addr) {
 __device__ __forceinline__ void lds_wait4(u32x4_t (&v)[4]) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
 }
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2_t ds_read8u(uint32_t addr) {
+  u32x2_t r;
+  asm volatile("ds_read_b64 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+  return r;
+}
+__device__ __forceinline__ void lds_wait8(u32x2_t (&v)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]));
+}
 __device__ __forceinline__ int32_t ds_read4(const int32_t* p) {
   int32_t r;
   asm volatile("ds_read_b32 %0, %1" : "=v"(r) : "v"((uint32_t)(uintptr_t)p) : "memory");
-  return r;
-}
-// 8- and 16-byte LDS reads (8- / 16-byte aligned), completed likewise.
-__device__ __forceinline__ uint2 ds_read8_sync(const uint32_t* p) {
-  uint2 r;
-  asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"((uint32_t)(uintptr_t)p) : "memory");
-  return r;
-}
-__device__ __forceinline__ uint4 ds_read16_sync(const uint32_t* p) {
-  uint4 r;
-  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"((uint32_t)(uintptr_t)p) : "memory");
   return r;
 }
 
@@ -727,13 +726,19 @@ __device__ __forceinline__ void epilogue_b(const GemmArgs& a, const Tile& t, con
     const int fb = t.c0 + wn * 32 + hq * 4;
     const bool oai = a.oai && !t.sh;
     uint4 bw[4];
+    if (BIAS == 1) {  // the four reads in flight together, one wait
+      u32x4_t bq[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) bq[g] = ds_read16u((uint32_t)(uintptr_t)(bias_lds + wn * 32 + g * 8 + hq * 4));
+      lds_wait4(bq);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) bw[g] = make_uint4(bq[g].x, bq[g].y, bq[g].z, bq[g].w);
+    }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      if (BIAS == 1)
-        bw[g] = ds_read16_sync(bias_lds + wn * 32 + g * 8 + hq * 4);
-      else if (BIAS == 2)
+      if (BIAS == 2)
         bw[g] = *reinterpret_cast<const uint4*>(a.bias + (size_t)t.seg * 2 * a.F + 2 * min(fb + g * 8, t.Fe - 4));
-      else
+      else if (BIAS == 0)
         bw[g] = make_uint4(0u, 0u, 0u, 0u);
     }
     if (BIAS == 2) vm_wait_all();
@@ -817,17 +822,28 @@ __device__ __forceinline__ void epilogue_b(const GemmArgs& a, const Tile& t, con
     const bool split = MODE == MODE_ROUTER && a.ksplit > 1;  // partial sums: no bias
     const bool vec = MODE != MODE_ROUTER || t.ncols % 4 == 0;
     uint2 bb[2][4];
+    if (BIAS == 1) {  // the eight reads in flight together, one wait
+      u32x2_t bq[8];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          bq[j * 4 + g] = ds_read8u((uint32_t)(uintptr_t)(bias_lds + (ob + j * 32 + g * 8 - t.c0) / 2));
+      lds_wait8(bq);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) bb[j][g] = make_uint2(bq[j * 4 + g].x, bq[j * 4 + g].y);
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int o = ob + j * 32 + g * 8;
-        if (BIAS == 1)
-          bb[j][g] = ds_read8_sync(bias_lds + (o - t.c0) / 2);
-        else if (BIAS == 2 && vec)
+        if (BIAS == 2 && vec)
           bb[j][g] = *reinterpret_cast<const uint2*>(a.bias + (MODE == MODE_DOWN ? (size_t)t.seg * a.H : 0) +
                                                      min(o, t.ncols - 4));
-        else
+        else if (BIAS != 1)
           bb[j][g] = make_uint2(0u, 0u);
       }
     if (BIAS == 2) vm_wait_all();
@@ -847,9 +863,12 @@ __device__ __forceinline__ void epilogue_b(const GemmArgs& a, const Tile& t, con
         for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const uint32_t y01 = pack_bf16(acc[i][j][g * 4] + bf16lo(bb[j][g].x), acc[i][j][g * 4 + 1] + bf16hi(bb[j][g].x));
-            const uint32_t y23 =
-                pack_bf16(acc[i][j][g * 4 + 2] + bf16lo(bb[j][g].y), acc[i][j][g * 4 + 3] + bf16hi(bb[j][g].y));
+            // (without a bias the sums go out as they are: no +0 per output)
+            const float v0 = BIAS ? acc[i][j][g * 4] + bf16lo(bb[j][g].x) : acc[i][j][g * 4];
+            const float v1 = BIAS ? acc[i][j][g * 4 + 1] + bf16hi(bb[j][g].x) : acc[i][j][g * 4 + 1];
+            const float v2 = BIAS ? acc[i][j][g * 4 + 2] + bf16lo(bb[j][g].y) : acc[i][j][g * 4 + 2];
+            const float v3 = BIAS ? acc[i][j][g * 4 + 3] + bf16hi(bb[j][g].y) : acc[i][j][g * 4 + 3];
+            const uint32_t y01 = pack_bf16(v0, v1), y23 = pack_bf16(v2, v3);
             ds_write8(R + rl * 128 + (((j * 4 + g) ^ (rl & 7)) << 4) + hq * 8, y01, y23);
           }
         u32x4_t v[4];
