@@ -491,10 +491,13 @@ __device__ void make_pipe(const GemmArgs& a, const Tile& t, int32_t* ids, uint32
   // and the epilogue read them.
   p.ids = ids;
   p.bias = bias;
-  if (MODE != MODE_ROUTER && tid < BM) {
+  // (branches on the wave index, so each load's descriptor is wave-uniform
+  // in scalar registers)
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+  if (MODE != MODE_ROUTER && wv < BM / kWave) {
     const __amdgpu_buffer_rsrc_t ri = make_rsrc(a.sorted_assign + t.p0, (uint32_t)t.rows * 4);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ri, (lds_ptr_t)(ids + (tid & ~(kWave - 1))), 4, (int)(tid * 4), 0, 0, 0);
-  } else if (MODE != MODE_ROUTER && tid < 2 * BM && a.bias) {
+  } else if (MODE != MODE_ROUTER && wv < 2 * BM / kWave && a.bias) {
     const bool hb = !t.sh && (MODE == MODE_DOWN || a.oai);
     const size_t e0 = MODE == MODE_GATEUP ? (size_t)t.seg * 2 * a.F + 2 * t.c0 : (size_t)t.seg * a.H + t.c0;
     const int n = MODE == MODE_GATEUP ? 2 * (a.F - t.c0) : a.H - t.c0;
@@ -1173,10 +1176,11 @@ __device__ void mx8_make_pipe(const GemmArgs& a, const Tile& t, int K, int32_t* 
   p.seg = t.seg;
   p.c0 = t.c0;
   p.bias = bias;
-  if (tid < BM) {
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform descriptors
+  if (wv < BM / kWave) {
     const __amdgpu_buffer_rsrc_t ri = make_rsrc(a.sorted_assign + t.p0, (uint32_t)t.rows * 4);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ri, (lds_ptr_t)(ids + (tid & ~(kWave - 1))), 4, (int)(tid * 4), 0, 0, 0);
-  } else if (tid < 2 * BM) {
+  } else if (wv < 2 * BM / kWave) {
     // the tile's bias, 512 bytes from dword-aligned offsets (columns past
     // the matrix read zeros), so the epilogue has no global load to wait for
     const size_t e0 = MODE == MODE_GATEUP ? (size_t)t.seg * 2 * a.F + 2 * t.c0 : (size_t)t.seg * a.H + t.c0;

@@ -103,8 +103,12 @@ __device__ void permute_one_block(const int32_t* idx_s, int32_t T, int32_t k, in
   int cnt = 0;
   if (tid < E)
     for (int w = 0; w < W; ++w) cnt += __popcll(mask[tid * W + w]);
+  // one scan gives both the segment starts (low 20 bits: n = T*k <= 256*32
+  // here) and each non-empty segment's slot (the count of non-empty ones
+  // before it, high bits: E <= 1024)
   int total;
-  const int excl = block_excl_scan(tid < E ? cnt : 0, wsum, &total);
+  const int packed = block_excl_scan(tid < E ? cnt + (cnt > 0 ? 1 << 20 : 0) : 0, wsum, &total);
+  const int excl = packed & 0xFFFFF;
   if (tid < E) {
     base[tid] = excl;
     offsets[tid] = excl;
@@ -115,8 +119,7 @@ __device__ void permute_one_block(const int32_t* idx_s, int32_t T, int32_t k, in
   }
   __syncthreads();
   if (segtab) {
-    int nact;
-    const int r = block_excl_scan(tid < E && cnt > 0 ? 1 : 0, wsum, &nact);
+    const int nact = total >> 20, r = packed >> 20;
     int4* tab = reinterpret_cast<int4*>(segtab);
     if (tid < E && cnt > 0 && shared + r < nslots) tab[shared + r] = make_int4(tid, excl, cnt, 0);
     if (tid == 0 && shared) tab[0] = make_int4(E, n, T, 0);
