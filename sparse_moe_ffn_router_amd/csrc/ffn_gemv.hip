@@ -401,23 +401,19 @@ __global__ __launch_bounds__(kWaves * kWave) void k_down_gemv(DownArgs a, const 
 }
 
 // out[t][o] = sum_j w[t][j] y[t*k + j][o] (+ sgate[t] y[T*k + t][o]), the
-// picks summed in pick order, in fp32 (y fp32 or bf16).  The y rows of up to
-// 8 picks are loaded together before the sums, so the loads overlap.
-template <typename YT> __device__ __forceinline__ float4 load_y4(const YT* y, size_t row, int o4, int H);
-template <> __device__ __forceinline__ float4 load_y4<float>(const float* y, size_t row, int o4, int H) {
+// picks summed in pick order, in fp32.  The y rows of up to 8 picks are
+// loaded together before the sums, so the loads overlap.  This form takes
+// the few-token kernels' fp32 y, 4 outputs per thread.
+__device__ __forceinline__ float4 load_y4(const float* y, size_t row, int o4, int H) {
   return reinterpret_cast<const float4*>(y + row * H)[o4];
-}
-template <> __device__ __forceinline__ float4 load_y4<uint16_t>(const uint16_t* y, size_t row, int o4, int H) {
-  const uint2 v = reinterpret_cast<const uint2*>(y + row * H)[o4];
-  return make_float4(bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y));
 }
 
 // RD: residual rows added last (the decoder block's residual): 0 none,
 // 1 bf16, 2 fp32 (a template parameter: a runtime choice between two
 // loads made the wave wait for one before issuing the y loads).
 // SH: a shared expert (its row and gate), likewise a template parameter.
-template <typename YT, int RD, bool SH>
-__global__ __launch_bounds__(256) void k_combine_gather(const YT* __restrict__ y, const float* __restrict__ topk_w,
+template <int RD, bool SH>
+__global__ __launch_bounds__(256) void k_combine_gather(const float* __restrict__ y, const float* __restrict__ topk_w,
                                                         const float* __restrict__ sgate, int32_t T, int32_t k,
                                                         int32_t H, float* __restrict__ out,
                                                         const void* __restrict__ resid) {
@@ -431,7 +427,7 @@ __global__ __launch_bounds__(256) void k_combine_gather(const YT* __restrict__ y
   float4 vs = make_float4(0.f, 0.f, 0.f, 0.f);
   if constexpr (SH) {
     g = sgate[t];
-    vs = load_y4<YT>(y, (size_t)T * k + t, o4, H);
+    vs = load_y4(y, (size_t)T * k + t, o4, H);
   }
   // raw residual bits, converted only where they are added: a conversion
   // right after the load would make the wave wait for it before the y loads
@@ -450,7 +446,7 @@ __global__ __launch_bounds__(256) void k_combine_gather(const YT* __restrict__ y
     for (int j = 0; j < kBatch; ++j) {
       const bool ok = j0 + j < k;
       wj[j] = ok ? topk_w[(size_t)t * k + j0 + j] : 0.f;
-      v[j] = ok ? load_y4<YT>(y, (size_t)t * k + j0 + j, o4, H) : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[j] = ok ? load_y4(y, (size_t)t * k + j0 + j, o4, H) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
@@ -481,8 +477,8 @@ __global__ __launch_bounds__(256) void k_combine_gather(const YT* __restrict__ y
 }
 
 // The same sum for bf16 y (the grouped GEMMs' output): 8 outputs per thread,
-// so each y row piece is one 16-byte load (the 4-output form above loads 8
-// bytes per row and thread).  Same operations in the same order per output.
+// so each y row piece is one 16-byte load.  Same operations in the same
+// order per output.  Its layers have bf16 x, so a residual is bf16 (RD 0/1).
 template <int RD, bool SH>
 __global__ __launch_bounds__(256) void k_combine_gather8(const uint16_t* __restrict__ y,
                                                          const float* __restrict__ topk_w,
@@ -492,29 +488,16 @@ __global__ __launch_bounds__(256) void k_combine_gather8(const uint16_t* __restr
   constexpr int kBatch = 8;
   const int t = blockIdx.y;
   const int o8 = blockIdx.x * blockDim.x + threadIdx.x;  // index of 8 outputs
+  static_assert(RD == 0 || RD == 1, "bf16 residual rows only");
   if (o8 * 8 >= H) return;
-  auto load8 = [&](size_t row, float (&v)[8]) {
-    const uint4 q = reinterpret_cast<const uint4*>(y + row * H)[o8];
-    const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = bf16lo(w4[i]);
-      v[2 * i + 1] = bf16hi(w4[i]);
-    }
-  };
   float g = 0.f;
   uint4 sraw = make_uint4(0, 0, 0, 0);
   if constexpr (SH) {
     g = sgate[t];
     sraw = reinterpret_cast<const uint4*>(y + ((size_t)T * k + t) * H)[o8];
   }
-  uint4 rraw[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
-  if constexpr (RD == 1) {
-    rraw[0] = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(resid) + (size_t)t * H)[o8];
-  } else if constexpr (RD == 2) {
-    rraw[0] = reinterpret_cast<const uint4*>(static_cast<const float*>(resid) + (size_t)t * H)[2 * o8];
-    rraw[1] = reinterpret_cast<const uint4*>(static_cast<const float*>(resid) + (size_t)t * H)[2 * o8 + 1];
-  }
+  uint4 rraw = make_uint4(0, 0, 0, 0);
+  if constexpr (RD == 1) rraw = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(resid) + (size_t)t * H)[o8];
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
@@ -548,16 +531,12 @@ __global__ __launch_bounds__(256) void k_combine_gather8(const uint16_t* __restr
     }
   }
   if constexpr (RD == 1) {
-    const uint32_t w4[4] = {rraw[0].x, rraw[0].y, rraw[0].z, rraw[0].w};
+    const uint32_t w4[4] = {rraw.x, rraw.y, rraw.z, rraw.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       acc[2 * i] = bf16lo(w4[i]) + acc[2 * i];
       acc[2 * i + 1] = bf16hi(w4[i]) + acc[2 * i + 1];
     }
-  } else if constexpr (RD == 2) {
-    const uint32_t w8[8] = {rraw[0].x, rraw[0].y, rraw[0].z, rraw[0].w, rraw[1].x, rraw[1].y, rraw[1].z, rraw[1].w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = __uint_as_float(w8[i]) + acc[i];
   }
   float4* dst = reinterpret_cast<float4*>(out + (size_t)t * H) + 2 * o8;
   dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
@@ -685,24 +664,15 @@ hipError_t launch_down(const moe_config* c, const moe_weights* w, const void* h,
   return hipGetLastError();
 }
 
-template <typename YT, bool SH>
-static void combine_launch_sh(int rd, dim3 grid, int threads, hipStream_t s, const YT* y, const float* topk_w,
+template <bool SH>
+static void combine_launch_sh(int rd, dim3 grid, int threads, hipStream_t s, const float* y, const float* topk_w,
                               const float* sg, int32_t T, int32_t k, int32_t H, float* out, const void* resid) {
   if (rd == 1)
-    k_combine_gather<YT, 1, SH><<<grid, threads, 0, s>>>(y, topk_w, sg, T, k, H, out, resid);
+    k_combine_gather<1, SH><<<grid, threads, 0, s>>>(y, topk_w, sg, T, k, H, out, resid);
   else if (rd == 2)
-    k_combine_gather<YT, 2, SH><<<grid, threads, 0, s>>>(y, topk_w, sg, T, k, H, out, resid);
+    k_combine_gather<2, SH><<<grid, threads, 0, s>>>(y, topk_w, sg, T, k, H, out, resid);
   else
-    k_combine_gather<YT, 0, SH><<<grid, threads, 0, s>>>(y, topk_w, sg, T, k, H, out, resid);
-}
-
-template <typename YT>
-static void combine_launch(int rd, dim3 grid, int threads, hipStream_t s, const void* y, const float* topk_w,
-                           const float* sg, int32_t T, int32_t k, int32_t H, float* out, const void* resid) {
-  if (sg)
-    combine_launch_sh<YT, true>(rd, grid, threads, s, (const YT*)y, topk_w, sg, T, k, H, out, resid);
-  else
-    combine_launch_sh<YT, false>(rd, grid, threads, s, (const YT*)y, topk_w, sg, T, k, H, out, resid);
+    k_combine_gather<0, SH><<<grid, threads, 0, s>>>(y, topk_w, sg, T, k, H, out, resid);
 }
 
 hipError_t launch_combine_gather(const moe_config* c, const void* y, const float* topk_w, const float* sgate,
@@ -713,20 +683,23 @@ hipError_t launch_combine_gather(const moe_config* c, const void* y, const float
   dim3 grid((c->hidden / 4 + threads - 1) / threads, T);
   const float* sg = c->shared_ff > 0 ? sgate : nullptr;
   const int rd = !resid ? 0 : c->x_dtype == MOE_DTYPE_BF16 ? 1 : 2;
-  if (y_is_bf16(c, T) && c->hidden % 8 == 0) {
+  if (y_is_bf16(c, T)) {
+    // bf16 y comes from the MFMA path: x (so any residual) is bf16 and the
+    // hidden size a multiple of 32, so every row splits into 8-output pieces
     const dim3 g8((c->hidden / 8 + threads - 1) / threads, T);
     const uint16_t* yb = (const uint16_t*)y;
 #define MOE_C8(RD, SH) k_combine_gather8<RD, SH><<<g8, threads, 0, s>>>(yb, topk_w, sg, T, c->top_k, c->hidden, out, resid)
     if (sg) {
-      if (rd == 1) MOE_C8(1, true); else if (rd == 2) MOE_C8(2, true); else MOE_C8(0, true);
+      if (rd) MOE_C8(1, true); else MOE_C8(0, true);
     } else {
-      if (rd == 1) MOE_C8(1, false); else if (rd == 2) MOE_C8(2, false); else MOE_C8(0, false);
+      if (rd) MOE_C8(1, false); else MOE_C8(0, false);
     }
 #undef MOE_C8
-  } else if (y_is_bf16(c, T))
-    combine_launch<uint16_t>(rd, grid, threads, s, y, topk_w, sg, T, c->top_k, c->hidden, out, resid);
-  else
-    combine_launch<float>(rd, grid, threads, s, y, topk_w, sg, T, c->top_k, c->hidden, out, resid);
+  } else if (sg) {
+    combine_launch_sh<true>(rd, grid, threads, s, (const float*)y, topk_w, sg, T, c->top_k, c->hidden, out, resid);
+  } else {
+    combine_launch_sh<false>(rd, grid, threads, s, (const float*)y, topk_w, sg, T, c->top_k, c->hidden, out, resid);
+  }
   return hipGetLastError();
 }
 
